@@ -1,0 +1,215 @@
+"""fp64 CPU oracle for Kimi Delta Attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg
+may import this package.  The HIP product library never calls it, and this
+package imports nothing from the product package.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, OpenMP over
+(sequence, head)); this module only marshals numpy arrays through ctypes.
+Sources are cited in the C file: the token loop of "How Kimi K3 Engineered Its
+Way to the Frontier" (section "How KDA updates its state"), the KDA equation of
+"Kimi K3: Open Frontier Intelligence" (section 6) and of "Kimi K3: a 2.8T open
+model ..." (section "Kimi Delta Attention"), and the segment transition of
+"Kimi K3 -- Training and Infrastructure Notes" (section 4.1).
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build_oracle, library_path
+
+__all__ = [
+    "recurrent",
+    "chunked",
+    "decode_step",
+    "transition",
+    "max_threads",
+    "load",
+    "open_library",
+    "using",
+]
+
+_LIB = None
+_DP = ctypes.POINTER(ctypes.c_double)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+
+def load(rebuild: bool = False):
+    """Load (building with gcc first if needed) the oracle shared library."""
+    global _LIB
+    if _LIB is not None and not rebuild:
+        return _LIB
+    path = library_path()
+    if rebuild or not os.path.exists(path):
+        build_oracle()
+    _LIB = open_library(path)
+    return _LIB
+
+
+@contextlib.contextmanager
+def using(lib):
+    """Temporarily route this module's functions through another build of the
+    oracle (the tests use it to run the pins against planted mistakes)."""
+    global _LIB
+    saved = _LIB
+    _LIB = lib
+    try:
+        yield lib
+    finally:
+        _LIB = saved
+
+
+def open_library(path):
+    """Open an oracle shared library at ``path`` and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    lib.kda_oracle_recurrent.argtypes = [
+        ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _DP, _DP, _DP, _DP, _DP, ctypes.c_double, _DP, _DP, _DP, ctypes.c_int,
+    ]
+    lib.kda_oracle_chunked.argtypes = [
+        ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _DP, _DP, _DP, _DP, _DP, ctypes.c_double, _DP, _DP, _DP, ctypes.c_int,
+    ]
+    lib.kda_oracle_decode_step.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _DP, _DP, _DP, _DP, _DP, ctypes.c_double, _DP, _I64P, ctypes.c_int64, _DP,
+        ctypes.c_int,
+    ]
+    lib.kda_oracle_transition.argtypes = [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, _DP, _DP, _DP,
+    ]
+    lib.kda_oracle_max_threads.argtypes = []
+    for fn in ("kda_oracle_recurrent", "kda_oracle_chunked", "kda_oracle_decode_step",
+               "kda_oracle_transition", "kda_oracle_max_threads"):
+        getattr(lib, fn).restype = ctypes.c_int
+    return lib
+
+
+def _f64(a, name):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # a torch tensor: upcast exactly what it holds
+        a = a.detach().to("cpu").double().numpy()
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_DP)
+
+
+def _cu(cu_seqlens, T):
+    if cu_seqlens is None:
+        raise ValueError("cu_seqlens is required")
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if cu.ndim != 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing, start at 0 and end at T_total")
+    return cu
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def _common(q, k, v, g, beta, cu_seqlens, initial_state):
+    q, k, v, g, beta = (_f64(x, n) for x, n in
+                        ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta")))
+    if q.ndim != 3 or k.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, g must be [T, H, K] with equal shapes")
+    T, H, K = q.shape
+    if v.ndim != 3 or v.shape[:2] != (T, H):
+        raise ValueError("v must be [T, H, V]")
+    V = v.shape[2]
+    if beta.shape != (T, H):
+        raise ValueError("beta must be [T, H]")
+    if cu_seqlens is None:
+        cu_seqlens = [0, T]
+    cu = _cu(cu_seqlens, T)
+    N = cu.shape[0] - 1
+    s0 = _f64(initial_state, "initial_state")
+    if s0 is not None and s0.shape != (N, H, K, V):
+        raise ValueError(f"initial_state must be [{N}, {H}, {K}, {V}]")
+    return q, k, v, g, beta, cu, s0, T, H, K, V, N
+
+
+def recurrent(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0,
+              nthreads=0):
+    """Token-by-token KDA (the definition). Returns (o [T,H,V], S_final [N,H,K,V])."""
+    lib = load()
+    q, k, v, g, beta, cu, s0, T, H, K, V, N = _common(q, k, v, g, beta, cu_seqlens,
+                                                      initial_state)
+    o = np.zeros((T, H, V))
+    sf = np.zeros((N, H, K, V))
+    rc = lib.kda_oracle_recurrent(N, cu.ctypes.data_as(_I64P), H, K, V, _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(s0),
+                                  _ptr(o), _ptr(sf), int(nthreads))
+    _check(rc, "kda_oracle_recurrent")
+    return o, sf
+
+
+def chunked(q, k, v, g, beta, chunk_size, cu_seqlens=None, initial_state=None, scale=1.0,
+            nthreads=0):
+    """Chunkwise KDA in fp64 (block form of the same recurrence). Same returns."""
+    lib = load()
+    q, k, v, g, beta, cu, s0, T, H, K, V, N = _common(q, k, v, g, beta, cu_seqlens,
+                                                      initial_state)
+    o = np.zeros((T, H, V))
+    sf = np.zeros((N, H, K, V))
+    rc = lib.kda_oracle_chunked(N, cu.ctypes.data_as(_I64P), H, K, V, int(chunk_size),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                float(scale), _ptr(s0), _ptr(o), _ptr(sf), int(nthreads))
+    _check(rc, "kda_oracle_chunked")
+    return o, sf
+
+
+def decode_step(q, k, v, g, beta, state_pool, slot_idx=None, scale=1.0, nthreads=0):
+    """One decode token per row, in place on a copy of ``state_pool``.
+
+    q, k, g: [B, H, K]; v: [B, H, V]; beta: [B, H]; state_pool: [S, H, K, V].
+    Returns (o [B, H, V] -- NaN rows for skipped slots, new_state_pool).
+    """
+    lib = load()
+    q, k, v, g, beta = (_f64(x, "x") for x in (q, k, v, g, beta))
+    B, H, K = q.shape
+    V = v.shape[2]
+    pool = np.array(_f64(state_pool, "state_pool"), copy=True)
+    if pool.shape[1:] != (H, K, V):
+        raise ValueError("state_pool must be [slots, H, K, V]")
+    idx = None
+    if slot_idx is not None:
+        idx = np.ascontiguousarray(np.asarray(slot_idx, dtype=np.int64))
+        if idx.shape != (B,):
+            raise ValueError("slot_idx must be [B]")
+    o = np.full((B, H, V), np.nan)
+    rc = lib.kda_oracle_decode_step(B, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), float(scale), _ptr(pool),
+                                    None if idx is None else idx.ctypes.data_as(_I64P),
+                                    pool.shape[0], _ptr(o), int(nthreads))
+    _check(rc, "kda_oracle_decode_step")
+    return o, pool
+
+
+def transition(k, v, g, beta):
+    """Segment transition of one head: returns (M [K,K], S_tilde [K,V]).
+
+    k, g: [T, K]; v: [T, V]; beta: [T].  S_out = M @ S_in + S_tilde.
+    """
+    lib = load()
+    k, v, g, beta = (_f64(x, "x") for x in (k, v, g, beta))
+    T, K = k.shape
+    V = v.shape[1]
+    M = np.zeros((K, K))
+    St = np.zeros((K, V))
+    rc = lib.kda_oracle_transition(T, K, V, _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(M), _ptr(St))
+    _check(rc, "kda_oracle_transition")
+    return M, St
+
+
+def max_threads() -> int:
+    return int(load().kda_oracle_max_threads())

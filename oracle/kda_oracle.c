@@ -1,0 +1,330 @@
+/*
+ * kda_oracle.c -- plain, slow, fp64 CPU oracle for Kimi Delta Attention (KDA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's cpu_baseline leg may load this library.  The product path
+ * (the HIP library) shares no code, header, table or helper with it and never
+ * calls it.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [P1] "How Kimi K3 Engineered Its Way to the Frontier", section
+ *       "How KDA updates its state" (the forget / erase+write / read token loop
+ *       of flash-linear-attention's naive.py, decay on the key axis, state
+ *       layout S[B,HV,K,V], gates g[B,T,HV,K] in natural-log space) and section
+ *       "FlashKDA steps the state once per 16 tokens" (the chunkwise form gives
+ *       the same result as the token loop; only the schedule changes).
+ *  [P2] "Kimi K3: Open Frontier Intelligence" (Chlience paper archive), section 6
+ *       (the KDA equation S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+ *       o_t = S_t^T q_t).
+ *  [P3] "Kimi K3 -- Training and Infrastructure Notes", section 4.1 "KDA
+ *       algorithm-system co-design" (a segment's effect is a transition M acting
+ *       on the incoming state plus a state S~ generated from zero) and section
+ *       4.5 "Inference and online serving" (decode updates the state in place).
+ *  [P4] "Kimi K3: a 2.8T open model ...", section "Kimi Delta Attention:
+ *       constant-size memory over a million tokens" (same equation) and
+ *       subsection "FlashKDA: the equation, shipped as a kernel" (optional state
+ *       in and out, variable-length batches through cumulative sequence lengths).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - No query scale appears in any formula; `scale` multiplies o and the pages'
+ *    formula is scale = 1.
+ *  - g is the natural-log decay (alpha = exp(g)), beta is already post-sigmoid.
+ *  - Variable-length batches reset the state to the sequence's own initial state
+ *    at every cu_seqlens boundary.
+ *
+ * Layouts (row-major, innermost last), the same as the product ABI:
+ *   q, k, g : [T_total, H, K]      v, o : [T_total, H, V]      beta : [T_total, H]
+ *   state   : [N, H, K, V]  (rows = key channels, columns = value channels)
+ * cu_seqlens: N+1 non-decreasing offsets into T_total, cu_seqlens[0] == 0.
+ *
+ * Parity status: every function below is pinned by the CPU tests (brute-force
+ * equation form on tiny inputs, closed forms, invariants); none is unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define KDA_ORACLE_OK 0
+#define KDA_ORACLE_EINVAL 1
+#define KDA_ORACLE_ENOMEM 2
+
+static int check_cu(int N, const int64_t *cu, int64_t T_total) {
+  if (N < 0 || !cu || cu[0] != 0) return 0;
+  for (int n = 0; n < N; ++n)
+    if (cu[n + 1] < cu[n]) return 0;
+  return cu[N] == T_total;
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+}
+
+/*
+ * One token of the recurrence on one head's state S (K x V), in the order of
+ * [P1] "How KDA updates its state": forget (scale row i of S by exp(g_i)),
+ * erase+write (S += beta * k (v - k^T S)^T, with k^T S read from the decayed
+ * state), then read o = scale * S^T q from the updated state.
+ * `r` is caller-provided scratch of length V.
+ */
+static void token_step(int K, int V, double *S, const double *q, const double *k,
+                       const double *v, const double *g, double beta, double scale,
+                       double *o, double *r) {
+  /* forget: decay acts on the key axis, i.e. on rows of S */
+  for (int i = 0; i < K; ++i) {
+    const double a = exp(g[i]);
+    for (int j = 0; j < V; ++j) S[(size_t)i * V + j] *= a; /*MUT_DECAY*/
+  }
+  /* what the decayed state returns for key k:  r = S^T k */
+  for (int j = 0; j < V; ++j) r[j] = 0.0;
+  for (int i = 0; i < K; ++i)
+    for (int j = 0; j < V; ++j) r[j] += k[i] * S[(size_t)i * V + j];
+  /*MUT_WRITE_BEGIN*/
+  /* erase + write: S += beta * k (v - r)^T */
+  for (int i = 0; i < K; ++i) {
+    const double bk = beta * k[i];
+    for (int j = 0; j < V; ++j) S[(size_t)i * V + j] += bk * (v[j] - r[j]); /*MUT_ERASE*/
+  }
+  /*MUT_WRITE_END*/
+  /*MUT_READ_BEGIN*/
+  /* read from the updated state: o = scale * S^T q */
+  if (o) {
+    for (int j = 0; j < V; ++j) o[j] = 0.0;
+    for (int i = 0; i < K; ++i)
+      for (int j = 0; j < V; ++j) o[j] += q[i] * S[(size_t)i * V + j];
+    for (int j = 0; j < V; ++j) o[j] *= scale;
+  }
+  /*MUT_READ_END*/
+}
+
+/*
+ * The definition: the token-by-token recurrence over a packed batch of N
+ * sequences and H heads.  S0 may be NULL (zero initial state); S_final may be
+ * NULL (not written).  o may be NULL (outputs not written).
+ */
+int kda_oracle_recurrent(int N, const int64_t *cu_seqlens, int H, int K, int V,
+                         const double *q, const double *k, const double *v,
+                         const double *g, const double *beta, double scale,
+                         const double *S0, double *o, double *S_final, int nthreads) {
+  if (H <= 0 || K <= 0 || V <= 0 || !cu_seqlens) return KDA_ORACLE_EINVAL;
+  if (!check_cu(N, cu_seqlens, cu_seqlens[N])) return KDA_ORACLE_EINVAL;
+  set_threads(nthreads);
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int64_t nh = 0; nh < (int64_t)N * H; ++nh) {
+    const int n = (int)(nh / H), h = (int)(nh % H);
+    double *S = (double *)malloc(sizeof(double) * ((size_t)K * V + V));
+    if (!S) { err |= 1; continue; }
+    double *r = S + (size_t)K * V;
+    if (S0) memcpy(S, S0 + ((size_t)n * H + h) * K * V, sizeof(double) * K * V);
+    else memset(S, 0, sizeof(double) * K * V);
+    for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+      const size_t th = (size_t)t * H + h;
+      token_step(K, V, S, q + th * K, k + th * K, v + th * V, g + th * K, beta[th],
+                 scale, o ? o + th * V : NULL, r);
+    }
+    if (S_final) memcpy(S_final + ((size_t)n * H + h) * K * V, S, sizeof(double) * K * V);
+    free(S);
+  }
+  return err ? KDA_ORACLE_ENOMEM : KDA_ORACLE_OK;
+}
+
+/*
+ * Decode: one token per batch row, applied in place to a slot pool
+ * state_pool[num_slots, H, K, V] ([P3] section 4.5: the state is updated in
+ * place at every decoding step).  Row b uses slot slot_idx[b] (identity when
+ * slot_idx is NULL); a negative slot skips the row (its o is left untouched).
+ * q, k, g: [B, H, K]; v, o: [B, H, V]; beta: [B, H].
+ */
+int kda_oracle_decode_step(int B, int H, int K, int V, const double *q, const double *k,
+                           const double *v, const double *g, const double *beta,
+                           double scale, double *state_pool, const int64_t *slot_idx,
+                           int64_t num_slots, double *o, int nthreads) {
+  if (B < 0 || H <= 0 || K <= 0 || V <= 0 || !state_pool) return KDA_ORACLE_EINVAL;
+  for (int b = 0; b < B; ++b) {
+    const int64_t s = slot_idx ? slot_idx[b] : b;
+    if (s >= num_slots) return KDA_ORACLE_EINVAL;
+    for (int b2 = 0; b2 < b; ++b2) /* two rows may not share a slot */
+      if (s >= 0 && (slot_idx ? slot_idx[b2] : b2) == s) return KDA_ORACLE_EINVAL;
+  }
+  set_threads(nthreads);
+  int err = 0;
+#pragma omp parallel for schedule(static) reduction(| : err)
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int64_t s = slot_idx ? slot_idx[b] : b;
+    if (s < 0) continue;
+    double *r = (double *)malloc(sizeof(double) * V);
+    if (!r) { err |= 1; continue; }
+    const size_t th = (size_t)b * H + h;
+    token_step(K, V, state_pool + ((size_t)s * H + h) * K * V, q + th * K, k + th * K,
+               v + th * V, g + th * K, beta[th], scale, o ? o + th * V : NULL, r);
+    free(r);
+  }
+  return err ? KDA_ORACLE_ENOMEM : KDA_ORACLE_OK;
+}
+
+/*
+ * The chunkwise evaluation ([P1] "FlashKDA steps the state once per 16 tokens":
+ * split the sequence into blocks of C tokens, compute inside a block with dense
+ * products, step the state once per block; the result matches the token loop).
+ * The pages give the shape, not the algebra; this is the block form obtained by
+ * unrolling the recurrence over one block with incoming state S (K x V):
+ *
+ *   G_r   = sum_{s<=r} g_s                        (per key channel, within the block)
+ *   A[r,s]= beta_r * sum_c k_r[c] k_s[c] exp(G_r[c]-G_s[c])     for s <  r
+ *   P[r,s]=          sum_c q_r[c] k_s[c] exp(G_r[c]-G_s[c])     for s <= r
+ *   u_r   = beta_r (v_r - S^T (exp(G_r) * k_r)) - sum_{s<r} A[r,s] u_s
+ *           (i.e. (I + A) U = diag(beta) (V - K~ S): a unit lower-triangular
+ *            system, solved here by plain forward substitution)
+ *   o_r   = scale * ( S^T (exp(G_r) * q_r) + sum_{s<=r} P[r,s] u_s )
+ *   S    <- exp(G_last) * S + sum_s (exp(G_last - G_s) * k_s) u_s^T
+ *
+ * Every exponent in A and P is G_r - G_s with s <= r, so no factor exceeds 1.
+ * Independent of the token loop above: it shares nothing with token_step.
+ */
+int kda_oracle_chunked(int N, const int64_t *cu_seqlens, int H, int K, int V, int C,
+                       const double *q, const double *k, const double *v, const double *g,
+                       const double *beta, double scale, const double *S0, double *o,
+                       double *S_final, int nthreads) {
+  if (H <= 0 || K <= 0 || V <= 0 || C <= 0 || !cu_seqlens) return KDA_ORACLE_EINVAL;
+  if (!check_cu(N, cu_seqlens, cu_seqlens[N])) return KDA_ORACLE_EINVAL;
+  set_threads(nthreads);
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int64_t nh = 0; nh < (int64_t)N * H; ++nh) {
+    const int n = (int)(nh / H), h = (int)(nh % H);
+    const size_t kv = (size_t)K * V;
+    /* S, Snew, G, A, P, U, tmp */
+    const size_t need = 2 * kv + (size_t)C * K + 2 * (size_t)C * C + (size_t)C * V + (size_t)V;
+    double *buf = (double *)malloc(sizeof(double) * need);
+    if (!buf) { err |= 1; continue; }
+    double *S = buf, *Sn = S + kv, *G = Sn + kv, *A = G + (size_t)C * K;
+    double *P = A + (size_t)C * C, *U = P + (size_t)C * C, *tmp = U + (size_t)C * V;
+    if (S0) memcpy(S, S0 + ((size_t)n * H + h) * kv, sizeof(double) * kv);
+    else memset(S, 0, sizeof(double) * kv);
+
+    for (int64_t c0 = cu_seqlens[n]; c0 < cu_seqlens[n + 1]; c0 += C) {
+      const int L = (int)((cu_seqlens[n + 1] - c0 < C) ? (cu_seqlens[n + 1] - c0) : C);
+#define ROW(ptr, r, D) ((ptr) + ((size_t)(c0 + (r)) * H + h) * (D))
+      /* cumulative log-decay inside the block */
+      for (int r = 0; r < L; ++r)
+        for (int c = 0; c < K; ++c)
+          G[(size_t)r * K + c] = ROW(g, r, K)[c] + (r ? G[(size_t)(r - 1) * K + c] : 0.0);
+      /* A and P */
+      for (int r = 0; r < L; ++r) {
+        const double br = beta[(size_t)(c0 + r) * H + h];
+        for (int s = 0; s <= r; ++s) {
+          double a = 0.0, p = 0.0;
+          for (int c = 0; c < K; ++c) {
+            const double e = exp(G[(size_t)r * K + c] - G[(size_t)s * K + c]);
+            a += ROW(k, r, K)[c] * ROW(k, s, K)[c] * e;
+            p += ROW(q, r, K)[c] * ROW(k, s, K)[c] * e;
+          }
+          A[(size_t)r * C + s] = (s < r) ? br * a : 0.0;
+          P[(size_t)r * C + s] = p;
+        }
+      }
+      /* forward substitution for U */
+      for (int r = 0; r < L; ++r) {
+        const double br = beta[(size_t)(c0 + r) * H + h];
+        for (int j = 0; j < V; ++j) tmp[j] = 0.0; /* S^T (exp(G_r) * k_r) */
+        for (int c = 0; c < K; ++c) {
+          const double kt = ROW(k, r, K)[c] * exp(G[(size_t)r * K + c]);
+          for (int j = 0; j < V; ++j) tmp[j] += kt * S[(size_t)c * V + j];
+        }
+        for (int j = 0; j < V; ++j) {
+          double u = br * (ROW(v, r, V)[j] - tmp[j]);
+          for (int s = 0; s < r; ++s) u -= A[(size_t)r * C + s] * U[(size_t)s * V + j];
+          U[(size_t)r * V + j] = u;
+        }
+      }
+      /* outputs */
+      if (o) {
+        for (int r = 0; r < L; ++r) {
+          for (int j = 0; j < V; ++j) tmp[j] = 0.0;
+          for (int c = 0; c < K; ++c) {
+            const double qt = ROW(q, r, K)[c] * exp(G[(size_t)r * K + c]);
+            for (int j = 0; j < V; ++j) tmp[j] += qt * S[(size_t)c * V + j];
+          }
+          for (int s = 0; s <= r; ++s)
+            for (int j = 0; j < V; ++j) tmp[j] += P[(size_t)r * C + s] * U[(size_t)s * V + j];
+          double *orow = ROW(o, r, V);
+          for (int j = 0; j < V; ++j) orow[j] = scale * tmp[j];
+        }
+      }
+      /* state step */
+      for (int c = 0; c < K; ++c) {
+        const double gl = G[(size_t)(L - 1) * K + c];
+        for (int j = 0; j < V; ++j) Sn[(size_t)c * V + j] = exp(gl) * S[(size_t)c * V + j];
+        for (int s = 0; s < L; ++s) {
+          const double kb = ROW(k, s, K)[c] * exp(gl - G[(size_t)s * K + c]);
+          for (int j = 0; j < V; ++j) Sn[(size_t)c * V + j] += kb * U[(size_t)s * V + j];
+        }
+      }
+      memcpy(S, Sn, sizeof(double) * kv);
+#undef ROW
+    }
+    if (S_final) memcpy(S_final + ((size_t)n * H + h) * kv, S, sizeof(double) * kv);
+    free(buf);
+  }
+  return err ? KDA_ORACLE_ENOMEM : KDA_ORACLE_OK;
+}
+
+/*
+ * Segment transition ([P3] section 4.1, intra-device and cross-device context
+ * parallelism): over tokens t = 0..T-1 of one head, the segment maps an
+ * incoming state S_in to S_out = M S_in + S~, with
+ *   M  = M_{T-1} ... M_1 M_0,   M_t = (I - beta_t k_t k_t^T) Diag(exp(g_t))   (K x K)
+ *   S~ = the state the recurrence reaches from a zero incoming state        (K x V)
+ * k, g: [T, K], v: [T, V], beta: [T] (one head, contiguous).  Either output may
+ * be NULL.
+ */
+int kda_oracle_transition(int64_t T, int K, int V, const double *k, const double *v,
+                          const double *g, const double *beta, double *M, double *S_tilde) {
+  if (T < 0 || K <= 0 || V <= 0) return KDA_ORACLE_EINVAL;
+  double *Mt = (double *)malloc(sizeof(double) * ((size_t)K * K + K));
+  double *S = (double *)calloc((size_t)K * V + V, sizeof(double));
+  if (!Mt || !S) { free(Mt); free(S); return KDA_ORACLE_ENOMEM; }
+  double *w = Mt + (size_t)K * K;
+  double *r = S + (size_t)K * V;
+  for (int i = 0; i < K; ++i)
+    for (int j = 0; j < K; ++j) Mt[(size_t)i * K + j] = (i == j) ? 1.0 : 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const double *kt = k + (size_t)t * K, *gt = g + (size_t)t * K;
+    /* M <- (I - b k k^T) Diag(a) M : first Diag(a) M, then subtract b k (k^T (Diag(a) M)) */
+    for (int i = 0; i < K; ++i) {
+      const double a = exp(gt[i]);
+      for (int j = 0; j < K; ++j) Mt[(size_t)i * K + j] *= a;
+    }
+    for (int j = 0; j < K; ++j) {
+      double s = 0.0;
+      for (int i = 0; i < K; ++i) s += kt[i] * Mt[(size_t)i * K + j];
+      w[j] = s;
+    }
+    for (int i = 0; i < K; ++i)
+      for (int j = 0; j < K; ++j) Mt[(size_t)i * K + j] -= beta[t] * kt[i] * w[j];
+    /* S~: the plain token recurrence from zero, outputs not needed */
+    token_step(K, V, S, kt, kt, v + (size_t)t * V, gt, beta[t], 1.0, NULL, r);
+  }
+  if (M) memcpy(M, Mt, sizeof(double) * K * K);
+  if (S_tilde) memcpy(S_tilde, S, sizeof(double) * K * V);
+  free(Mt);
+  free(S);
+  return KDA_ORACLE_OK;
+}
+
+int kda_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,376 @@
+"""Pins for the fp64 oracle: each test checks the oracle against something other
+than itself -- the KDA equation written as explicit matrix products (a second
+published form of the recurrence), exact rational arithmetic, closed forms,
+invariants, and numbers printed on the pages.
+
+Pages (cited by title and section):
+  [P1] "How Kimi K3 Engineered Its Way to the Frontier" -- "How KDA updates its
+       state" (token loop, decay on the key axis, erase reads the decayed state,
+       beta near 1 clears the old value); "FlashKDA steps the state once per 16
+       tokens" (chunked result matches the token loop); "What the hybrid saves".
+  [P2] "Kimi K3: Open Frontier Intelligence", section 6 (the KDA equation).
+  [P3] "Kimi K3 -- Training and Infrastructure Notes", section 4.1 (segment
+       transition M and zero-start state S~ compose exactly).
+  [P4] "Kimi K3: a 2.8T open model ...", "Kimi Delta Attention" (same equation).
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.build import SOURCE, build_oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+def rand_inputs(rng, T, H, K, V, unit=True, g_scale=1.0):
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    if unit:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, V))
+    g = -np.logaddexp(0.0, rng.standard_normal((T, H, K))) * g_scale  # -softplus
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))
+    return q, k, v, g, beta
+
+
+def equation_form(q, k, v, g, beta, S0, scale=1.0):
+    """The KDA equation of [P2] section 6 / [P4] "Kimi Delta Attention", written
+    as explicit matrix products for one head:
+        S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t
+    q, k, g: [T, K]; v: [T, V]; beta: [T]; S0: [K, V]."""
+    T, K = k.shape
+    S = S0.copy()
+    outs = []
+    for t in range(T):
+        kt = k[t][:, None]
+        Mt = (np.eye(K) - beta[t] * kt @ kt.T) @ np.diag(np.exp(g[t]))
+        S = Mt @ S + beta[t] * kt @ v[t][None, :]
+        outs.append(scale * S.T @ q[t])
+    return np.array(outs), S
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("K,V,T", [(1, 1, 3), (2, 3, 2), (3, 2, 3), (4, 4, 3), (5, 2, 1)])
+def test_tiny_matches_equation_form(K, V, T):
+    """Tiny inputs (K != V catches a transposed operand): the token loop equals
+    the matrix-product form of the KDA equation."""
+    rng = np.random.default_rng(100 + 10 * K + V)
+    H = 2
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V, unit=False)
+    S0 = rng.standard_normal((1, H, K, V))
+    o, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0, scale=0.75)
+    for h in range(H):
+        o_ref, s_ref = equation_form(q[:, h], k[:, h], v[:, h], g[:, h], beta[:, h],
+                                     S0[0, h], scale=0.75)
+        np.testing.assert_allclose(o[:, h], o_ref, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(sf[0, h], s_ref, rtol=1e-13, atol=1e-13)
+
+
+def test_exact_rational_two_tokens():
+    """d_k = d_v = 2, two tokens, hand-chosen rational values, expanded in exact
+    rational arithmetic from the KDA equation.  Decays are chosen as exp(g) with
+    g = ln(1/2), ln(1/4), so alpha is 1/2, 1/4 up to one rounding of exp/log."""
+    F = Fraction
+    alphas = [[F(1, 2), F(1, 4)], [F(1, 4), F(1, 2)]]
+    ks = [[F(3, 5), F(4, 5)], [F(1), F(0)]]
+    vs = [[F(2), F(-1)], [F(1, 2), F(3)]]
+    qs = [[F(1), F(2)], [F(-1), F(1)]]
+    betas = [F(1, 2), F(1, 3)]
+    S = [[F(1), F(0)], [F(2), F(-1)]]  # initial state, rows = key channels
+    outs = []
+    for t in range(2):
+        a, kk, vv, qq, b = alphas[t], ks[t], vs[t], qs[t], betas[t]
+        D = [[a[i] * S[i][j] for j in range(2)] for i in range(2)]       # Diag(a) S
+        kTD = [sum(kk[i] * D[i][j] for i in range(2)) for j in range(2)]  # k^T D S
+        S = [[D[i][j] - b * kk[i] * kTD[j] + b * kk[i] * vv[j] for j in range(2)]
+             for i in range(2)]
+        outs.append([sum(qq[i] * S[i][j] for i in range(2)) for j in range(2)])
+    fl = lambda m: np.array(m, dtype=np.float64)
+    q = fl(qs)[:, None, :]
+    k = fl(ks)[:, None, :]
+    v = fl(vs)[:, None, :]
+    g = np.log(fl(alphas))[:, None, :]
+    beta = fl(betas)[:, None]
+    S0 = fl([[1, 0], [2, -1]])[None, None]
+    o, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    np.testing.assert_allclose(o[:, 0], fl(outs), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(sf[0, 0], fl(S), rtol=1e-14, atol=1e-14)
+
+
+# --------------------------------------------------------------- closed forms
+def test_beta0_alpha1_leaves_state_unchanged():
+    rng = np.random.default_rng(1)
+    T, H, K, V = 37, 3, 8, 6
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    g[:] = 0.0
+    beta[:] = 0.0
+    S0 = rng.standard_normal((1, H, K, V))
+    o, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    assert np.array_equal(sf, S0)
+    np.testing.assert_allclose(o, np.einsum("thk,hkv->thv", q, S0[0]), rtol=1e-13)
+
+
+def test_beta0_pure_decay_closed_form():
+    """beta = 0: S_T = Diag(exp(sum_t g_t)) S0, o_t = (Diag(exp(G_t)) S0)^T q_t."""
+    rng = np.random.default_rng(2)
+    T, H, K, V = 29, 2, 8, 5
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V, g_scale=0.1)
+    beta[:] = 0.0
+    S0 = rng.standard_normal((1, H, K, V))
+    o, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    G = np.cumsum(g, axis=0)
+    np.testing.assert_allclose(sf[0], np.exp(G[-1])[:, :, None] * S0[0], rtol=1e-12)
+    o_ref = np.einsum("thk,thk,hkv->thv", q, np.exp(G), S0[0])
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-14)
+
+
+def test_beta1_unit_key_reads_back_its_value():
+    """[P1] "How KDA updates its state": beta near 1 clears the old value and the
+    next read for k_t returns what this token wrote.  With beta = 1, |k| = 1 and
+    q = k the read returns v_t exactly, for any prior state and decay."""
+    rng = np.random.default_rng(3)
+    T, H, K, V = 41, 2, 16, 12
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    beta[:] = 1.0
+    q = k.copy()
+    S0 = rng.standard_normal((1, H, K, V))
+    o, _ = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    np.testing.assert_allclose(o, v, rtol=1e-12, atol=1e-12)
+
+
+def test_orthonormal_keys_exact_retrieval():
+    """alpha = 1, beta = 1, S0 = 0 and orthonormal keys: every written value is
+    retrieved exactly, k_j^T S_T = v_j^T for all j."""
+    rng = np.random.default_rng(4)
+    K = V = 16
+    T = 16
+    Q, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    k = Q.T[:T][:, None, :]  # rows are orthonormal keys
+    v = rng.standard_normal((T, 1, V))
+    q = rng.standard_normal((T, 1, K))
+    g = np.zeros((T, 1, K))
+    beta = np.ones((T, 1))
+    _, sf = oracle.recurrent(q, k, v, g, beta)
+    np.testing.assert_allclose(k[:, 0] @ sf[0, 0], v[:, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_decay_is_natural_exponential_of_gate():
+    """The page's decay floor: with g = -5 the state survives as exp(-5) ~ 0.0067
+    (a base-2 reading would give 2^-5 = 0.031)."""
+    c = json.load(open(GOLDEN))["decay_floor"]
+    H, K, V = 1, 4, 3
+    S0 = np.ones((1, H, K, V))
+    q = np.zeros((1, H, K))
+    k = np.zeros((1, H, K))
+    v = np.zeros((1, H, V))
+    g = np.full((1, H, K), c["gate_lower_bound"])
+    beta = np.zeros((1, H))
+    _, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    assert abs(sf[0, 0, 0, 0] - c["alpha_floor_printed"]) <= c["printed_digits_tol"]
+
+
+def test_cumulative_16_token_bound_of_lower_bounded_gate():
+    """[P2] section 6: with every g >= -5 a 16-token cumulative log-decay lies in
+    [-80, 0]; checked on the clamped synthetic gate the prefill workload uses."""
+    import torch
+    import kda_inputs as ki
+    c = json.load(open(GOLDEN))["cumulative_bound_16"]
+    cfg = ki.PrefillConfig("t", (4096,), 2, "bf16", g_lower_bound=c["gate_lower_bound"])
+    x = ki.make_prefill(cfg, heads=2)
+    G16 = x["g"].double().view(-1, c["tokens"], 2, 128).sum(dim=1)
+    assert float(G16.min()) >= c["lower"] and float(G16.max()) <= c["upper"]
+    assert float(x["g"].min()) >= c["gate_lower_bound"]
+    assert math.isclose(c["lower"], c["tokens"] * c["gate_lower_bound"])
+
+
+# ----------------------------------------------------------------- invariants
+@pytest.mark.parametrize("C", [1, 7, 16, 64])
+def test_chunked_equals_sequential(C):
+    """[P1] "FlashKDA steps the state once per 16 tokens": the chunked result
+    matches the token loop.  Packed batch, partial last chunks, initial state."""
+    rng = np.random.default_rng(10 + C)
+    lens = [1, 63, 64, 65, 150, 0, 29]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, K, V = int(cu[-1]), 2, 16, 12
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    S0 = 0.3 * rng.standard_normal((len(lens), H, K, V))
+    o1, s1 = oracle.recurrent(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0, scale=0.5)
+    o2, s2 = oracle.chunked(q, k, v, g, beta, C, cu_seqlens=cu, initial_state=S0, scale=0.5)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12 * np.max(np.abs(o1))
+    assert np.max(np.abs(s1 - s2)) <= 1e-12 * np.max(np.abs(s1))
+
+
+def test_chunked_equals_sequential_at_head_dim_128():
+    rng = np.random.default_rng(11)
+    T, H, K, V = 200, 1, 128, 128
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    o1, s1 = oracle.recurrent(q, k, v, g, beta)
+    o2, s2 = oracle.chunked(q, k, v, g, beta, 64)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12 * np.max(np.abs(o1))
+    assert np.max(np.abs(s1 - s2)) <= 1e-12 * np.max(np.abs(s1))
+
+
+def test_segment_transition_composes_exactly():
+    """[P3] section 4.1: a segment maps S_in to M S_in + S~; M is the ordered
+    product of (I - b k k^T) Diag(a) (built here with numpy), S~ the state from
+    zero; composing two segments equals running both."""
+    rng = np.random.default_rng(12)
+    T1, T2, K, V = 23, 31, 8, 6
+    q, k, v, g, beta = rand_inputs(rng, T1 + T2, 1, K, V)
+    k1, v1, g1, b1 = k[:, 0], v[:, 0], g[:, 0], beta[:, 0]
+    M, St = oracle.transition(k1, v1, g1, b1)
+    Mref = np.eye(K)
+    for t in range(T1 + T2):
+        kt = k1[t][:, None]
+        Mref = (np.eye(K) - b1[t] * kt @ kt.T) @ np.diag(np.exp(g1[t])) @ Mref
+    np.testing.assert_allclose(M, Mref, rtol=1e-12, atol=1e-14)
+    S0 = rng.standard_normal((1, 1, K, V))
+    _, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    np.testing.assert_allclose(sf[0, 0], M @ S0[0, 0] + St, rtol=1e-12, atol=1e-13)
+    # two segments composed
+    Ma, Sa = oracle.transition(k1[:T1], v1[:T1], g1[:T1], b1[:T1])
+    Mb, Sb = oracle.transition(k1[T1:], v1[T1:], g1[T1:], b1[T1:])
+    np.testing.assert_allclose(Mb @ (Ma @ S0[0, 0] + Sa) + Sb, sf[0, 0], rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_outputs_affine_in_initial_state():
+    rng = np.random.default_rng(13)
+    T, H, K, V = 40, 2, 8, 8
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    Sa = rng.standard_normal((1, H, K, V))
+    Sb = rng.standard_normal((1, H, K, V))
+    oa, sa = oracle.recurrent(q, k, v, g, beta, initial_state=Sa)
+    ob, sb = oracle.recurrent(q, k, v, g, beta, initial_state=Sb)
+    oab, sab = oracle.recurrent(q, k, v, g, beta, initial_state=Sa + Sb)
+    o0, s0 = oracle.recurrent(q, k, v, g, beta)
+    np.testing.assert_allclose(oab, oa + ob - o0, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sab, sa + sb - s0, rtol=1e-11, atol=1e-12)
+
+
+def test_split_and_resume_is_bitwise():
+    rng = np.random.default_rng(14)
+    T, H, K, V = 90, 2, 8, 4
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    S0 = rng.standard_normal((1, H, K, V))
+    o, sf = oracle.recurrent(q, k, v, g, beta, initial_state=S0)
+    t = 37
+    o1, s1 = oracle.recurrent(q[:t], k[:t], v[:t], g[:t], beta[:t], initial_state=S0)
+    o2, s2 = oracle.recurrent(q[t:], k[t:], v[t:], g[t:], beta[t:], initial_state=s1)
+    assert np.array_equal(np.concatenate([o1, o2]), o)
+    assert np.array_equal(s2, sf)
+
+
+def test_varlen_equals_separate_runs():
+    rng = np.random.default_rng(15)
+    lens = [5, 0, 17, 1, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, K, V = int(cu[-1]), 2, 8, 4
+    q, k, v, g, beta = rand_inputs(rng, T, H, K, V)
+    S0 = rng.standard_normal((len(lens), H, K, V))
+    o, sf = oracle.recurrent(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        on, sn = oracle.recurrent(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b],
+                                  initial_state=S0[n:n + 1])
+        assert np.array_equal(o[a:b], on)
+        assert np.array_equal(sf[n], sn[0])
+
+
+def test_decode_steps_equal_token_loop():
+    """T decode steps through a slot pool equal the token loop per sequence; a
+    negative slot leaves its state untouched."""
+    rng = np.random.default_rng(16)
+    B, H, K, V, T = 5, 2, 8, 6, 7
+    q, k, v, g, beta = rand_inputs(rng, T * B, H, K, V)
+    shp = lambda x: x.reshape((T, B) + x.shape[1:])
+    q, k, v, g, beta = map(shp, (q, k, v, g, beta))
+    pool = rng.standard_normal((8, H, K, V))
+    slots = np.array([6, 0, -1, 3, 1])
+    cur = pool.copy()
+    outs = []
+    for t in range(T):
+        o_t, cur = oracle.decode_step(q[t], k[t], v[t], g[t], beta[t], cur, slots)
+        outs.append(o_t)
+    for b, s in enumerate(slots):
+        if s < 0:
+            continue
+        o_ref, s_ref = oracle.recurrent(q[:, b], k[:, b], v[:, b], g[:, b], beta[:, b],
+                                        initial_state=pool[s:s + 1])
+        np.testing.assert_allclose(np.array(outs)[:, b], o_ref, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(cur[s], s_ref[0], rtol=1e-13, atol=1e-14)
+    untouched = [s for s in range(8) if s not in set(slots.tolist())]
+    assert np.array_equal(cur[untouched], pool[untouched])
+    assert np.all(np.isnan(np.array(outs)[:, 2]))
+
+
+# ------------------------------------------- planted mistakes must be caught
+def _pins_pass():
+    """Run a compact set of the pins above; True if all hold."""
+    checks = [
+        lambda: test_tiny_matches_equation_form(3, 2, 3),
+        test_exact_rational_two_tokens,
+        test_beta1_unit_key_reads_back_its_value,
+        test_beta0_pure_decay_closed_form,
+        test_decay_is_natural_exponential_of_gate,
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def _swap_blocks(src, a, b):
+    """Move the text between markers ``b`` before the text between markers ``a``."""
+    ia0, ia1 = src.index(f"/*{a}_BEGIN*/"), src.index(f"/*{a}_END*/") + len(f"/*{a}_END*/")
+    ib0, ib1 = src.index(f"/*{b}_BEGIN*/"), src.index(f"/*{b}_END*/") + len(f"/*{b}_END*/")
+    assert ia1 <= ib0
+    return src[:ia0] + src[ib0:ib1] + src[ia1:ib0] + src[ia0:ia1] + src[ib1:]
+
+
+MUTANTS = {
+    # erase term dropped (plain linear attention with decay)
+    "no_erase": lambda s: s.replace("bk * (v[j] - r[j]); /*MUT_ERASE*/", "bk * v[j];"),
+    # sign of the erase flipped
+    "erase_sign": lambda s: s.replace("bk * (v[j] - r[j]); /*MUT_ERASE*/",
+                                      "bk * (v[j] + r[j]);"),
+    # decay applied to the value axis (columns) instead of the key axis (rows)
+    "decay_on_value_axis": lambda s: s.replace(
+        "S[(size_t)i * V + j] *= a; /*MUT_DECAY*/",
+        "S[(size_t)i * V + j] *= exp(g[j % K]); (void)a;"),
+    # base-2 gate instead of natural log
+    "base2_gate": lambda s: s.replace("const double a = exp(g[i]);",
+                                      "const double a = exp2(g[i]);"),
+    # read before the write
+    "read_before_write": lambda s: _swap_blocks(s, "MUT_WRITE", "MUT_READ"),
+    # erase measured with the query instead of the key
+    "erase_with_query": lambda s: s.replace(
+        "const double bk = beta * k[i];", "const double bk = beta * q[i];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    """Each plausible mistake, planted in a copy of the oracle on the CPU, fails
+    at least one pin; the unmodified oracle passes them all."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(SOURCE).read()
+    mutated = MUTANTS[name](src)
+    assert mutated != src, "mutation did not apply"
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(mutated)
+    lib_path = build_oracle(str(path), str(tmp_path / f"libmut_{name}.so"))
+    assert _pins_pass(), "unmodified oracle must pass the pins"
+    with oracle.using(oracle.open_library(lib_path)):
+        assert not _pins_pass(), f"planted mistake '{name}' was not caught"
