@@ -1,0 +1,204 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+A step is one chunked prefill forward of the 4 x 8,192-token, 96-head bf16
+workload (chunk 64, fp32 state, outputs + final states), inputs resident in HBM
+before the timed region.  The recurrent decode workload (512 sequences x 96
+heads, fp32 states in HBM, 1000 in-place steps) is timed after it and reported
+in the same JSON line.
+
+Algorithmic accounting (fixed; it does not depend on the implementation):
+  prefill FLOP per token-head = 6 d^2 + C (3 d + 2 d) = 139,264   (d = 128, C = 64)
+  prefill bytes per token-head = q, k, v, o in bf16 (4 x 256) + g fp32 (512) + beta (4)
+                                 = 1,540, plus 64 KiB per (sequence, head) final state
+  decode bytes per (row, head) per step = 2 x 65,536 (state read + write)
+                                 + 3 x 256 (q, k, v) + 512 (g) + 4 (beta) + 256 (o) = 132,612
+Roofline peaks: HBM 8.0 TB/s; bf16 dense matrix 2.5 PFLOP/s (2,516.6 TFLOP/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + % MFMA peak; decode step GB/s + % HBM peak"
+PREFILL_WORKLOAD = "kda_prefill_b4_t8192_h96_bf16"
+DECODE_WORKLOAD = "kda_decode_b512_h96_bf16_f32state"
+D, C = 128, 64
+FLOP_PER_TOKEN_HEAD = 6 * D * D + C * (3 * D + 2 * D)          # 139,264
+BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 4 * D + 4                   # 1,540
+STATE_BYTES = D * D * 4                                        # 65,536
+DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 3 * 2 * D + 4 * D + 4 + 2 * D   # 132,612
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-chains-per-core", type=int, default=2)
+    ap.add_argument("--workload", default=PREFILL_WORKLOAD)
+    return ap.parse_args()
+
+
+def time_prefill(kda, ki, workload, steps, warmup):
+    import torch
+    cfg = ki.CONFIGS[workload]
+    x = ki.make_prefill(cfg, device="cuda", seed=1002)
+    N, H = len(x["lengths"]), x["heads"]
+    varlen = cfg.varlen
+    o = torch.empty_like(x["q"])
+    sf = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    ws_bytes = kda.chunk_fwd_workspace_size(
+        x["q"], num_seqs=N, cu_seqlens_host=x["cu_seqlens_host"] if varlen else None)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                      cu_seqlens=x["cu_seqlens"] if varlen else None,
+                      cu_seqlens_host=x["cu_seqlens_host"] if varlen else None,
+                      initial_state=x["initial_state"], num_seqs=N, out=o, final_state=sf,
+                      workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    tokens = x["q"].shape[0]
+    res = dict(ms=ms, wall_s=wall, tokens=tokens, heads=H, seqs=N, x=x, cfg=cfg)
+    return res
+
+
+def time_decode(kda, ki, steps, warmup=10):
+    import torch
+    cfg = ki.DECODE_CONFIGS[DECODE_WORKLOAD]
+    x = ki.make_decode_ring(cfg, device="cuda")
+    state = x["state"]
+    o = torch.empty_like(x["q"][0])
+
+    def step(t):
+        r = t % cfg.ring
+        kda.recurrent_step(x["q"][r], x["k"][r], x["v"][r], x["g"][r], x["beta"][r], state,
+                           out=o)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for t in range(steps):
+        step(warmup + t)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    heads = cfg.batch * cfg.heads
+    gbs = heads * DECODE_BYTES_PER_HEAD / (ms * 1e-3) / 1e9
+    del x, state
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms, steps=steps, gb_per_s=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+                bytes_per_step=heads * DECODE_BYTES_PER_HEAD, batch=cfg.batch, heads=cfg.heads)
+
+
+def cpu_baseline(x, chains_per_core):
+    """Time the fp64 oracle on a bounded sample of the same workload's chains."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    nchains = max(1, cores * chains_per_core)
+    cu = x["cu_seqlens_host"]
+    N, H = len(cu) - 1, x["heads"]
+    chains = [(i % N, (i * 7) % H) for i in range(nchains)]
+    to = lambda t: t.detach().cpu().double().numpy()
+    qs, ks, vs, gs, bs, lens = [], [], [], [], [], []
+    for n, h in chains:
+        a, b = cu[n], cu[n + 1]
+        qs.append(to(x["q"][a:b, h])); ks.append(to(x["k"][a:b, h])); vs.append(to(x["v"][a:b, h]))
+        gs.append(to(x["g"][a:b, h])); bs.append(to(x["beta"][a:b, h])); lens.append(b - a)
+    cu2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    cat = lambda xs: np.concatenate(xs, axis=0)[:, None]
+    args = (cat(qs), cat(ks), cat(vs), cat(gs), np.concatenate(bs)[:, None])
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.recurrent(*args, cu_seqlens=cu2, nthreads=cores)
+    dt = time.perf_counter() - t0
+    token_heads = int(cu2[-1])
+    return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nchains} (sequence, head) chains of {lens[0]} tokens each "
+                      f"({token_heads} token-heads, fp64 token loop, OpenMP over chains); "
+                      f"value = token-heads/s divided by {H} heads",
+            "token_heads_per_s": token_heads / dt, "seconds": dt}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_delta_rule_10_amd as kda
+    import kda_inputs as ki
+    kda.library()
+    torch.cuda.set_device(0)
+
+    pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup)
+    H, tokens, N = pre["heads"], pre["tokens"], pre["seqs"]
+    ms = pre["ms"]
+    tok_s = tokens / (ms * 1e-3)
+    tflops = tok_s * H * FLOP_PER_TOKEN_HEAD / 1e12
+    alg_bytes = tokens * H * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES * (
+        2 if pre["x"]["initial_state"] is not None else 1)
+    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": N, "seq_len": tokens // N,
+                   "heads": H, "head_dim": D, "chunk": C, "state": "fp32"},
+        "tflops": tflops,
+        "mfma_peak_frac": tflops / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel<bf16,128>",
+                     "bytes_per_launch": alg_bytes},
+    }
+    if not args.no_decode:
+        line["decode"] = time_decode(kda, ki, args.decode_steps)
+        line["decode"]["workload"] = DECODE_WORKLOAD
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,301 @@
+"""MI355X (gfx950) Kimi Delta Attention: chunked prefill, recurrent decode, state pools.
+
+A thin ctypes binding over ``libkda.so`` (C ABI in ``include/kda.h``).  This
+module only marshals arguments: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the current stream.
+If the library is missing the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KDAError",
+    "chunk_fwd",
+    "chunk_fwd_workspace_size",
+    "recurrent_step",
+    "state_io",
+    "state_bytes",
+    "library",
+    "LIB_PATH",
+    "KDA_F32",
+    "KDA_BF16",
+    "STATE_ZERO",
+    "STATE_COPY",
+    "STATE_GATHER",
+    "STATE_SCATTER",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATE_ZERO, STATE_COPY, STATE_GATHER, STATE_SCATTER = 0, 1, 2, 3
+_STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_UNSUPPORTED",
+           3: "KDA_ERROR_WORKSPACE", 4: "KDA_ERROR_LAUNCH"}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+class ChunkFwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p),
+        ("final_state", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("segments", ctypes.c_int32),
+    ]
+
+
+class RecurrentStepArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32),
+        ("o", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def library(path: str = LIB_PATH):
+    """Open libkda.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkda.so not found at {path}; build it with "
+                           "`python -m gated_delta_rule_10_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkFwdArgs),
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs), ctypes.c_void_p]
+    lib.kda_state_io.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_void_p]
+    for fn in ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_recurrent_step",
+               "kda_state_io"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.kda_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+    lib.kda_state_bytes.restype = ctypes.c_size_t
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t=None) -> ctypes.c_void_p:
+    dev = t.device if t is not None else None
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise KDAError(st, what)
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _chunk_args(q, N, cu_seqlens, cu_seqlens_host, scale, segments):
+    """Fill the size fields of kda_chunk_fwd_args; returns (args, host_array)."""
+    T, H, D = q.shape
+    a = ChunkFwdArgs()
+    host = None
+    a.num_seqs = N
+    if cu_seqlens_host is not None:
+        host = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+        a.cu_seqlens_host = host
+        a.seq_len = 0
+    else:
+        if T % N:
+            raise ValueError("T_total must be a multiple of the number of sequences")
+        a.seq_len = T // N
+    a.num_heads, a.head_dim, a.chunk_size = H, D, 64
+    a.io_dtype = _dtype_code(q.dtype)
+    a.scale = float(scale)
+    a.segments = int(segments)
+    return a, host
+
+
+def chunk_fwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None, segments=0) -> int:
+    """Workspace bytes for a prefill of ``q``'s shape (host only, no GPU work)."""
+    lib = library()
+    N = len(cu_seqlens_host) - 1 if cu_seqlens_host is not None else (num_seqs or 1)
+    a, host = _chunk_args(q, N, None, cu_seqlens_host, 1.0, segments)
+    if cu_seqlens_host is not None:
+        a.cu_seqlens = 16  # non-null marker: only the host copy is read here
+    out = ctypes.c_size_t(0)
+    _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out)),
+           "kda_chunk_fwd_workspace_size")
+    del host
+    return int(out.value)
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+              output_final_state=True, scale=1.0, segments=0, num_seqs=None, out=None,
+              final_state=None, workspace=None):
+    """Chunkwise KDA prefill forward.
+
+    q, k, v: [T, H, 128] bf16 or fp32 (same dtype); g: [T, H, 128] fp32 log-decay;
+    beta: [T, H] fp32; cu_seqlens: int32 [N+1] on the device (packed batch) or None
+    for ``num_seqs`` (default 1, or initial_state.shape[0]) sequences of equal
+    length; initial_state: [N, H, 128, 128] fp32 or None.
+    Returns (o [T, H, 128], final_state [N, H, 128, 128] fp32 or None).
+    """
+    lib = library()
+    _need(q, "q", ndim=3)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, dtype=q.dtype, ndim=3)
+    _need(g, "g", dtype=torch.float32, ndim=3)
+    _need(beta, "beta", dtype=torch.float32, ndim=2)
+    T, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape or beta.shape != (T, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = num_seqs or (initial_state.shape[0] if initial_state is not None else 1)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dtype=torch.float32, ndim=4)
+        if initial_state.shape != (N, H, D, D):
+            raise ValueError(f"initial_state must be [{N}, {H}, {D}, {D}]")
+    o = out if out is not None else torch.empty_like(q)
+    if not output_final_state:
+        final_state = None
+    elif final_state is None:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=q.device)
+    if cu_seqlens is not None and cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.tolist()  # one device-to-host copy
+    a, host = _chunk_args(q, N, cu_seqlens, cu_seqlens_host, scale, segments)
+    a.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.g, a.beta = g.data_ptr(), beta.data_ptr()
+    a.initial_state = None if initial_state is None else initial_state.data_ptr()
+    a.final_state = None if final_state is None else final_state.data_ptr()
+    a.o = o.data_ptr()
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws_bytes)),
+           "kda_chunk_fwd_workspace_size")
+    if ws_bytes.value:
+        if workspace is None or workspace.numel() < ws_bytes.value:
+            workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel()
+    _check(lib.kda_chunk_fwd(ctypes.byref(a), _stream(q)), "kda_chunk_fwd")
+    del host
+    return o, final_state
+
+
+def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=None):
+    """One decode token per row, applied in place to ``state`` ([slots, H, 128, 128] fp32).
+
+    q, k, v: [B, H, 128]; g: [B, H, 128] fp32; beta: [B, H] fp32;
+    state_indices: int32 [B] (slot per row; negative = skip) or None (identity).
+    Returns o [B, H, 128].
+    """
+    lib = library()
+    _need(q, "q", ndim=3)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, dtype=q.dtype, ndim=3)
+    _need(g, "g", dtype=torch.float32, ndim=3)
+    _need(beta, "beta", dtype=torch.float32, ndim=2)
+    _need(state, "state", dtype=torch.float32, ndim=4)
+    B, H, D = q.shape
+    if state_indices is not None:
+        _need(state_indices, "state_indices", dtype=torch.int32, ndim=1)
+    o = out if out is not None else torch.empty_like(q)
+    a = RecurrentStepArgs()
+    a.batch, a.num_heads, a.head_dim = B, H, D
+    a.io_dtype = _dtype_code(q.dtype)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
+    a.state = state.data_ptr()
+    a.state_indices = None if state_indices is None else state_indices.data_ptr()
+    a.num_slots = state.shape[0]
+    a.o = o.data_ptr()
+    _check(lib.kda_recurrent_step(ctypes.byref(a), _stream(q)), "kda_recurrent_step")
+    return o
+
+
+def state_io(op: int, dst, src=None, indices=None, count=None):
+    """Zero / copy / gather / scatter states between pools ([slots, H, 128, 128])."""
+    lib = library()
+    _need(dst, "dst", ndim=4)
+    if src is not None:
+        _need(src, "src", ndim=4)
+    if indices is not None:
+        _need(indices, "indices", dtype=torch.int32, ndim=1)
+    H, D = dst.shape[1], dst.shape[2]
+    if count is None:
+        count = indices.shape[0] if indices is not None else (
+            src.shape[0] if src is not None and op == STATE_COPY else dst.shape[0])
+    st = lib.kda_state_io(int(op), _ptr(src), _dtype_code(src.dtype) if src is not None else 0,
+                          src.shape[0] if src is not None else 0, _ptr(dst),
+                          _dtype_code(dst.dtype), dst.shape[0], _ptr(indices), int(count), H, D,
+                          _stream(dst))
+    _check(st, "kda_state_io")
+    return dst
+
+
+def state_bytes(num_heads: int, head_dim: int = 128, dtype: torch.dtype = torch.float32) -> int:
+    return int(library().kda_state_bytes(num_heads, head_dim, _dtype_code(dtype)))

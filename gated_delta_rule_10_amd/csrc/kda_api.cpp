@@ -1,0 +1,165 @@
+// kda_api.cpp -- the extern "C" entry points declared in include/kda.h:
+// host-side validation (before anything is enqueued), workspace planning and
+// dispatch to the HIP launchers.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+
+kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH; }
+
+// Shared checks of the prefill arguments; fills the token count on success.
+// The workspace query reads sizes only, so it skips the pointer checks.
+kda_status check_chunk_args(const kda_chunk_fwd_args *a, int64_t *total_tokens,
+                            bool check_pointers) {
+  if (!a) return KDA_ERROR_INVALID_VALUE;
+  if (a->num_seqs < 1 || a->num_heads < 1) return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(a->io_dtype)) return KDA_ERROR_INVALID_VALUE;
+  if (!isfinite(a->scale)) return KDA_ERROR_INVALID_VALUE;
+  if (a->segments < 0) return KDA_ERROR_INVALID_VALUE;
+  if (a->head_dim != KDA_HEAD_DIM || a->chunk_size != KDA_CHUNK) return KDA_ERROR_UNSUPPORTED;
+  int64_t T = 0;
+  if (a->cu_seqlens) {
+    if (!a->cu_seqlens_host || ((uintptr_t)a->cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
+    if (a->cu_seqlens_host[0] != 0) return KDA_ERROR_INVALID_VALUE;
+    for (int32_t i = 0; i < a->num_seqs; ++i)
+      if (a->cu_seqlens_host[i + 1] < a->cu_seqlens_host[i]) return KDA_ERROR_INVALID_VALUE;
+    T = a->cu_seqlens_host[a->num_seqs];
+  } else {
+    if (a->seq_len < 0) return KDA_ERROR_INVALID_VALUE;
+    T = (int64_t)a->num_seqs * a->seq_len;
+    if (T > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  }
+  // every element offset must fit comfortably in 64-bit index math; tokens in int32
+  if ((int64_t)a->num_seqs * a->num_heads > INT32_MAX / 2) return KDA_ERROR_INVALID_VALUE;
+  if (T > 0 && check_pointers) {
+    const void *req[] = {a->q, a->k, a->v, a->g, a->o};
+    for (const void *p : req)
+      if (!p || !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->beta || !aligned(a->beta, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (a->o == a->q || a->o == a->k || a->o == a->v) return KDA_ERROR_INVALID_VALUE;
+  }
+  if (check_pointers) {
+    if (a->initial_state && !aligned16(a->initial_state)) return KDA_ERROR_INVALID_VALUE;
+    if (a->final_state && !aligned16(a->final_state)) return KDA_ERROR_INVALID_VALUE;
+  }
+  *total_tokens = T;
+  return KDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_SUCCESS: return "KDA_SUCCESS";
+    case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+    case KDA_ERROR_UNSUPPORTED: return "KDA_ERROR_UNSUPPORTED";
+    case KDA_ERROR_WORKSPACE: return "KDA_ERROR_WORKSPACE";
+    case KDA_ERROR_LAUNCH: return "KDA_ERROR_LAUNCH";
+  }
+  return "KDA_ERROR_UNKNOWN";
+}
+
+const char *kda_version(void) { return "libkda 0.1 (gfx950)"; }
+
+size_t kda_state_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype) {
+  if (num_heads < 1 || head_dim < 1 || !valid_dtype(dtype)) return 0;
+  return (size_t)num_heads * head_dim * head_dim * (dtype == KDA_F32 ? 4u : 2u);
+}
+
+kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *a, size_t *bytes) {
+  if (!bytes) return KDA_ERROR_INVALID_VALUE;
+  int64_t T = 0;
+  const kda_status st = check_chunk_args(a, &T, false);
+  if (st != KDA_SUCCESS) return st;
+  kda::ChunkPlan plan;
+  const kda_status ps = kda::plan_chunk_fwd(*a, &plan);
+  if (ps != KDA_SUCCESS) return ps;
+  *bytes = plan.total_bytes;
+  return KDA_SUCCESS;
+}
+
+kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a, void *stream) {
+  int64_t T = 0;
+  const kda_status st = check_chunk_args(a, &T, true);
+  if (st != KDA_SUCCESS) return st;
+  kda::ChunkPlan plan;
+  const kda_status ps = kda::plan_chunk_fwd(*a, &plan);
+  if (ps != KDA_SUCCESS) return ps;
+  if (plan.total_bytes > 0) {
+    if (!a->workspace || a->workspace_bytes < plan.total_bytes) return KDA_ERROR_WORKSPACE;
+    if (((uintptr_t)a->workspace & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
+  }
+  return launch_status(kda::launch_chunk_fwd(*a, plan, (hipStream_t)stream));
+}
+
+kda_status kda_recurrent_step(const kda_recurrent_step_args *a, void *stream) {
+  if (!a) return KDA_ERROR_INVALID_VALUE;
+  if (a->batch < 0 || a->num_heads < 1 || a->num_slots < 0) return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(a->io_dtype) || !isfinite(a->scale)) return KDA_ERROR_INVALID_VALUE;
+  if (a->head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
+  if ((int64_t)a->batch * a->num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if (!a->state_indices && a->batch > a->num_slots) return KDA_ERROR_INVALID_VALUE;
+  if (a->batch > 0) {
+    // the step reads q, k, v, g, beta and writes o element by element; the state
+    // is accessed in 16-byte vectors
+    const uintptr_t es = a->io_dtype == KDA_F32 ? 4u : 2u;
+    const void *io[] = {a->q, a->k, a->v, a->o};
+    for (const void *p : io)
+      if (!p || !aligned(p, es)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->g || !aligned(a->g, 4) || !a->beta || !aligned(a->beta, 4))
+      return KDA_ERROR_INVALID_VALUE;
+    if (!a->state || !aligned16(a->state)) return KDA_ERROR_INVALID_VALUE;
+    if (a->state_indices && ((uintptr_t)a->state_indices & 3u)) return KDA_ERROR_INVALID_VALUE;
+  }
+  return launch_status(kda::launch_recurrent_step(*a, (hipStream_t)stream));
+}
+
+kda_status kda_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
+                        int32_t src_slots, void *dst, kda_dtype dst_dtype, int32_t dst_slots,
+                        const int32_t *indices, int32_t count, int32_t num_heads,
+                        int32_t head_dim, void *stream) {
+  if (op != KDA_STATE_ZERO && op != KDA_STATE_COPY && op != KDA_STATE_GATHER &&
+      op != KDA_STATE_SCATTER)
+    return KDA_ERROR_INVALID_VALUE;
+  if (count < 0 || num_heads < 1 || src_slots < 0 || dst_slots < 0)
+    return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(dst_dtype) || (op != KDA_STATE_ZERO && !valid_dtype(src_dtype)))
+    return KDA_ERROR_INVALID_VALUE;
+  if (head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
+  if ((int64_t)count * 64 > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if (count == 0) return KDA_SUCCESS;
+  if (!dst || !aligned16(dst)) return KDA_ERROR_INVALID_VALUE;
+  if (op != KDA_STATE_ZERO && (!src || !aligned16(src))) return KDA_ERROR_INVALID_VALUE;
+  if ((op == KDA_STATE_GATHER || op == KDA_STATE_SCATTER) && !indices)
+    return KDA_ERROR_INVALID_VALUE;
+  if (indices && ((uintptr_t)indices & 3u)) return KDA_ERROR_INVALID_VALUE;
+  // the positions i themselves index a pool: they must lie inside it
+  if (op == KDA_STATE_COPY && (count > src_slots || count > dst_slots))
+    return KDA_ERROR_INVALID_VALUE;
+  if (op == KDA_STATE_GATHER && count > dst_slots) return KDA_ERROR_INVALID_VALUE;
+  if (op == KDA_STATE_SCATTER && count > src_slots) return KDA_ERROR_INVALID_VALUE;
+  if (op == KDA_STATE_ZERO && !indices && count > dst_slots) return KDA_ERROR_INVALID_VALUE;
+  if (op != KDA_STATE_ZERO) {
+    // source and destination ranges must not overlap
+    const size_t sb = kda_state_bytes(num_heads, head_dim, src_dtype) * (size_t)src_slots;
+    const size_t db = kda_state_bytes(num_heads, head_dim, dst_dtype) * (size_t)dst_slots;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + db && d0 < s0 + sb) return KDA_ERROR_INVALID_VALUE;
+  }
+  const int64_t elems = (int64_t)num_heads * head_dim * head_dim;
+  return launch_status(kda::launch_state_io(op, src, src_dtype, src_slots, dst, dst_dtype,
+                                            dst_slots, indices, count, elems,
+                                            (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// kda_internal.h -- host-side launchers shared between the libkda sources.
+// Every launcher assumes its arguments were validated by kda_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Decode step: one workgroup per (row, head).
+hipError_t launch_recurrent_step(const kda_recurrent_step_args &a, hipStream_t stream);
+
+// State pool copy/convert/zero.
+hipError_t launch_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
+                           int32_t src_slots, void *dst, kda_dtype dst_dtype,
+                           int32_t dst_slots, const int32_t *indices, int32_t count,
+                           int64_t elems_per_state, hipStream_t stream);
+
+// Chunked prefill plan, computed on the host from sizes only.
+struct ChunkPlan {
+  int32_t num_seqs = 0;
+  int32_t heads = 0;
+  int64_t total_tokens = 0;
+  bool varlen = false;
+  int32_t segments = 1;          // segments per sequence (1 = no split)
+  int64_t max_chunks = 0;        // chunks of the longest sequence
+  // workspace layout (byte offsets)
+  size_t order_off = 0, order_bytes = 0;      // int32 [N] longest-first sequence order
+  size_t seg_state_off = 0, seg_state_bytes = 0;  // fp32 segment M / S~ / S_in buffers
+  size_t total_bytes = 0;
+};
+
+kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan);
+hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
+                            hipStream_t stream);
+
+}  // namespace kda

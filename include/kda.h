@@ -1,0 +1,210 @@
+/*
+ * kda.h -- C ABI of libkda, an MI355X (gfx950) implementation of the Kimi Delta
+ * Attention (KDA) token mixer: the chunkwise-parallel prefill forward and the
+ * single-token recurrent decode step, plus state-pool copies.
+ *
+ * Pages this interface follows (cited by title and section):
+ *  [P1] "How Kimi K3 Engineered Its Way to the Frontier": section "How KDA
+ *       updates its state" (recurrence order forget -> erase+write -> read;
+ *       decay per key channel; state layout S[B,HV,K,V], gate g[B,T,HV,K] in
+ *       natural-log space); section "What the hybrid saves" (per-layer state of
+ *       96 heads x 128 x 128; FlashKDA accepts bf16 or fp32 states); section
+ *       "FlashKDA steps the state once per 16 tokens" (chunkwise form, result
+ *       equal to the token loop; forward-only prefill with head dim fixed at
+ *       128).
+ *  [P2] "Kimi K3: Open Frontier Intelligence", section 6: the KDA equation
+ *       S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *       o_t = S_t^T q_t.
+ *  [P3] "Kimi K3 -- Training and Infrastructure Notes": section 4.1 (segment
+ *       transitions evaluated independently of the incoming state and composed
+ *       exactly afterwards, inside one device); section 4.5 (decode updates the
+ *       state in place; states stored head by head contiguously; checkpoints are
+ *       read-only snapshots copied into a private running state).
+ *  [P4] "Kimi K3: a 2.8T open model ...", subsection "FlashKDA: the equation,
+ *       shipped as a kernel": query, key, value, gate and beta in, optional
+ *       recurrent state in and out, variable-length batches through cumulative
+ *       sequence lengths, bf16 activations with fp32 parameters.
+ *
+ * Conventions shared by every entry point
+ *  - Layouts are row-major with the innermost index last.  Tokens of all
+ *    sequences are packed: q, k, v, o are [T_total, H, 128]; g is
+ *    [T_total, H, 128]; beta is [T_total, H]; states are [N, H, 128, 128] with
+ *    rows indexed by key channel and columns by value channel, each head's
+ *    128 x 128 block contiguous.  A fixed-length batch [B, T, ...] is the same
+ *    memory with N = B and T_total = B * T.
+ *  - g is the natural-log decay (alpha = exp(g), g <= 0 expected); beta is the
+ *    post-sigmoid write strength in [0, 1].  o = scale * S_t^T q_t; the pages'
+ *    formula has scale = 1.
+ *  - Ownership: the caller allocates and owns every buffer (device memory unless
+ *    a field says host).  The library allocates no device memory, keeps no
+ *    pointer after a call returns and holds no mutable global state.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Work is enqueued asynchronously; no call synchronises the host.
+ *  - Errors: arguments are validated on the host before anything is enqueued.
+ *    An invalid call returns a status other than KDA_SUCCESS and touches no
+ *    buffer.  A launch failure reported by the HIP runtime returns
+ *    KDA_ERROR_LAUNCH.  Values inside device buffers (cu_seqlens contents,
+ *    slot indices) cannot be checked on the host; how each call treats bad
+ *    device-side values is stated at the call.  No C++ exception crosses the ABI.
+ *  - Alignment: state pools and the prefill's q, k, v, g, o must be 16-byte
+ *    aligned; beta needs 4 bytes; the decode step's q, k, v, o need their
+ *    element size and g 4 bytes.
+ *  - Thread safety: calls are reentrant.  Two calls that write the same buffer
+ *    must be ordered by the caller (same stream or events).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_SUCCESS = 0,
+  KDA_ERROR_INVALID_VALUE = 1, /* null pointer, bad size, bad alignment, bad offsets */
+  KDA_ERROR_UNSUPPORTED = 2,   /* a valid request this build does not implement     */
+  KDA_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required        */
+  KDA_ERROR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch          */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Head dimension (d_k = d_v) and chunk length this build implements. */
+#define KDA_HEAD_DIM 128
+#define KDA_CHUNK 64
+
+/* ------------------------------------------------------------------------
+ * Chunkwise prefill forward ([P1] "FlashKDA steps the state once per 16
+ * tokens"; [P2] section 6; [P4] "FlashKDA: the equation, shipped as a kernel").
+ *
+ * For every sequence n and head h, starting from S = initial_state[n, h] (zero
+ * when initial_state is NULL) it computes, for each token t of the sequence in
+ * order, the KDA recurrence
+ *     S <- (I - beta_t k_t k_t^T) Diag(exp(g_t)) S + beta_t k_t v_t^T
+ *     o_t = scale * S^T q_t
+ * and stores the last S into final_state[n, h].  Tokens are processed in chunks
+ * of `chunk_size` that start at each sequence start; the result equals the
+ * token loop up to rounding.  The state is carried in fp32; products of the
+ * chunk algebra run on matrix cores in bf16 (io_dtype KDA_BF16) or fp32
+ * (io_dtype KDA_F32) with fp32 accumulation; o is written in io_dtype (bf16
+ * rounded to nearest-even).
+ *
+ * Intra-device segment parallelism ([P3] section 4.1): with `segments` > 1
+ * (or 0 = chosen automatically) long sequences are split into segments whose
+ * transitions are evaluated from a zero incoming state in parallel, composed in
+ * order, and then re-run from their exact incoming states.  The result is the
+ * same recurrence.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_chunk_fwd_args {
+  int32_t num_seqs;               /* N >= 1                                              */
+  int32_t seq_len;                /* tokens per sequence when cu_seqlens == NULL (>= 0)  */
+  const int32_t *cu_seqlens;      /* device [N+1] packed offsets, or NULL (fixed length) */
+  const int32_t *cu_seqlens_host; /* host copy of cu_seqlens; required with cu_seqlens.  */
+                                  /* Must be 0-based, non-decreasing, the device copy     */
+                                  /* must hold the same values (not checked).            */
+  int32_t num_heads;              /* H >= 1                                              */
+  int32_t head_dim;               /* must be KDA_HEAD_DIM                                */
+  int32_t chunk_size;             /* must be KDA_CHUNK                                   */
+  kda_dtype io_dtype;             /* dtype of q, k, v and o                              */
+  float scale;                    /* output scale (1.0 = the pages' formula)             */
+  const void *q;                  /* [T_total, H, 128] io_dtype                          */
+  const void *k;                  /* [T_total, H, 128] io_dtype                          */
+  const void *v;                  /* [T_total, H, 128] io_dtype                          */
+  const float *g;                 /* [T_total, H, 128] log-decay                         */
+  const float *beta;              /* [T_total, H]                                        */
+  const float *initial_state;     /* [N, H, 128, 128] or NULL = zeros                    */
+  float *final_state;             /* [N, H, 128, 128] or NULL = not written.  May equal  */
+                                  /* initial_state (in-place update).                    */
+  void *o;                        /* [T_total, H, 128] io_dtype; must not alias inputs   */
+  void *workspace;                /* device scratch of >= the queried size, 256-B aligned */
+  size_t workspace_bytes;
+  int32_t segments;               /* 0 = automatic, 1 = never split, > 1 = split each    */
+                                  /* sequence into this many segments (capped so every   */
+                                  /* segment holds at least one chunk)                   */
+} kda_chunk_fwd_args;
+
+/* Bytes of workspace kda_chunk_fwd needs for these arguments (pointers are not
+ * read; only sizes, cu_seqlens_host and segments).  Host only, no HIP call. */
+kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *args, size_t *bytes);
+
+/* Enqueue the prefill forward on `stream`.  Errors: KDA_ERROR_INVALID_VALUE for
+ * null required pointers, negative sizes, misaligned pointers, cu_seqlens_host
+ * that is not 0-based and non-decreasing, or T_total * H * 128 beyond 2^31;
+ * KDA_ERROR_UNSUPPORTED for head_dim != 128 or chunk_size != 64;
+ * KDA_ERROR_WORKSPACE when the workspace is smaller than queried. */
+kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Recurrent decode step ([P1] "How KDA updates its state"; [P3] section 4.5:
+ * the state is updated in place at every decoding step).
+ *
+ * For each row b with slot s = state_indices[b] (s = b when state_indices is
+ * NULL) and each head h, one token is applied in place to state[s, h]:
+ *     S <- Diag(exp(g)) S;  r = S^T k;  S <- S + beta k (v - r)^T;
+ *     o = scale * S^T q
+ * Rows whose slot is negative or >= num_slots are skipped: their state is not
+ * touched and their o rows are not written.  Two rows naming the same slot race
+ * (caller error; no out-of-bounds access results).
+ * ---------------------------------------------------------------------- */
+typedef struct kda_recurrent_step_args {
+  int32_t batch;                  /* B >= 0 rows, one token each                         */
+  int32_t num_heads;              /* H >= 1                                              */
+  int32_t head_dim;               /* must be KDA_HEAD_DIM                                */
+  kda_dtype io_dtype;             /* dtype of q, k, v and o                              */
+  float scale;
+  const void *q;                  /* [B, H, 128] io_dtype                                */
+  const void *k;                  /* [B, H, 128] io_dtype                                */
+  const void *v;                  /* [B, H, 128] io_dtype                                */
+  const float *g;                 /* [B, H, 128]                                         */
+  const float *beta;              /* [B, H]                                              */
+  float *state;                   /* pool [num_slots, H, 128, 128] fp32, in place        */
+  const int32_t *state_indices;   /* device [B] or NULL (identity, needs B <= num_slots) */
+  int32_t num_slots;
+  void *o;                        /* [B, H, 128] io_dtype                                */
+} kda_recurrent_step_args;
+
+kda_status kda_recurrent_step(const kda_recurrent_step_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
+ * State-pool copies ([P3] section 4.5: states are stored head by head
+ * contiguously; a cache hit copies a read-only snapshot into the request's
+ * private running state; new checkpoints are written to fresh slots).
+ * One "state" is H x 128 x 128 elements.  For i in [0, count):
+ *   KDA_STATE_ZERO    dst[slot] = 0,              slot = indices ? indices[i] : i
+ *   KDA_STATE_COPY    dst[i] = src[i]
+ *   KDA_STATE_GATHER  dst[i] = src[indices[i]]    (restore a snapshot)
+ *   KDA_STATE_SCATTER dst[indices[i]] = src[i]    (save a checkpoint)
+ * converting between src_dtype and dst_dtype (fp32 -> bf16 rounds to nearest
+ * even).  A negative index, or one >= the slot count of the indexed pool,
+ * skips that i.  src and dst must not overlap.
+ * ---------------------------------------------------------------------- */
+typedef enum kda_state_op {
+  KDA_STATE_ZERO = 0,
+  KDA_STATE_COPY = 1,
+  KDA_STATE_GATHER = 2,
+  KDA_STATE_SCATTER = 3
+} kda_state_op;
+
+kda_status kda_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
+                        int32_t src_slots, void *dst, kda_dtype dst_dtype,
+                        int32_t dst_slots, const int32_t *indices, int32_t count,
+                        int32_t num_heads, int32_t head_dim, void *stream);
+
+/* Bytes of one state (H x head_dim x head_dim elements of dtype), e.g. 3 MiB
+ * for 96 heads in bf16 ([P1] "What the hybrid saves").  0 for invalid input. */
+size_t kda_state_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype);
+
+/* Human-readable name of a status code (static string). */
+const char *kda_status_string(kda_status status);
+
+/* Library version string (static). */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

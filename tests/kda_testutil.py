@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests (not a test module)."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+# Tolerances of max|x_gpu - x_ref| / max|x_ref| per output tensor: 2e-2 for bf16
+# inputs with an fp32 state, 1e-4 for fp32 inputs.
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def announce(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in GPU output"
+    denom = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / denom) if denom > 0 else float(np.max(np.abs(x)))
+
+
+def to64(t) -> np.ndarray:
+    return t.detach().to("cpu").double().numpy()
+
+
+def oracle_chains(inp: dict, chains, scale=1.0, nthreads=0):
+    """Run the oracle on selected (sequence n, head h) chains of a prefill batch.
+
+    Returns {(n, h): (o [L, 128], S_final [128, 128])} computed from exactly the
+    tensors in ``inp`` (the values the GPU received)."""
+    cu = inp["cu_seqlens_host"]
+    # gather every chain into one packed single-head batch for one oracle call
+    qs, ks, vs, gs, bs, s0s, lens = [], [], [], [], [], [], []
+    for n, h in chains:
+        a, b = cu[n], cu[n + 1]
+        qs.append(to64(inp["q"][a:b, h]))
+        ks.append(to64(inp["k"][a:b, h]))
+        vs.append(to64(inp["v"][a:b, h]))
+        gs.append(to64(inp["g"][a:b, h]))
+        bs.append(to64(inp["beta"][a:b, h]))
+        s0 = inp.get("initial_state")
+        s0s.append(to64(s0[n, h]) if s0 is not None else np.zeros((128, 128)))
+        lens.append(b - a)
+    cu2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    cat = lambda xs: np.concatenate(xs, axis=0)[:, None]
+    o, sf = oracle.recurrent(cat(qs), cat(ks), cat(vs), cat(gs),
+                             np.concatenate(bs)[:, None], cu_seqlens=cu2,
+                             initial_state=np.stack(s0s)[:, None], scale=scale,
+                             nthreads=nthreads)
+    out = {}
+    for i, (n, h) in enumerate(chains):
+        out[(n, h)] = (o[cu2[i]:cu2[i + 1], 0], sf[i, 0])
+    return out

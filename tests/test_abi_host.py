@@ -1,0 +1,152 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, rejects invalid arguments before touching the GPU, and sizes
+states as the pages' memory accounting says ("How Kimi K3 Engineered Its Way to
+the Frontier", section "What the hybrid saves")."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_10_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_constants.json")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.fail("libkda.so is not built (run __graft_entry__.build())")
+    return kda.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_recurrent_step", "kda_state_io"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        getattr(lib, n)  # resolvable through ctypes
+
+
+def test_status_strings_and_version(lib):
+    for code, name in [(0, b"KDA_SUCCESS"), (1, b"KDA_ERROR_INVALID_VALUE"),
+                       (2, b"KDA_ERROR_UNSUPPORTED"), (3, b"KDA_ERROR_WORKSPACE"),
+                       (4, b"KDA_ERROR_LAUNCH")]:
+        assert lib.kda_status_string(code) == name
+    assert b"gfx950" in lib.kda_version()
+
+
+def test_state_bytes_match_page_accounting(lib):
+    c = json.load(open(GOLDEN))["state_memory"]
+    bf16_layer = lib.kda_state_bytes(c["heads"], c["head_dim"], kda.KDA_BF16)
+    assert bf16_layer == c["bf16_state_bytes_per_layer"]  # 3 MiB
+    per_request = c["kda_layers"] * (bf16_layer + c["conv_cache_bytes_per_layer"]) / 2**20
+    assert abs(per_request - c["per_request_mib_printed"]) < 0.005
+    assert lib.kda_state_bytes(c["heads"], c["head_dim"], kda.KDA_F32) == 2 * bf16_layer
+    assert lib.kda_state_bytes(0, 128, kda.KDA_F32) == 0
+
+
+def _args(**kw):
+    a = kda.ChunkFwdArgs()
+    a.num_seqs, a.seq_len, a.num_heads, a.head_dim, a.chunk_size = 1, 64, 2, 128, 64
+    a.io_dtype, a.scale = kda.KDA_BF16, 1.0
+    fake = 1 << 20  # 16-byte aligned non-null placeholder; never dereferenced on error
+    a.q = a.k = a.v = a.g = a.beta = fake
+    a.o = fake + 4096
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, 2),
+    ("chunk_size", 16, 2),
+    ("num_seqs", 0, 1),
+    ("num_heads", 0, 1),
+    ("seq_len", -1, 1),
+    ("io_dtype", 7, 1),
+    ("segments", -2, 1),
+    ("q", 0, 1),
+    ("g", (1 << 20) + 4, 1),  # misaligned
+    ("beta", (1 << 20) + 2, 1),  # beta needs 4 bytes
+    ("o", 1 << 20, 1),        # aliases q
+    ("scale", float("nan"), 1),
+])
+def test_chunk_fwd_rejects_invalid_arguments(lib, field, value, status):
+    a = _args(**{field: value})
+    assert lib.kda_chunk_fwd(ctypes.byref(a), None) == status
+    size = ctypes.c_size_t(0)
+    pointer_field = field in ("q", "g", "beta", "o")  # the size query reads no pointer
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(size)) == (
+        0 if pointer_field else status)
+
+
+def test_chunk_fwd_rejects_bad_cu_seqlens(lib):
+    for host in ([1, 5, 9], [0, 9, 5]):
+        arr = (ctypes.c_int32 * 3)(*host)
+        a = _args(num_seqs=2, cu_seqlens=1 << 20)
+        a.cu_seqlens_host = arr
+        assert lib.kda_chunk_fwd(ctypes.byref(a), None) == 1
+    a = _args(num_seqs=2, cu_seqlens=1 << 20)  # device offsets without a host copy
+    assert lib.kda_chunk_fwd(ctypes.byref(a), None) == 1
+
+
+def test_workspace_size_and_shortfall(lib):
+    lens = [0, 100, 7, 4096]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    a = _args(num_seqs=len(lens), cu_seqlens=1 << 20)
+    a.cu_seqlens_host = arr
+    size = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(size)) == 0
+    assert size.value >= 4 * len(lens)  # the longest-first sequence order
+    a.workspace, a.workspace_bytes = 1 << 20, 0
+    assert lib.kda_chunk_fwd(ctypes.byref(a), None) == 3
+
+
+def test_recurrent_step_rejects_invalid_arguments(lib):
+    def args(**kw):
+        a = kda.RecurrentStepArgs()
+        a.batch, a.num_heads, a.head_dim, a.io_dtype, a.scale = 4, 2, 128, kda.KDA_BF16, 1.0
+        fake = 1 << 20
+        a.q = a.k = a.v = a.g = a.beta = a.state = a.o = fake
+        a.num_slots = 4
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return a
+    assert lib.kda_recurrent_step(ctypes.byref(args(head_dim=96)), None) == 2
+    assert lib.kda_recurrent_step(ctypes.byref(args(batch=-1)), None) == 1
+    assert lib.kda_recurrent_step(ctypes.byref(args(num_slots=3)), None) == 1  # identity needs B<=slots
+    assert lib.kda_recurrent_step(ctypes.byref(args(state=0)), None) == 1
+    assert lib.kda_recurrent_step(ctypes.byref(args(state_indices=(1 << 20) + 2)), None) == 1
+    assert lib.kda_recurrent_step(ctypes.byref(args(batch=0, q=0)), None) == 0  # nothing to do
+    assert lib.kda_recurrent_step(ctypes.byref(args(state=(1 << 20) + 8)), None) == 1
+    assert lib.kda_recurrent_step(ctypes.byref(args(q=(1 << 20) + 1)), None) == 1
+
+
+def test_state_io_rejects_invalid_arguments(lib):
+    f = lib.kda_state_io
+    base = 1 << 24
+    # op out of range, gather without indices, overlapping ranges, unsupported dim
+    assert f(9, base, 0, 2, base * 2, 0, 2, None, 1, 4, 128, None) == 1
+    assert f(kda.STATE_GATHER, base, 0, 2, base * 2, 0, 2, None, 1, 4, 128, None) == 1
+    assert f(kda.STATE_COPY, base, 0, 2, base + 4096, 0, 2, None, 1, 4, 128, None) == 1
+    assert f(kda.STATE_COPY, base, 0, 2, base * 4, 0, 2, None, 1, 4, 64, None) == 2
+    assert f(kda.STATE_COPY, base, 0, 1, base * 4, 0, 2, None, 2, 4, 128, None) == 1  # count > src
+    assert f(kda.STATE_ZERO, None, 0, 0, base, 0, 2, None, 0, 4, 128, None) == 0  # empty

@@ -1,0 +1,184 @@
+"""GPU parity of the chunked prefill (kda_chunk_fwd) against the fp64 oracle.
+
+The kernel evaluates the chunkwise form of the recurrence ("How Kimi K3
+Engineered Its Way to the Frontier", section "FlashKDA steps the state once per
+16 tokens"); the oracle is the token loop, so these tests also check that the
+chunked schedule reproduces the loop.  Small cases are checked element by
+element in full; full-size workloads on sampled (sequence, head) chains.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+from kda_testutil import TOL, announce, oracle_chains, rel_err, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_10_amd as m
+    m.library()
+    return m
+
+
+def run(kda, inp, scale=1.0, varlen=True, **kw):
+    return kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                         cu_seqlens=inp["cu_seqlens"] if varlen else None,
+                         cu_seqlens_host=inp["cu_seqlens_host"] if varlen else None,
+                         initial_state=inp["initial_state"],
+                         num_seqs=len(inp["lengths"]), scale=scale, **kw)
+
+
+def check_chains(inp, o, sf, chains, dtype, scale=1.0):
+    ref = oracle_chains(inp, chains, scale=scale)
+    cu = inp["cu_seqlens_host"]
+    worst_o = worst_s = 0.0
+    for (n, h), (o_ref, s_ref) in ref.items():
+        a, b = cu[n], cu[n + 1]
+        if b > a:
+            worst_o = max(worst_o, rel_err(to64(o[a:b, h]), o_ref))
+        worst_s = max(worst_s, rel_err(to64(sf[n, h]), s_ref))
+    print(f"  max rel err: o {worst_o:.3e}  S_final {worst_s:.3e}", flush=True)
+    assert worst_o <= TOL[dtype], worst_o
+    assert worst_s <= TOL[dtype], worst_s
+
+
+def test_fp32_forward_b1_t256_h2(kda):
+    """The fp32 workload in full: B=1, T=256, H=2, chunk 64, zero initial state."""
+    announce("chunk fp32 b1 t256 h2")
+    cfg = ki.CONFIGS["kda_fwd_b1_t256_h2_f32"]
+    inp = ki.make_prefill(cfg, device="cuda")
+    o, sf = run(kda, inp, varlen=False)
+    torch.cuda.synchronize()
+    check_chains(inp, o, sf, [(0, 0), (0, 1)], torch.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_ragged_with_initial_state(kda, dtype):
+    """Packed sequences ending inside chunks, an empty sequence, a one-token
+    sequence, nonzero initial states, a non-unit output scale."""
+    announce(f"chunk varlen ragged dtype={dtype}")
+    lens = (1, 63, 64, 65, 130, 0, 300, 17)
+    cfg = ki.PrefillConfig("t", lens, 3, dtype, init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=7)
+    o, sf = run(kda, inp, scale=0.7)
+    torch.cuda.synchronize()
+    chains = [(n, h) for n in range(len(lens)) for h in range(3)]
+    check_chains(inp, o, sf, chains, inp["dtype"], scale=0.7)
+
+
+def test_fixed_batch_matches_varlen(kda):
+    announce("chunk fixed batch vs varlen")
+    cfg = ki.PrefillConfig("t", (200, 200, 200), 4, "bf16", init_std=0.1)
+    inp = ki.make_prefill(cfg, device="cuda", seed=11)
+    o1, s1 = run(kda, inp, varlen=False)
+    o2, s2 = run(kda, inp, varlen=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    check_chains(inp, o1, s1, [(0, 0), (1, 3), (2, 1)], torch.bfloat16)
+
+
+def test_bounded_gate_slow_decay_and_long_memory(kda):
+    """Gates near zero (slow forgetting) keep the state alive across many chunks
+    and exercise the recurrence rather than the decay; gates at the -5 floor
+    exercise the reference-point scaling inside 16-token sub-tiles."""
+    announce("chunk slow and floor decay")
+    cfg = ki.PrefillConfig("t", (700, 333), 2, "bf16", init_std=0.2)
+    inp = ki.make_prefill(cfg, device="cuda", seed=13)
+    T = inp["g"].shape[0]
+    g = inp["g"]
+    g[: T // 2] *= 0.01                    # alpha ~ 0.99
+    g[T // 2:] = -5.0                      # alpha = exp(-5), the page's floor
+    o, sf = run(kda, inp)
+    torch.cuda.synchronize()
+    check_chains(inp, o, sf, [(0, 0), (0, 1), (1, 0), (1, 1)], torch.bfloat16)
+
+
+def test_deterministic(kda):
+    announce("chunk determinism")
+    cfg = ki.PrefillConfig("t", (1000, 37), 8, "bf16", init_std=0.1, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=3)
+    o1, s1 = run(kda, inp)
+    o2, s2 = run(kda, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_split_and_resume(kda):
+    """Prefill [0, t) then [t, T) from the carried state equals one pass."""
+    announce("chunk split/resume")
+    cfg = ki.PrefillConfig("t", (500,), 2, "bf16", init_std=0.1)
+    inp = ki.make_prefill(cfg, device="cuda", seed=5)
+    o, sf = run(kda, inp, varlen=False)
+    t = 200
+    part = lambda d, a, b: {**d, "q": d["q"][a:b].contiguous(), "k": d["k"][a:b].contiguous(),
+                            "v": d["v"][a:b].contiguous(), "g": d["g"][a:b].contiguous(),
+                            "beta": d["beta"][a:b].contiguous(), "lengths": [b - a]}
+    o1, s1 = run(kda, part(inp, 0, t), varlen=False)
+    p2 = part(inp, t, 500)
+    p2["initial_state"] = s1
+    o2, s2 = run(kda, p2, varlen=False)
+    torch.cuda.synchronize()
+    assert rel_err(to64(torch.cat([o1, o2])), to64(o)) <= TOL[torch.bfloat16]
+    assert rel_err(to64(s2), to64(sf)) <= TOL[torch.bfloat16]
+
+
+def test_decode_steps_equal_prefill(kda):
+    """T recurrent decode steps reproduce the prefill of the same T tokens."""
+    announce("decode == prefill")
+    H, T = 4, 90
+    cfg = ki.PrefillConfig("t", (T,), H, "bf16", init_std=0.1)
+    inp = ki.make_prefill(cfg, device="cuda", seed=21)
+    o, sf = run(kda, inp, varlen=False)
+    state = inp["initial_state"].clone()
+    outs = []
+    for t in range(T):
+        sl = lambda x: x[t:t + 1].contiguous()
+        outs.append(kda.recurrent_step(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["g"]),
+                                       sl(inp["beta"]), state))
+    torch.cuda.synchronize()
+    assert rel_err(to64(torch.cat(outs)), to64(o)) <= TOL[torch.bfloat16]
+    assert rel_err(to64(state), to64(sf)) <= TOL[torch.bfloat16]
+
+
+# ----------------------------------------------------------- full-size workloads
+def test_full_b4_t8192_h96_sampled(kda):
+    """B=4, T=8192, H=96, bf16, zero initial state -- the benchmark workload, in the
+    launch configuration the benchmark times; six chains replayed by the oracle."""
+    announce("chunk full b4 t8192 h96")
+    cfg = ki.CONFIGS["kda_prefill_b4_t8192_h96_bf16"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1002)
+    o, sf = run(kda, inp, varlen=False)
+    torch.cuda.synchronize()
+    check_chains(inp, o, sf, [(0, 0), (1, 17), (2, 50), (3, 95), (0, 63), (3, 1)],
+                 torch.bfloat16)
+
+
+def test_full_t65536_h96_initial_state_sampled(kda):
+    """One 65,536-token sequence, H=96, N(0, 0.02) initial state, gate clamped at -5."""
+    announce("chunk full t65536 h96 s0")
+    cfg = ki.CONFIGS["kda_prefill_t65536_h96_bf16_s0_gclamp5"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1003)
+    o, sf = run(kda, inp, varlen=False)
+    torch.cuda.synchronize()
+    check_chains(inp, o, sf, [(0, 0), (0, 47), (0, 95)], torch.bfloat16)
+
+
+def test_full_varlen32_t1m_h96_sampled(kda):
+    """32 packed sequences (log-uniform 1K..256K tokens, 1,048,576 total), H=96."""
+    announce("chunk full varlen32 t1m h96")
+    cfg = ki.CONFIGS["kda_prefill_varlen32_t1m_h96_bf16"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1004)
+    o, sf = run(kda, inp)
+    torch.cuda.synchronize()
+    lens = inp["lengths"]
+    longest = int(np.argmax(lens))
+    shortest = int(np.argmin(lens))
+    chains = [(longest, 3), (shortest, 95), (5, 40), (31, 0)]
+    check_chains(inp, o, sf, chains, torch.bfloat16)
+    del inp, o, sf
+    torch.cuda.empty_cache()
