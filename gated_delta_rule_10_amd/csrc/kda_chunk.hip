@@ -82,26 +82,23 @@ struct Layout {
   static constexpr int LD_D = kD + PADE;
   static constexpr int LD_C = kC + PADE;
   static constexpr int LD_O = DV + PADE;
-  static constexpr int LD_F = kC + 4;                    // fp32 solve buffers
-  static constexpr int LD_W = 17;                        // per-wave 16x16 fp32 scratch
   static constexpr int NVT = DV / 64;                    // 16-column value tiles per wave
   // Region R: three phases reuse the same bytes.
   //  Gram:       Kr[64][LD_KH], Qr[64][LD_KH], Kc[160][LD_KH]                 (OpT)
-  //  solve:      A[64][LD_F], X[64][LD_F], 4 waves x 4 x [16][LD_W]          (fp32)
   //  recurrence: Qt[64][LD_D], nBKt[64][LD_D], KbT[128][LD_C], BVT[DV][LD_C]  (OpT)
   //  output:     Ost[64][LD_O]                                               (OpT)
   static constexpr size_t kGram = (size_t)(64 + 64 + 160) * LD_KH * sizeof(OpT);
-  static constexpr size_t kSolve = (size_t)2 * 64 * LD_F * 4 + (size_t)4 * 4 * 16 * LD_W * 4;
   static constexpr size_t kRec =
       ((size_t)2 * 64 * LD_D + (size_t)128 * LD_C + (size_t)DV * LD_C) * sizeof(OpT);
   static constexpr size_t kOut = (size_t)64 * LD_O * sizeof(OpT);
   static constexpr size_t kRegion =
-      kGram > kSolve ? (kGram > kRec ? (kGram > kOut ? kGram : kOut) : (kRec > kOut ? kRec : kOut))
-                     : (kSolve > kRec ? (kSolve > kOut ? kSolve : kOut) : (kRec > kOut ? kRec : kOut));
-  static constexpr size_t kXinv = (size_t)64 * LD_C * sizeof(OpT);
-  static constexpr size_t kP = kXinv;
+      kGram > kRec ? (kGram > kOut ? kGram : kOut) : (kRec > kOut ? kRec : kOut);
+  // Lm: the unit-lower-triangular system, -A in the strictly lower 16x16 blocks
+  // and the inverse of each diagonal block on the diagonal; Pm: the P matrix.
+  static constexpr size_t kLm = (size_t)64 * LD_C * sizeof(OpT);
+  static constexpr size_t kP = kLm;
   static constexpr size_t kSmall = (size_t)(4 * 128 + 4 * 128 + 64 + 128) * 4;
-  static constexpr size_t kTotal = kRegion + kXinv + kP + kSmall;
+  static constexpr size_t kTotal = kRegion + kLm + kP + kSmall;
   static_assert(kTotal <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -116,41 +113,22 @@ template <> struct Raw<float> {
   __device__ __forceinline__ float lo() const { return f[0]; }
   __device__ __forceinline__ float hi() const { return f[1]; }
 };
-__device__ __forceinline__ void raw_load(Raw<bf16> &r, const bf16 *p) {
-  r.u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+__device__ __forceinline__ void raw_load(Raw<bf16> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  r.u = buf_load_b32(rs, off);
 }
-__device__ __forceinline__ void raw_load(Raw<float> &r, const float *p) {
-  r.f = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(p));
+__device__ __forceinline__ void raw_load(Raw<float> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  r.f = buf_load_f32x2(rs, off);
 }
 template <class OpT> __device__ __forceinline__ void raw_zero(Raw<OpT> &r);
 template <> __device__ __forceinline__ void raw_zero(Raw<bf16> &r) { r.u = 0u; }
 template <> __device__ __forceinline__ void raw_zero(Raw<float> &r) { r.f = f32x2{0.f, 0.f}; }
 
-// acc += X * Y for 16x16 fp32 blocks held in LDS (row-major), fp32 matrix cores.
-// X rows/cols at x[r * ldx + c], Y at y[r * ldy + c]; result layout as mma().
-__device__ __forceinline__ void mm16_f32(f32x4 &acc, const float *x, int ldx, const float *y,
-                                         int ldy, int lane) {
-  const int col = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float a = x[col * ldx + 4 * j + g];
-    const float b = y[(4 * j + g) * ldy + col];
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-  }
+// Off-diagonal (row-tile, column-tile) pairs of the 4x4 block lower triangle,
+// and the wave that computes each: wave w takes entries w and w + 4.
+__device__ __forceinline__ void off_tile(int o, int &i, int &j) {
+  i = o == 0 ? 1 : o < 3 ? 2 : 3;
+  j = o == 0 ? 0 : o < 3 ? o - 1 : o - 3;
 }
-__device__ __forceinline__ void st16(float *c, int ldc, const f32x4 &acc, int lane) {
-  const int col = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[(4 * g + i) * ldc + col] = acc[i];
-}
-__device__ __forceinline__ f32x4 ld16(const float *c, int ldc, int lane) {
-  const int col = lane & 15, g = lane >> 4;
-  f32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = c[(4 * g + i) * ldc + col];
-  return r;
-}
-__device__ __forceinline__ void wave_lds_fence() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <class OpT, int DV>
 __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
@@ -159,9 +137,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::kTotal];
 
   unsigned char *region = smem;
-  OpT *Xinv = reinterpret_cast<OpT *>(smem + L::kRegion);
-  OpT *Pm = reinterpret_cast<OpT *>(smem + L::kRegion + L::kXinv);
-  float *gtot = reinterpret_cast<float *>(smem + L::kRegion + L::kXinv + L::kP);
+  OpT *Lm = reinterpret_cast<OpT *>(smem + L::kRegion);
+  OpT *Pm = reinterpret_cast<OpT *>(smem + L::kRegion + L::kLm);
+  float *gtot = reinterpret_cast<float *>(smem + L::kRegion + L::kLm + L::kP);
   float *gmid = gtot + 4 * 128;
   float *sbeta = gmid + 4 * 128;
   float *sgam = sbeta + 64;
@@ -170,10 +148,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   OpT *Kr = reinterpret_cast<OpT *>(region);
   OpT *Qr = Kr + 64 * L::LD_KH;
   OpT *Kc = Qr + 64 * L::LD_KH;
-  // solve phase views
-  float *A32 = reinterpret_cast<float *>(region);
-  float *X32 = A32 + 64 * L::LD_F;
-  float *Wscr = X32 + 64 * L::LD_F;
   // recurrence phase views
   OpT *Qt = reinterpret_cast<OpT *>(region);
   OpT *nBKt = Qt + 64 * L::LD_D;
@@ -183,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   OpT *Ost = reinterpret_cast<OpT *>(region);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
@@ -204,21 +178,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   }
   const int nchunks = (int)((len + kC - 1) / kC);
   const int H = p.H;
-  const int vblk = vs * DV;               // first value column of this workgroup
-  const int vw = vblk + w * (DV / 4);     // first value column of this wave
+  const int64_t rowstride = (int64_t)H * kD;  // elements between consecutive tokens
+  const int vblk = vs * DV;                   // first value column of this workgroup
+  const int vw = vblk + w * (DV / 4);         // first value column of this wave
 
-  const OpT *__restrict__ qg = reinterpret_cast<const OpT *>(p.q);
-  const OpT *__restrict__ kg = reinterpret_cast<const OpT *>(p.k);
-  const OpT *__restrict__ vg = reinterpret_cast<const OpT *>(p.v);
-  OpT *__restrict__ og = reinterpret_cast<OpT *>(p.o);
+  const OpT *__restrict__ qg = reinterpret_cast<const OpT *>(p.q) + (int64_t)h * kD;
+  const OpT *__restrict__ kg = reinterpret_cast<const OpT *>(p.k) + (int64_t)h * kD;
+  const OpT *__restrict__ vg = reinterpret_cast<const OpT *>(p.v) + (int64_t)h * kD + vblk;
+  const float *__restrict__ gg = p.g + (int64_t)h * kD;
+  OpT *__restrict__ og = reinterpret_cast<OpT *>(p.o) + (int64_t)h * kD + vblk;
 
-  // One-time zero of the strictly-upper blocks of X and P that the 32-wide
-  // k-steps read: blocks (0,1) and (2,3).
+  // One-time zero of the strictly-upper blocks (0,1) and (2,3) of P, which the
+  // 32-wide k-steps of the P U product read.
   for (int e = tid; e < 2 * 256; e += kThreads) {
     const int b = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-    const int r = 16 * (2 * b) + rr, c = 16 * (2 * b + 1) + cc;
-    Xinv[r * L::LD_C + c] = from_f32<OpT>(0.f);
-    Pm[r * L::LD_C + c] = from_f32<OpT>(0.f);
+    Pm[(32 * b + rr) * L::LD_C + 32 * b + 16 + cc] = from_f32<OpT>(0.f);
   }
 
   // ---- state (fp32 accumulators): S[ct][vt] holds S[16ct+4g4+i][vw+16vt+l16]
@@ -235,32 +209,39 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   }
 
   // ---- register prefetch of a chunk's raw inputs: wave w = tokens 16w..16w+15,
-  //      lane = channels 2*lane, 2*lane+1 (value channels vblk + 2*lane for DV=128;
-  //      lanes < 32 cover the 64 columns when DV=64).
+  //      lane = channels 2*lane, 2*lane+1 (value channels vblk + 2*lane; lanes < 32
+  //      cover the 64 columns when DV = 64).
   Raw<OpT> rq[16], rk[16], rv[16];
   f32x2 rg[16];
   float rb = 0.f;
   const int c0 = 2 * lane;
   const bool has_v = (DV == 128) || (lane < 32);
+  const uint32_t lane_off_qk = (uint32_t)c0 * (uint32_t)sizeof(OpT);  // byte offsets
+  const uint32_t lane_off_g = (uint32_t)c0 * 4u;
+  const uint32_t row_qk = (uint32_t)rowstride * (uint32_t)sizeof(OpT);  // bytes per token
+  const uint32_t row_g = (uint32_t)rowstride * 4u;
   auto prefetch = [&](int j) {
-    const int64_t t0 = bos + (int64_t)j * kC + 16 * w;
-    const int64_t lim = bos + len;
+    const int64_t t0 = bos + (int64_t)j * kC + 16 * w;  // uniform
+    const int64_t rem = bos + len - t0;
+    const uint32_t nv = rem <= 0 ? 0u : (rem >= 16 ? 16u : (uint32_t)rem);  // valid rows
+    // descriptors cover exactly this wave's valid rows of its head
+    const __amdgpu_buffer_rsrc_t rq_s = make_rsrc(qg + t0 * rowstride, nv * row_qk);
+    const __amdgpu_buffer_rsrc_t rk_s = make_rsrc(kg + t0 * rowstride, nv * row_qk);
+    const __amdgpu_buffer_rsrc_t rv_s = make_rsrc(vg + t0 * rowstride, has_v ? nv * row_qk : 0u);
+    const __amdgpu_buffer_rsrc_t rg_s = make_rsrc(gg + t0 * rowstride, nv * row_g);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int64_t tok = t0 + t;
-      if (tok < lim) {
-        const int64_t base = (tok * H + h) * kD;
-        raw_load(rq[t], qg + base + c0);
-        raw_load(rk[t], kg + base + c0);
-        if (has_v) raw_load(rv[t], vg + base + vblk + c0); else raw_zero(rv[t]);
-        rg[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(p.g + base + c0));
+      if ((uint32_t)t < nv) {
+        raw_load(rq[t], rq_s, lane_off_qk + t * row_qk);
+        raw_load(rk[t], rk_s, lane_off_qk + t * row_qk);
+        raw_load(rv[t], rv_s, lane_off_qk + t * row_qk);  // zero where has_v is false
+        rg[t] = buf_load_f32x2(rg_s, lane_off_g + t * row_g);
       } else {
         raw_zero(rq[t]); raw_zero(rk[t]); raw_zero(rv[t]);
         rg[t] = f32x2{0.f, 0.f};
       }
     }
-    const int64_t tb = t0 + (lane & 15);
-    rb = (lane < 16 && tb < lim) ? p.beta[tb * H + h] : 0.f;
+    rb = (lane < 16 && (uint32_t)l16 < nv) ? p.beta[(t0 + l16) * H + h] : 0.f;
   };
   if (nchunks > 0) prefetch(0);
 
@@ -278,10 +259,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
         G0[t] = a0;
         G1[t] = a1;
       }
-      gtot[w * 128 + c0] = a0;
-      gtot[w * 128 + c0 + 1] = a1;
-      gmid[w * 128 + c0] = G0[kRef];
-      gmid[w * 128 + c0 + 1] = G1[kRef];
+      *reinterpret_cast<f32x2 *>(gtot + w * 128 + c0) = f32x2{a0, a1};
+      *reinterpret_cast<f32x2 *>(gmid + w * 128 + c0) = f32x2{G0[kRef], G1[kRef]};
       if (lane < 16) sbeta[16 * w + lane] = rb;
     }
     block_sync();
@@ -290,10 +269,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
     float gref0[4], gref1[4], glast0 = 0.f, glast1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      gref0[i] = glast0 + gmid[i * 128 + c0];
-      gref1[i] = glast1 + gmid[i * 128 + c0 + 1];
-      glast0 += gtot[i * 128 + c0];
-      glast1 += gtot[i * 128 + c0 + 1];
+      const f32x2 gm = *reinterpret_cast<const f32x2 *>(gmid + i * 128 + c0);
+      const f32x2 gt = *reinterpret_cast<const f32x2 *>(gtot + i * 128 + c0);
+      gref0[i] = glast0 + gm[0];
+      gref1[i] = glast1 + gm[1];
+      glast0 += gt[0];
+      glast1 += gt[1];
     }
     // E1 = e^{G_t - G_ref} (row factor), E2 = e^{G_ref - G_t} (column factor)
     float E1a[16], E1b[16], E2a[16], E2b[16];
@@ -306,15 +287,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
       E2b[t] = fast_exp2(-d1);
     }
 
-    // ===== P1 + Gram: A = beta (Kr Kc^T), P = Qr Kc^T over the 10 lower tile pairs.
-    // Tile t of the list (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),(3,1),(3,2),(3,3)
-    // belongs to wave t % 4.
-    f32x4 accA[3], accP[3];
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      accA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accP[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    // ===== P1 + Gram.  Wave w computes the diagonal tile (w, w) -- A in both
+    // orientations for the in-register Neumann inverse, and P -- plus the
+    // off-diagonal tiles w and w + 4 of the list (1,0),(2,0),(2,1),(3,0),(3,1),(3,2).
+    f32x4 accN = {0.f, 0.f, 0.f, 0.f}, accNT = accN, accPd = accN;
+    f32x4 accA[2] = {accN, accN}, accP[2] = {accN, accN};
 #pragma unroll
     for (int hc = 0; hc < L::NH; ++hc) {
       if (c0 / L::KH == hc) {
@@ -334,24 +311,35 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
           store2<OpT>(Qr + r * L::LD_KH + cc, q0 * E1a[t], q1 * E1b[t]);
           const float b0 = k0 * E2a[t], b1 = k1 * E2b[t];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (i >= w) {
-              OpT *dst = Kc + (tri_index(i, w) * 16 + t) * L::LD_KH + cc;
-              store2<OpT>(dst, b0 * F0[i], b1 * F1[i]);
-            }
-          }
+          for (int i = 0; i < 4; ++i)
+            if (i >= w)
+              store2<OpT>(Kc + (tri_index(i, w) * 16 + t) * L::LD_KH + cc, b0 * F0[i], b1 * F1[i]);
         }
       }
       block_sync();
+      const OpT *krw = Kr + 16 * w * L::LD_KH;
+      const OpT *qrw = Qr + 16 * w * L::LD_KH;
+      const OpT *kcw = Kc + tri_index(w, w) * 16 * L::LD_KH;
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int tile = w + 4 * u;
-        if (tile < 10) {
-          const int ti = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+      for (int kk = 0; kk < L::KH / 32; ++kk) {
+        Frag<OpT> fk, fc, fq;
+        lds_frag_ck(fk, krw, L::LD_KH, l16, 32 * kk, g4);
+        lds_frag_ck(fc, kcw, L::LD_KH, l16, 32 * kk, g4);
+        lds_frag_ck(fq, qrw, L::LD_KH, l16, 32 * kk, g4);
+        mma(accN, fk, fc);   // [r][s]
+        mma(accNT, fc, fk);  // [s][r]
+        mma(accPd, fc, fq);  // [s][r] of P
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int o = w + 4 * u;
+        if (o < 6) {
+          int ti, tj;
+          off_tile(o, ti, tj);
 #pragma unroll
           for (int kk = 0; kk < L::KH / 32; ++kk) {
             Frag<OpT> xs, yk, yq;
-            lds_frag_ck(xs, Kc + tile * 16 * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
+            lds_frag_ck(xs, Kc + tri_index(ti, tj) * 16 * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
             lds_frag_ck(yk, Kr + 16 * ti * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
             lds_frag_ck(yq, Qr + 16 * ti * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
             mma(accA[u], xs, yk);
@@ -359,101 +347,65 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
           }
         }
       }
-      block_sync();
+      if (L::NH > 1) block_sync();  // the next channel pass rewrites the Gram region
     }
-    // results: lane holds A[r = 16 ti + l16][s = 16 tj + 4 g4 + i]
+
+    // off-diagonal results: lane holds A[r = 16 ti + l16][s = 16 tj + 4 g4 + i]
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int tile = w + 4 * u;
-      if (tile < 10) {
-        const int ti = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-        const int tj = tile - tri_index(ti, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int o = w + 4 * u;
+      if (o < 6) {
+        int ti, tj;
+        off_tile(o, ti, tj);
         const int r = 16 * ti + l16;
         const float br = sbeta[r];
-        f32x4 av, pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * tj + 4 * g4 + i;
-          av[i] = s < r ? br * accA[u][i] : 0.f;
-          pv[i] = s <= r ? accP[u][i] : 0.f;
-        }
-        *reinterpret_cast<f32x4 *>(A32 + r * L::LD_F + 16 * tj + 4 * g4) = av;
-        OpT *pp = Pm + r * L::LD_C + 16 * tj + 4 * g4;
-        store2<OpT>(pp, pv[0], pv[1]);
-        store2<OpT>(pp + 2, pv[2], pv[3]);
+        store4<OpT>(Lm + r * L::LD_C + 16 * tj + 4 * g4, accA[u] * (-br));
+        store4<OpT>(Pm + r * L::LD_C + 16 * tj + 4 * g4, accP[u]);
       }
     }
-    block_sync();
-
-    // ===== solve: X = (I + A)^{-1}, fp32 matrix cores.
+    // diagonal tile w: P (s <= r) and the inverse of I + A_ww
     {
-      float *scr = Wscr + w * 4 * 16 * L::LD_W;  // four 16x16 scratch blocks of this wave
-      float *s0b = scr, *s1b = scr + 16 * L::LD_W, *s2b = scr + 32 * L::LD_W,
-            *s3b = scr + 48 * L::LD_W;
-      // diagonal block w: Neumann series (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8)
-      const float *Nb = A32 + 16 * w * L::LD_F + 16 * w;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm16_f32(acc, Nb, L::LD_F, Nb, L::LD_F, lane);  // N^2
-      st16(s0b, L::LD_W, acc, lane);
-      wave_lds_fence();
-      f32x4 n3 = {0.f, 0.f, 0.f, 0.f};
-      mm16_f32(n3, Nb, L::LD_F, s0b, L::LD_W, lane);  // N^3
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16_f32(acc, s0b, L::LD_W, s0b, L::LD_W, lane);  // N^4
-      st16(s1b, L::LD_W, acc, lane);
-      {
-        const f32x4 nn = ld16(Nb, L::LD_F, lane), n2 = ld16(s0b, L::LD_W, lane);
-        f32x4 p1;
+      const int r = 16 * w + l16;
+      f32x4 pv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p1[i] = ((4 * g4 + i) == l16 ? 1.f : 0.f) - nn[i] + n2[i] - n3[i];
-        st16(s2b, L::LD_W, p1, lane);  // P1 = (I - N)(I + N^2)
-      }
-      wave_lds_fence();
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16_f32(acc, s1b, L::LD_W, s1b, L::LD_W, lane);  // N^8
-      st16(s3b, L::LD_W, acc, lane);
-      f32x4 p2 = ld16(s2b, L::LD_W, lane);
-      mm16_f32(p2, s2b, L::LD_W, s1b, L::LD_W, lane);  // P2 = P1 + P1 N^4
-      st16(s0b, L::LD_W, p2, lane);
-      wave_lds_fence();
-      f32x4 xd = p2;
-      mm16_f32(xd, s0b, L::LD_W, s3b, L::LD_W, lane);  // X = P2 + P2 N^8
-      st16(X32 + 16 * w * L::LD_F + 16 * w, L::LD_F, xd, lane);
-      block_sync();
-      // off-diagonal blocks, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, by distance
+      for (int i = 0; i < 4; ++i) pv[i] = (4 * g4 + i) <= l16 ? accPd[i] : 0.f;
+      store4<OpT>(Pm + r * L::LD_C + 16 * w + 4 * g4, pv);
+      // R-layout tiles (lane holds M[4g4+i][l16]):  N = strictly lower A_ww,  NT = N^T
+      f32x4 N, NT;
+      const float bl = sbeta[16 * w + l16];
 #pragma unroll
-      for (int dist = 1; dist <= 3; ++dist) {
-        if (w < 4 - dist) {
-          const int jj = w, ii = w + dist;
-          f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
-          for (int kk = jj; kk < ii; ++kk)
-            mm16_f32(tacc, A32 + 16 * ii * L::LD_F + 16 * kk, L::LD_F,
-                     X32 + 16 * kk * L::LD_F + 16 * jj, L::LD_F, lane);
-          st16(s0b, L::LD_W, tacc, lane);
-          wave_lds_fence();
-          f32x4 xo = {0.f, 0.f, 0.f, 0.f};
-          mm16_f32(xo, X32 + 16 * ii * L::LD_F + 16 * ii, L::LD_F, s0b, L::LD_W, lane);
-          st16(X32 + 16 * ii * L::LD_F + 16 * jj, L::LD_F, -xo, lane);
-        }
-        block_sync();
+      for (int i = 0; i < 4; ++i) {
+        const int a = 4 * g4 + i;
+        N[i] = l16 < a ? sbeta[16 * w + a] * accN[i] : 0.f;
+        NT[i] = a < l16 ? bl * accNT[i] : 0.f;
       }
-      // X (lower blocks) -> Xinv in the operand type
-      for (int e = tid; e < 10 * 256; e += kThreads) {
-        const int tile = e >> 8;
-        const int ti = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-        const int tj = tile - tri_index(ti, 0);
-        const int r = 16 * ti + ((e >> 4) & 15), c = 16 * tj + (e & 15);
-        Xinv[r * L::LD_C + c] = from_f32<OpT>(X32[r * L::LD_F + c]);
+      // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0.
+      // rr_tn(B, C) = B^T C, so products pair each power with its transpose.
+      const f32x4 N2 = rr_tn(NT, N), T2 = rr_tn(N, NT);
+      const f32x4 N3 = rr_tn(NT, N2), T3 = rr_tn(N, T2);
+      const f32x4 N4 = rr_tn(T2, N2), T4 = rr_tn(N2, T2);
+      const f32x4 N8 = rr_tn(T4, N4);
+      f32x4 P1, P1T;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float id = (4 * g4 + i) == l16 ? 1.f : 0.f;
+        P1[i] = id - N[i] + N2[i] - N3[i];
+        P1T[i] = id - NT[i] + T2[i] - T3[i];
       }
-      block_sync();
+      const f32x4 P2 = P1 + rr_tn(P1T, N4);
+      const f32x4 P2T = P1T + rr_tn(N4, P1T);
+      const f32x4 Xd = P2 + rr_tn(P2T, N8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Lm[(16 * w + 4 * g4 + i) * L::LD_C + 16 * w + l16] = from_f32<OpT>(Xd[i]);
     }
+    block_sync();  // Gram region free; Lm / Pm written
 
     // ===== P2: operands of the state products (region now holds the recurrence views)
     {
       const float eB0 = fast_exp2(gref0[w]), eB1 = fast_exp2(gref1[w]);               // e^{G_ref}
       const float eK0 = fast_exp2(glast0 - gref0[w]), eK1 = fast_exp2(glast1 - gref1[w]);  // e^{G_C-G_ref}
-      OpT kb0[16], kb1[16], bv0[16], bv1[16];
+      float kb0[16], kb1[16], bv0[16], bv1[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int r = 16 * w + t;
@@ -461,47 +413,45 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
         const float e0 = E1a[t] * eB0, e1 = E1b[t] * eB1;
         store2<OpT>(Qt + r * L::LD_D + c0, rq[t].lo() * e0, rq[t].hi() * e1);
         store2<OpT>(nBKt + r * L::LD_D + c0, -br * rk[t].lo() * e0, -br * rk[t].hi() * e1);
-        kb0[t] = from_f32<OpT>(rk[t].lo() * E2a[t] * eK0);
-        kb1[t] = from_f32<OpT>(rk[t].hi() * E2b[t] * eK1);
-        bv0[t] = from_f32<OpT>(br * rv[t].lo());
-        bv1[t] = from_f32<OpT>(br * rv[t].hi());
+        kb0[t] = rk[t].lo() * E2a[t] * eK0;
+        kb1[t] = rk[t].hi() * E2b[t] * eK1;
+        bv0[t] = br * rv[t].lo();
+        bv1[t] = br * rv[t].hi();
       }
-      // transposed rows: 16 consecutive tokens of one channel
+      // transposed rows: 16 consecutive tokens of one channel, 16-byte stores
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        KbT[c0 * L::LD_C + 16 * w + t] = kb0[t];
-        KbT[(c0 + 1) * L::LD_C + 16 * w + t] = kb1[t];
-      }
-      if (has_v) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          BVT[c0 * L::LD_C + 16 * w + t] = bv0[t];
-          BVT[(c0 + 1) * L::LD_C + 16 * w + t] = bv1[t];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        store4<OpT>(KbT + c0 * L::LD_C + 16 * w + 4 * q4,
+                    f32x4{kb0[4 * q4], kb0[4 * q4 + 1], kb0[4 * q4 + 2], kb0[4 * q4 + 3]});
+        store4<OpT>(KbT + (c0 + 1) * L::LD_C + 16 * w + 4 * q4,
+                    f32x4{kb1[4 * q4], kb1[4 * q4 + 1], kb1[4 * q4 + 2], kb1[4 * q4 + 3]});
+        if (has_v) {
+          store4<OpT>(BVT + c0 * L::LD_C + 16 * w + 4 * q4,
+                      f32x4{bv0[4 * q4], bv0[4 * q4 + 1], bv0[4 * q4 + 2], bv0[4 * q4 + 3]});
+          store4<OpT>(BVT + (c0 + 1) * L::LD_C + 16 * w + 4 * q4,
+                      f32x4{bv1[4 * q4], bv1[4 * q4 + 1], bv1[4 * q4 + 2], bv1[4 * q4 + 3]});
         }
       }
-      if (w == 0) {
-        sgam[c0] = fast_exp2(glast0);
-        sgam[c0 + 1] = fast_exp2(glast1);
-      }
+      if (w == 0) *reinterpret_cast<f32x2 *>(sgam + c0) = f32x2{fast_exp2(glast0), fast_exp2(glast1)};
     }
     // raw registers are free: start loading the next chunk
     if (j + 1 < nchunks) prefetch(j + 1);
     block_sync();
 
     // ===== recurrence on this wave's value columns
-    f32x4 accY[4][L::NVT], accO[4][L::NVT];
+    // Y = beta V - beta K~ S        (lane holds Y[s = 16 st + 4 g4 + i][v])
+    f32x4 accY[4][L::NVT];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int vt = 0; vt < L::NVT; ++vt) {
+      const int vc = vw - vblk + 16 * vt + l16;
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt) {
-        // Y starts at beta V: lane holds (s = 16 st + 4 g4 + i, v = local col)
-        const int vc = vw - vblk + 16 * vt + l16;
-        const OpT *src = BVT + vc * L::LD_C + 16 * st + 4 * g4;
+      for (int st = 0; st < 4; ++st) {
+        Frag4<OpT> b4;
+        lds_frag4(b4, BVT, L::LD_C, vc, 16 * st, g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) accY[st][vt][i] = to_f32(src[i]);
-        accO[st][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) accY[st][vt][i] = to_f32(b4.v[i]);
       }
-    // Y -= beta K~ S ; O = Q~ S   (S from registers as the Y operand)
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       Frag<OpT> sf[L::NVT];
@@ -509,45 +459,63 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
       for (int vt = 0; vt < L::NVT; ++vt) acc_frag_sk(sf[vt], S[2 * kk][vt], S[2 * kk + 1][vt]);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        Frag<OpT> xb, xq;
+        Frag<OpT> xb;
         lds_frag_sk(xb, nBKt, L::LD_D, 16 * st + l16, 32 * kk, g4);
-        lds_frag_sk(xq, Qt, L::LD_D, 16 * st + l16, 32 * kk, g4);
 #pragma unroll
-        for (int vt = 0; vt < L::NVT; ++vt) {
-          mma(accY[st][vt], xb, sf[vt]);
-          mma(accO[st][vt], xq, sf[vt]);
-        }
+        for (int vt = 0; vt < L::NVT; ++vt) mma(accY[st][vt], xb, sf[vt]);
       }
     }
-    // U = X Y
-    Frag<OpT> yf[2][L::NVT];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt)
-        acc_frag_sk(yf[kk][vt], accY[2 * kk][vt], accY[2 * kk + 1][vt]);
+    // U = (I + A)^{-1} Y by block forward substitution:
+    //   U_i = X_ii (Y_i - sum_{k<i} A_ik U_k)
     f32x4 accU[4][L::NVT];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt) {
-        accU[st][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < i; ++k) {
+        Frag4<OpT> la;
+        lds_frag4(la, Lm, L::LD_C, 16 * i + l16, 16 * k, g4);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          if (kk <= st / 2) {
-            Frag<OpT> xi;
-            lds_frag_sk(xi, Xinv, L::LD_C, 16 * st + l16, 32 * kk, g4);
-            mma(accU[st][vt], xi, yf[kk][vt]);
-          }
+        for (int vt = 0; vt < L::NVT; ++vt) {
+          Frag4<OpT> uk;
+          acc_frag4(uk, accU[k][vt]);
+          mma16(accY[i][vt], la, uk);
         }
       }
+      Frag4<OpT> xd;
+      lds_frag4(xd, Lm, L::LD_C, 16 * i + l16, 16 * i, g4);
+#pragma unroll
+      for (int vt = 0; vt < L::NVT; ++vt) {
+        Frag4<OpT> yi;
+        acc_frag4(yi, accY[i][vt]);
+        accU[i][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mma16(accU[i][vt], xd, yi);
+      }
+    }
     Frag<OpT> uf[2][L::NVT];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int vt = 0; vt < L::NVT; ++vt)
         acc_frag_sk(uf[kk][vt], accU[2 * kk][vt], accU[2 * kk + 1][vt]);
-    // O += P U
+    // O^T = S^T Q~^T + U^T P^T      (lane holds O[r = 16 rt + l16][v = .. + 4 g4 + i])
+    f32x4 accOT[L::NVT][4];
+#pragma unroll
+    for (int vt = 0; vt < L::NVT; ++vt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) accOT[vt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      Frag<OpT> sf[L::NVT];
+#pragma unroll
+      for (int vt = 0; vt < L::NVT; ++vt) acc_frag_sk(sf[vt], S[2 * kk][vt], S[2 * kk + 1][vt]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Frag<OpT> xq;
+        lds_frag_sk(xq, Qt, L::LD_D, 16 * rt + l16, 32 * kk, g4);
+#pragma unroll
+        for (int vt = 0; vt < L::NVT; ++vt) mma(accOT[vt][rt], sf[vt], xq);
+      }
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -556,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
           Frag<OpT> xp;
           lds_frag_sk(xp, Pm, L::LD_C, 16 * rt + l16, 32 * kk, g4);
 #pragma unroll
-          for (int vt = 0; vt < L::NVT; ++vt) mma(accO[rt][vt], xp, uf[kk][vt]);
+          for (int vt = 0; vt < L::NVT; ++vt) mma(accOT[vt][rt], uf[kk][vt], xp);
         }
       }
     // S <- Gamma S + Kbar^T U
@@ -577,24 +545,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
 
     // ===== output: stage O (scaled, io dtype) in LDS, then row-contiguous stores
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int vt = 0; vt < L::NVT; ++vt)
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ost[(16 * rt + 4 * g4 + i) * L::LD_O + (vw - vblk) + 16 * vt + l16] =
-              from_f32<OpT>(p.scale * accO[rt][vt][i]);
+      for (int rt = 0; rt < 4; ++rt)
+        store4<OpT>(Ost + (16 * rt + l16) * L::LD_O + (vw - vblk) + 16 * vt + 4 * g4,
+                    accOT[vt][rt] * p.scale);
     block_sync();
     {
       constexpr int kVec = 16 / (int)sizeof(OpT);       // elements per 16-byte store
       constexpr int kPerRow = DV / kVec;                // stores per output row
       constexpr int kRowsPerPass = kThreads / kPerRow;
       const int col = (tid % kPerRow) * kVec;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(og + (bos + (int64_t)j * kC) * rowstride, (uint32_t)Lc * row_qk);
       for (int r = tid / kPerRow; r < Lc; r += kRowsPerPass) {
-        const int64_t tok = bos + (int64_t)j * kC + r;
         const f32x4 val = *reinterpret_cast<const f32x4 *>(Ost + r * L::LD_O + col);
-        __builtin_nontemporal_store(
-            val, reinterpret_cast<f32x4 *>(og + (tok * H + h) * kD + vblk + col));
+        buf_store_b128(ors, (uint32_t)r * row_qk + (uint32_t)col * (uint32_t)sizeof(OpT), val);
       }
     }
     // (the next chunk's first barrier orders these LDS reads before its writes)

@@ -95,7 +95,72 @@ __device__ __forceinline__ void acc_frag_sk(Frag<float> &f, const f32x4 &lo, con
   for (int i = 0; i < 4; ++i) { f.v[i] = lo[i]; f.v[4 + i] = hi[i]; }
 }
 
+// ------------------------------------------- 16-wide k steps (k = 4g + {0..3})
+// Four k-values per lane, the natural layout of V_MFMA_F32_16X16X16_BF16 and of
+// a result tile's rows: a result tile acc[4g+i][y] is directly the Y fragment
+// of rows y with k = 4g + i.
+template <class OpT> struct Frag4;
+template <> struct Frag4<bf16> { bf16x4 v; };
+template <> struct Frag4<float> { f32x4 v; };
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mma16(f32x4 &acc, const Frag4<bf16> &x, const Frag4<bf16> &y) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, x.v),
+                                                  __builtin_bit_cast(shortx4, y.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4 &acc, const Frag4<float> &x, const Frag4<float> &y) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v[t], y.v[t], acc, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_frag4(Frag4<bf16> &f, const bf16 *base, int ld, int row, int k0,
+                                          int g) {
+  f.v = *reinterpret_cast<const bf16x4 *>(base + row * ld + k0 + 4 * g);
+}
+__device__ __forceinline__ void lds_frag4(Frag4<float> &f, const float *base, int ld, int row,
+                                          int k0, int g) {
+  f.v = *reinterpret_cast<const f32x4 *>(base + row * ld + k0 + 4 * g);
+}
+__device__ __forceinline__ void acc_frag4(Frag4<bf16> &f, const f32x4 &a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.v[i] = (bf16)a[i];
+}
+__device__ __forceinline__ void acc_frag4(Frag4<float> &f, const f32x4 &a) { f.v = a; }
+
+// Register-only product of two 16x16 fp32 tiles held in the result layout
+// (lane holds M[4g+i][l%16]): returns (B^T C) in the same layout, on fp32
+// matrix cores.  Instruction i pairs row 4g+i of B and C across lane groups g.
+__device__ __forceinline__ f32x4 rr_tn(const f32x4 &b, const f32x4 &c) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b[i], c[i], acc, 0, 0, 0);
+  return acc;
+}
+
 // ------------------------------------------------------- small vector I/O
+// Buffer resource over `bytes` bytes starting at a wave-uniform address: memory
+// instructions then take a scalar base plus a 32-bit per-lane offset, and any
+// access at or past `bytes` reads zero / is dropped by the hardware range check.
+// The base is made explicitly uniform so the descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t u = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  void *b = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+constexpr int kNonTemporal = 2;  // streaming access: do not keep in the caches
+__device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ f32x2 buf_load_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+}
+__device__ __forceinline__ void buf_store_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4 &v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kNonTemporal);
+}
+
 // Two consecutive elements of a row, widened to fp32.
 __device__ __forceinline__ f32x2 load2(const bf16 *p) {
   const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
@@ -106,6 +171,17 @@ __device__ __forceinline__ f32x2 load2(const bf16 *p) {
 }
 __device__ __forceinline__ f32x2 load2(const float *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(p));
+}
+
+template <class T> __device__ __forceinline__ void store4(T *p, const f32x4 &v);
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, const f32x4 &v) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x4 *>(p) = r;
+}
+template <> __device__ __forceinline__ void store4<float>(float *p, const f32x4 &v) {
+  *reinterpret_cast<f32x4 *>(p) = v;
 }
 
 template <class T> __device__ __forceinline__ void store2(T *p, float a, float b);
