@@ -53,7 +53,8 @@ namespace {
 
 constexpr int kC = KDA_CHUNK;     // 64 tokens per chunk
 constexpr int kD = KDA_HEAD_DIM;  // 128 channels
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRef = 8;           // reference token inside each 16-token sub-tile
 
 struct ChunkParams {
@@ -73,6 +74,14 @@ struct ChunkParams {
 // Tile list of the 10 lower (row-tile i, column-tile j) pairs and their owner wave.
 __device__ __forceinline__ int tri_index(int i, int j) { return i * (i + 1) / 2 + j; }
 
+// Column order of the matrices read as split-k fragments (k = 4g+i and
+// 16+4g+i of each 32-column block): stored so that those eight k-values are
+// adjacent, each fragment is one 16-byte LDS read.  Groups of four aligned
+// columns stay contiguous.
+__device__ __forceinline__ int skpos(int c) {
+  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+
 template <class OpT, int DV>
 struct Layout {
   static constexpr int NH = sizeof(OpT) == 4 ? 2 : 1;   // channel passes of the Gram products
@@ -82,7 +91,8 @@ struct Layout {
   static constexpr int LD_D = kD + PADE;
   static constexpr int LD_C = kC + PADE;
   static constexpr int LD_O = DV + PADE;
-  static constexpr int NVT = DV / 64;                    // 16-column value tiles per wave
+  static constexpr int NRW = DV / 16;                    // waves running the recurrence
+  static_assert(NRW <= kWaves, "value block too wide");
   // Region R: three phases reuse the same bytes.
   //  Gram:       Kr[64][LD_KH], Qr[64][LD_KH], Kc[160][LD_KH]                 (OpT)
   //  recurrence: Qt[64][LD_D], nBKt[64][LD_D], KbT[128][LD_C], BVT[DV][LD_C]  (OpT)
@@ -91,14 +101,20 @@ struct Layout {
   static constexpr size_t kRec =
       ((size_t)2 * 64 * LD_D + (size_t)128 * LD_C + (size_t)DV * LD_C) * sizeof(OpT);
   static constexpr size_t kOut = (size_t)64 * LD_O * sizeof(OpT);
-  static constexpr size_t kRegion =
-      kGram > kRec ? (kGram > kOut ? kGram : kOut) : (kRec > kOut ? kRec : kOut);
+  static constexpr size_t kGramOut = kGram > kOut ? kGram : kOut;
+  static constexpr size_t kRegion = kGramOut > kRec ? kGramOut : kRec;
+  // half-sub-tile totals and first values of the log-decay ([2][8][128] fp32):
+  // inside the region when the recurrence view leaves room past the Gram view
+  static constexpr size_t kHalf = (size_t)2 * kWaves * 128 * 4;
+  static constexpr bool kHalfInRegion = kRegion - kGramOut >= kHalf;
+  static constexpr size_t kHalfOff = kHalfInRegion ? kGramOut : kRegion;
+  static constexpr size_t kAfterRegion = kHalfInRegion ? kRegion : kRegion + kHalf;
   // Lm: the unit-lower-triangular system, -A in the strictly lower 16x16 blocks
   // and the inverse of each diagonal block on the diagonal; Pm: the P matrix.
   static constexpr size_t kLm = (size_t)64 * LD_C * sizeof(OpT);
   static constexpr size_t kP = kLm;
-  static constexpr size_t kSmall = (size_t)(4 * 128 + 4 * 128 + 64 + 128) * 4;
-  static constexpr size_t kTotal = kRegion + kLm + kP + kSmall;
+  static constexpr size_t kSmall = (size_t)(64 + 128) * 4;
+  static constexpr size_t kTotal = kAfterRegion + kLm + kP + kSmall;
   static_assert(kTotal <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -113,46 +129,59 @@ template <> struct Raw<float> {
   __device__ __forceinline__ float lo() const { return f[0]; }
   __device__ __forceinline__ float hi() const { return f[1]; }
 };
-__device__ __forceinline__ void raw_load(Raw<bf16> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  r.u = buf_load_b32(rs, off);
+__device__ __forceinline__ void raw_load(Raw<bf16> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                         uint32_t soff) {
+  r.u = buf_load_b32(rs, off, soff);
 }
-__device__ __forceinline__ void raw_load(Raw<float> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  r.f = buf_load_f32x2(rs, off);
+__device__ __forceinline__ void raw_load(Raw<float> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                         uint32_t soff) {
+  r.f = buf_load_f32x2(rs, off, soff);
 }
 template <class OpT> __device__ __forceinline__ void raw_zero(Raw<OpT> &r);
 template <> __device__ __forceinline__ void raw_zero(Raw<bf16> &r) { r.u = 0u; }
 template <> __device__ __forceinline__ void raw_zero(Raw<float> &r) { r.f = f32x2{0.f, 0.f}; }
 
-// Off-diagonal (row-tile, column-tile) pairs of the 4x4 block lower triangle,
-// and the wave that computes each: wave w takes entries w and w + 4.
-__device__ __forceinline__ void off_tile(int o, int &i, int &j) {
-  i = o == 0 ? 1 : o < 3 ? 2 : 3;
-  j = o == 0 ? 0 : o < 3 ? o - 1 : o - 3;
+// Gram jobs of waves 4..7: (kind, row tile i, column tile j), kind 0 = A, 1 = P.
+// Waves 0..3 compute A of the diagonal tile (w, w) in both orientations and its
+// inverse; waves 4..7 compute P of the diagonal tiles and A, P of the six
+// off-diagonal tiles.
+__device__ __forceinline__ void gram_job(int jw, int u, int &kind, int &i, int &j) {
+  // rows: [P00 A10 P10 A20] [P11 P20 A21 P21] [P22 A30 P30 A31] [P33 P31 A32 P32]
+  const int code[4][4] = {{0x100, 0x010, 0x110, 0x020},
+                          {0x111, 0x120, 0x021, 0x121},
+                          {0x122, 0x030, 0x130, 0x031},
+                          {0x133, 0x131, 0x032, 0x132}};
+  const int c = code[jw][u];
+  kind = c >> 8;
+  i = (c >> 4) & 15;
+  j = c & 15;
 }
 
 template <class OpT, int DV>
-__global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   typedef Layout<OpT, DV> L;
   constexpr int VS = kD / DV;  // value blocks per head
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::kTotal];
 
   unsigned char *region = smem;
-  OpT *Lm = reinterpret_cast<OpT *>(smem + L::kRegion);
-  OpT *Pm = reinterpret_cast<OpT *>(smem + L::kRegion + L::kLm);
-  float *gtot = reinterpret_cast<float *>(smem + L::kRegion + L::kLm + L::kP);
-  float *gmid = gtot + 4 * 128;
-  float *sbeta = gmid + 4 * 128;
+  float *htot = reinterpret_cast<float *>(smem + L::kHalfOff);  // [8][128]
+  float *hfirst = htot + kWaves * 128;                          // [8][128]
+  OpT *Lm = reinterpret_cast<OpT *>(smem + L::kAfterRegion);
+  OpT *Pm = reinterpret_cast<OpT *>(smem + L::kAfterRegion + L::kLm);
+  float *sbeta = reinterpret_cast<float *>(smem + L::kAfterRegion + L::kLm + L::kP);
   float *sgam = sbeta + 64;
 
   // Gram phase views
   OpT *Kr = reinterpret_cast<OpT *>(region);
   OpT *Qr = Kr + 64 * L::LD_KH;
   OpT *Kc = Qr + 64 * L::LD_KH;
-  // recurrence phase views
-  OpT *Qt = reinterpret_cast<OpT *>(region);
-  OpT *nBKt = Qt + 64 * L::LD_D;
-  OpT *KbT = nBKt + 64 * L::LD_D;
+  // recurrence phase views.  With a single Gram pass (bf16), -beta K~ and Q~ are
+  // rescalings of Kr and Qr in place: nBKt aliases Kr and Qt aliases Qr.
+  OpT *nBKt = reinterpret_cast<OpT *>(region);
+  OpT *Qt = nBKt + 64 * L::LD_D;
+  OpT *KbT = Qt + 64 * L::LD_D;
   OpT *BVT = KbT + 128 * L::LD_C;
+  constexpr bool kInPlace = L::NH == 1 && L::LD_D == L::LD_KH;
   // output staging
   OpT *Ost = reinterpret_cast<OpT *>(region);
 
@@ -161,6 +190,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
+  const int st = w >> 1;  // elementwise: 16-token sub-tile of this wave
+  const int th = w & 1;   //              and its half (tokens 8 th .. 8 th + 7)
 
   // ---- work item: (sequence rank, head, value block)
   const int item = blockIdx.x;
@@ -180,7 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   const int H = p.H;
   const int64_t rowstride = (int64_t)H * kD;  // elements between consecutive tokens
   const int vblk = vs * DV;                   // first value column of this workgroup
-  const int vw = vblk + w * (DV / 4);         // first value column of this wave
+  const int vloc = 16 * w;                    // recurrence: this wave's columns (local)
+  const bool rec_wave = w < L::NRW;
 
   const OpT *__restrict__ qg = reinterpret_cast<const OpT *>(p.q) + (int64_t)h * kD;
   const OpT *__restrict__ kg = reinterpret_cast<const OpT *>(p.k) + (int64_t)h * kD;
@@ -192,27 +224,26 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   // 32-wide k-steps of the P U product read.
   for (int e = tid; e < 2 * 256; e += kThreads) {
     const int b = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-    Pm[(32 * b + rr) * L::LD_C + 32 * b + 16 + cc] = from_f32<OpT>(0.f);
+    Pm[(32 * b + rr) * L::LD_C + skpos(32 * b + 16 + cc)] = from_f32<OpT>(0.f);
   }
 
-  // ---- state (fp32 accumulators): S[ct][vt] holds S[16ct+4g4+i][vw+16vt+l16]
-  f32x4 S[8][L::NVT];
+  // ---- state (fp32 accumulators) of the recurrence waves:
+  //      S[ct] holds S[16 ct + 4 g4 + i][vblk + vloc + l16]
+  f32x4 S[8];
   {
-    const float *s0 = p.s0 ? p.s0 + ((int64_t)n * H + h) * (kD * kD) : nullptr;
+    const float *s0 = (p.s0 && rec_wave) ? p.s0 + ((int64_t)n * H + h) * (kD * kD) : nullptr;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S[ct][vt][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * kD + vw + 16 * vt + l16] : 0.f;
+      for (int i = 0; i < 4; ++i)
+        S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * kD + vblk + vloc + l16] : 0.f;
   }
 
-  // ---- register prefetch of a chunk's raw inputs: wave w = tokens 16w..16w+15,
-  //      lane = channels 2*lane, 2*lane+1 (value channels vblk + 2*lane; lanes < 32
-  //      cover the 64 columns when DV = 64).
-  Raw<OpT> rq[16], rk[16], rv[16];
-  f32x2 rg[16];
+  // ---- register prefetch of a chunk's raw inputs: wave w = tokens
+  //      16 st + 8 th + t (t < 8); lane = channels 2 lane, 2 lane + 1 (value
+  //      channels vblk + 2 lane; lanes < 32 cover the 64 columns when DV = 64).
+  Raw<OpT> rq[8], rk[8], rv[8];
+  f32x2 rg[8];
   float rb = 0.f;
   const int c0 = 2 * lane;
   const bool has_v = (DV == 128) || (lane < 32);
@@ -220,164 +251,167 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
   const uint32_t lane_off_g = (uint32_t)c0 * 4u;
   const uint32_t row_qk = (uint32_t)rowstride * (uint32_t)sizeof(OpT);  // bytes per token
   const uint32_t row_g = (uint32_t)rowstride * 4u;
-  auto prefetch = [&](int j) {
-    const int64_t t0 = bos + (int64_t)j * kC + 16 * w;  // uniform
+  // next-chunk descriptors (scalar registers) and valid-row count
+  __amdgpu_buffer_rsrc_t rq_s, rk_s, rv_s, rg_s;
+  uint32_t nv = 0;
+  auto prefetch_begin = [&](int j) {
+    const int64_t t0 = bos + (int64_t)j * kC + 16 * st + 8 * th;  // uniform
     const int64_t rem = bos + len - t0;
-    const uint32_t nv = rem <= 0 ? 0u : (rem >= 16 ? 16u : (uint32_t)rem);  // valid rows
+    nv = rem <= 0 ? 0u : (rem >= 8 ? 8u : (uint32_t)rem);  // valid rows
     // descriptors cover exactly this wave's valid rows of its head
-    const __amdgpu_buffer_rsrc_t rq_s = make_rsrc(qg + t0 * rowstride, nv * row_qk);
-    const __amdgpu_buffer_rsrc_t rk_s = make_rsrc(kg + t0 * rowstride, nv * row_qk);
-    const __amdgpu_buffer_rsrc_t rv_s = make_rsrc(vg + t0 * rowstride, has_v ? nv * row_qk : 0u);
-    const __amdgpu_buffer_rsrc_t rg_s = make_rsrc(gg + t0 * rowstride, nv * row_g);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      if ((uint32_t)t < nv) {
-        raw_load(rq[t], rq_s, lane_off_qk + t * row_qk);
-        raw_load(rk[t], rk_s, lane_off_qk + t * row_qk);
-        raw_load(rv[t], rv_s, lane_off_qk + t * row_qk);  // zero where has_v is false
-        rg[t] = buf_load_f32x2(rg_s, lane_off_g + t * row_g);
-      } else {
-        raw_zero(rq[t]); raw_zero(rk[t]); raw_zero(rv[t]);
-        rg[t] = f32x2{0.f, 0.f};
-      }
+    rq_s = make_rsrc(qg + t0 * rowstride, nv * row_qk);
+    rk_s = make_rsrc(kg + t0 * rowstride, nv * row_qk);
+    rv_s = make_rsrc(vg + t0 * rowstride, has_v ? nv * row_qk : 0u);
+    rg_s = make_rsrc(gg + t0 * rowstride, nv * row_g);
+    rb = (lane < 8 && (uint32_t)lane < nv) ? p.beta[(t0 + lane) * H + h] : 0.f;
+  };
+  auto prefetch_row = [&](int t) {
+    if ((uint32_t)t < nv) {
+      // row offsets are uniform: they go in the scalar offset of the instruction
+      const uint32_t so_qk = __builtin_amdgcn_readfirstlane(t * row_qk);
+      const uint32_t so_g = __builtin_amdgcn_readfirstlane(t * row_g);
+      raw_load(rq[t], rq_s, lane_off_qk, so_qk);
+      raw_load(rk[t], rk_s, lane_off_qk, so_qk);
+      raw_load(rv[t], rv_s, lane_off_qk, so_qk);  // zero where has_v is false
+      rg[t] = buf_load_f32x2(rg_s, lane_off_g, so_g);
+    } else {
+      raw_zero(rq[t]); raw_zero(rk[t]); raw_zero(rv[t]);
+      rg[t] = f32x2{0.f, 0.f};
     }
-    rb = (lane < 16 && (uint32_t)l16 < nv) ? p.beta[(t0 + l16) * H + h] : 0.f;
+  };
+  auto prefetch = [&](int j) {
+    prefetch_begin(j);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) prefetch_row(t);
   };
   if (nchunks > 0) prefetch(0);
 
   for (int j = 0; j < nchunks; ++j) {
     const int Lc = (int)((len - (int64_t)j * kC) < kC ? (len - (int64_t)j * kC) : kC);
 
-    // ===== P0: per-channel cumulative log2-decay inside the sub-tile
-    float G0[16], G1[16];
+    // ===== P0: per-channel cumulative log2-decay over this wave's 8 tokens
+    float Gl0[8], Gl1[8];
     {
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 8; ++t) {
         a0 += rg[t][0] * kLog2e;
         a1 += rg[t][1] * kLog2e;
-        G0[t] = a0;
-        G1[t] = a1;
+        Gl0[t] = a0;
+        Gl1[t] = a1;
       }
-      *reinterpret_cast<f32x2 *>(gtot + w * 128 + c0) = f32x2{a0, a1};
-      *reinterpret_cast<f32x2 *>(gmid + w * 128 + c0) = f32x2{G0[kRef], G1[kRef]};
-      if (lane < 16) sbeta[16 * w + lane] = rb;
+      *reinterpret_cast<f32x2 *>(htot + w * 128 + c0) = f32x2{a0, a1};
+      *reinterpret_cast<f32x2 *>(hfirst + w * 128 + c0) = f32x2{Gl0[0], Gl1[0]};
+      if (lane < 8) sbeta[16 * st + 8 * th + lane] = rb;
     }
     block_sync();
 
-    // chunk-relative reference values G(16i + kRef) for all sub-tiles, and G(last)
-    float gref0[4], gref1[4], glast0 = 0.f, glast1 = 0.f;
+    // chunk-relative G at each sub-tile's reference token (its token 8), G(last),
+    // and this half's offset from its sub-tile start
+    float gref0[4], gref1[4], glast0 = 0.f, glast1 = 0.f, gmid0 = 0.f, gmid1 = 0.f;
+    float hoff0 = 0.f, hoff1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x2 gm = *reinterpret_cast<const f32x2 *>(gmid + i * 128 + c0);
-      const f32x2 gt = *reinterpret_cast<const f32x2 *>(gtot + i * 128 + c0);
-      gref0[i] = glast0 + gm[0];
-      gref1[i] = glast1 + gm[1];
-      glast0 += gt[0];
-      glast1 += gt[1];
+      const f32x2 t0v = *reinterpret_cast<const f32x2 *>(htot + (2 * i) * 128 + c0);
+      const f32x2 t1v = *reinterpret_cast<const f32x2 *>(htot + (2 * i + 1) * 128 + c0);
+      const f32x2 f1v = *reinterpret_cast<const f32x2 *>(hfirst + (2 * i + 1) * 128 + c0);
+      const float m0 = t0v[0] + f1v[0], m1 = t0v[1] + f1v[1];  // sub-tile relative
+      gref0[i] = glast0 + m0;
+      gref1[i] = glast1 + m1;
+      if (i == st) {
+        gmid0 = m0;
+        gmid1 = m1;
+        hoff0 = th ? t0v[0] : 0.f;
+        hoff1 = th ? t0v[1] : 0.f;
+      }
+      glast0 += t0v[0] + t1v[0];
+      glast1 += t0v[1] + t1v[1];
     }
     // E1 = e^{G_t - G_ref} (row factor), E2 = e^{G_ref - G_t} (column factor)
-    float E1a[16], E1b[16], E2a[16], E2b[16];
+    float E1a[8], E1b[8], E2a[8], E2b[8];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float d0 = G0[t] - G0[kRef], d1 = G1[t] - G1[kRef];
+    for (int t = 0; t < 8; ++t) {
+      const float d0 = hoff0 + Gl0[t] - gmid0, d1 = hoff1 + Gl1[t] - gmid1;
       E1a[t] = fast_exp2(d0);
       E1b[t] = fast_exp2(d1);
       E2a[t] = fast_exp2(-d0);
       E2b[t] = fast_exp2(-d1);
     }
 
-    // ===== P1 + Gram.  Wave w computes the diagonal tile (w, w) -- A in both
-    // orientations for the in-register Neumann inverse, and P -- plus the
-    // off-diagonal tiles w and w + 4 of the list (1,0),(2,0),(2,1),(3,0),(3,1),(3,2).
-    f32x4 accN = {0.f, 0.f, 0.f, 0.f}, accNT = accN, accPd = accN;
-    f32x4 accA[2] = {accN, accN}, accP[2] = {accN, accN};
+    // ===== P1 + Gram
+    f32x4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hc = 0; hc < L::NH; ++hc) {
       if (c0 / L::KH == hc) {
         const int cc = c0 - hc * L::KH;
-        float F0[4], F1[4];  // e^{G_ref(i) - G_ref(w)} for i > w
+        float F0[4], F1[4];  // e^{G_ref(i) - G_ref(st)} for i > st
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          F0[i] = i > w ? fast_exp2(gref0[i] - gref0[w]) : 1.f;
-          F1[i] = i > w ? fast_exp2(gref1[i] - gref1[w]) : 1.f;
+          F0[i] = i > st ? fast_exp2(gref0[i] - gref0[st]) : 1.f;
+          F1[i] = i > st ? fast_exp2(gref1[i] - gref1[st]) : 1.f;
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = 16 * w + t;
+        for (int t = 0; t < 8; ++t) {
+          const int r = 16 * st + 8 * th + t;
           const float k0 = rk[t].lo(), k1 = rk[t].hi();
           const float q0 = rq[t].lo(), q1 = rq[t].hi();
-          store2<OpT>(Kr + r * L::LD_KH + cc, k0 * E1a[t], k1 * E1b[t]);
-          store2<OpT>(Qr + r * L::LD_KH + cc, q0 * E1a[t], q1 * E1b[t]);
+          // columns in split-k order (the Gram products sum over channels, so a
+          // permutation shared by all three operands leaves them unchanged)
+          const int pc = skpos(cc);
+          store2<OpT>(Kr + r * L::LD_KH + pc, k0 * E1a[t], k1 * E1b[t]);
+          store2<OpT>(Qr + r * L::LD_KH + pc, q0 * E1a[t], q1 * E1b[t]);
           const float b0 = k0 * E2a[t], b1 = k1 * E2b[t];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (i >= w)
-              store2<OpT>(Kc + (tri_index(i, w) * 16 + t) * L::LD_KH + cc, b0 * F0[i], b1 * F1[i]);
+            if (i >= st)
+              store2<OpT>(Kc + (tri_index(i, st) * 16 + 8 * th + t) * L::LD_KH + pc, b0 * F0[i],
+                          b1 * F1[i]);
         }
       }
       block_sync();
-      const OpT *krw = Kr + 16 * w * L::LD_KH;
-      const OpT *qrw = Qr + 16 * w * L::LD_KH;
-      const OpT *kcw = Kc + tri_index(w, w) * 16 * L::LD_KH;
+      if (w < 4) {
+        // A_ww as [r][s] (acc[0]) and [s][r] (acc[1])
+        const OpT *krw = Kr + 16 * w * L::LD_KH;
+        const OpT *kcw = Kc + tri_index(w, w) * 16 * L::LD_KH;
 #pragma unroll
-      for (int kk = 0; kk < L::KH / 32; ++kk) {
-        Frag<OpT> fk, fc, fq;
-        lds_frag_ck(fk, krw, L::LD_KH, l16, 32 * kk, g4);
-        lds_frag_ck(fc, kcw, L::LD_KH, l16, 32 * kk, g4);
-        lds_frag_ck(fq, qrw, L::LD_KH, l16, 32 * kk, g4);
-        mma(accN, fk, fc);   // [r][s]
-        mma(accNT, fc, fk);  // [s][r]
-        mma(accPd, fc, fq);  // [s][r] of P
-      }
+        for (int kk = 0; kk < L::KH / 32; ++kk) {
+          Frag<OpT> fk, fc;
+          lds_frag_ck(fk, krw, L::LD_KH, l16, 32 * kk, g4);
+          lds_frag_ck(fc, kcw, L::LD_KH, l16, 32 * kk, g4);
+          mma(acc[0], fk, fc);
+          mma(acc[1], fc, fk);
+        }
+      } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int o = w + 4 * u;
-        if (o < 6) {
-          int ti, tj;
-          off_tile(o, ti, tj);
+        for (int u = 0; u < 4; ++u) {
+          int kind, ti, tj;
+          gram_job(w - 4, u, kind, ti, tj);
+          const OpT *xs = Kc + tri_index(ti, tj) * 16 * L::LD_KH;
+          const OpT *ys = (kind ? Qr : Kr) + 16 * ti * L::LD_KH;
 #pragma unroll
           for (int kk = 0; kk < L::KH / 32; ++kk) {
-            Frag<OpT> xs, yk, yq;
-            lds_frag_ck(xs, Kc + tri_index(ti, tj) * 16 * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
-            lds_frag_ck(yk, Kr + 16 * ti * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
-            lds_frag_ck(yq, Qr + 16 * ti * L::LD_KH, L::LD_KH, l16, 32 * kk, g4);
-            mma(accA[u], xs, yk);
-            mma(accP[u], xs, yq);
+            Frag<OpT> fx, fy;
+            lds_frag_ck(fx, xs, L::LD_KH, l16, 32 * kk, g4);
+            lds_frag_ck(fy, ys, L::LD_KH, l16, 32 * kk, g4);
+            mma(acc[u], fx, fy);  // lane holds [r = 16 ti + l16][s = 16 tj + 4 g4 + i]
           }
         }
       }
       if (L::NH > 1) block_sync();  // the next channel pass rewrites the Gram region
     }
 
-    // off-diagonal results: lane holds A[r = 16 ti + l16][s = 16 tj + 4 g4 + i]
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int o = w + 4 * u;
-      if (o < 6) {
-        int ti, tj;
-        off_tile(o, ti, tj);
-        const int r = 16 * ti + l16;
-        const float br = sbeta[r];
-        store4<OpT>(Lm + r * L::LD_C + 16 * tj + 4 * g4, accA[u] * (-br));
-        store4<OpT>(Pm + r * L::LD_C + 16 * tj + 4 * g4, accP[u]);
-      }
-    }
-    // diagonal tile w: P (s <= r) and the inverse of I + A_ww
-    {
-      const int r = 16 * w + l16;
-      f32x4 pv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = (4 * g4 + i) <= l16 ? accPd[i] : 0.f;
-      store4<OpT>(Pm + r * L::LD_C + 16 * w + 4 * g4, pv);
-      // R-layout tiles (lane holds M[4g4+i][l16]):  N = strictly lower A_ww,  NT = N^T
+    if (w < 4) {
+      // inverse of the diagonal block (I + A_ww), in registers.  R layout: lane
+      // holds M[4 g4 + i][l16].  N = strictly lower A_ww, NT = N^T.
       f32x4 N, NT;
       const float bl = sbeta[16 * w + l16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int a = 4 * g4 + i;
-        N[i] = l16 < a ? sbeta[16 * w + a] * accN[i] : 0.f;
-        NT[i] = a < l16 ? bl * accNT[i] : 0.f;
+        N[i] = l16 < a ? sbeta[16 * w + a] * acc[0][i] : 0.f;
+        NT[i] = a < l16 ? bl * acc[1][i] : 0.f;
       }
       // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0.
       // rr_tn(B, C) = B^T C, so products pair each power with its transpose.
@@ -398,37 +432,66 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         Lm[(16 * w + 4 * g4 + i) * L::LD_C + 16 * w + l16] = from_f32<OpT>(Xd[i]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int kind, ti, tj;
+        gram_job(w - 4, u, kind, ti, tj);
+        const int r = 16 * ti + l16;
+        if (kind == 0) {  // -beta_r A (strictly lower, off-diagonal tile)
+          store4<OpT>(Lm + r * L::LD_C + 16 * tj + 4 * g4, acc[u] * (-sbeta[r]));
+        } else {          // P, masked to s <= r on the diagonal
+          f32x4 pv = acc[u];
+          if (ti == tj) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[i] = (4 * g4 + i) <= l16 ? pv[i] : 0.f;
+          }
+          store4<OpT>(Pm + r * L::LD_C + skpos(16 * tj + 4 * g4), pv);
+        }
+      }
     }
     block_sync();  // Gram region free; Lm / Pm written
 
     // ===== P2: operands of the state products (region now holds the recurrence views)
     {
-      const float eB0 = fast_exp2(gref0[w]), eB1 = fast_exp2(gref1[w]);               // e^{G_ref}
-      const float eK0 = fast_exp2(glast0 - gref0[w]), eK1 = fast_exp2(glast1 - gref1[w]);  // e^{G_C-G_ref}
-      float kb0[16], kb1[16], bv0[16], bv1[16];
+      const float eB0 = fast_exp2(gref0[st]), eB1 = fast_exp2(gref1[st]);  // e^{G_ref}
+      const float eK0 = fast_exp2(glast0 - gref0[st]);                      // e^{G_C - G_ref}
+      const float eK1 = fast_exp2(glast1 - gref1[st]);
+      float kb0[8], kb1[8], bv0[8], bv1[8];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int r = 16 * w + t;
+      for (int t = 0; t < 8; ++t) {
+        const int r = 16 * st + 8 * th + t;
         const float br = sbeta[r];
-        const float e0 = E1a[t] * eB0, e1 = E1b[t] * eB1;
-        store2<OpT>(Qt + r * L::LD_D + c0, rq[t].lo() * e0, rq[t].hi() * e1);
-        store2<OpT>(nBKt + r * L::LD_D + c0, -br * rk[t].lo() * e0, -br * rk[t].hi() * e1);
+        if (kInPlace) {
+          // Q~ = Qr e^{G_ref}, -beta K~ = -beta Kr e^{G_ref}, element by element in place
+          OpT *pq = Qt + r * L::LD_D + skpos(c0);
+          OpT *pk = nBKt + r * L::LD_D + skpos(c0);
+          const float q0 = to_f32(pq[0]), q1 = to_f32(pq[1]);
+          const float kr0 = to_f32(pk[0]), kr1 = to_f32(pk[1]);
+          store2<OpT>(pq, q0 * eB0, q1 * eB1);
+          store2<OpT>(pk, -br * kr0 * eB0, -br * kr1 * eB1);
+        } else {
+          const float e0 = E1a[t] * eB0, e1 = E1b[t] * eB1;
+          store2<OpT>(Qt + r * L::LD_D + skpos(c0), rq[t].lo() * e0, rq[t].hi() * e1);
+          store2<OpT>(nBKt + r * L::LD_D + skpos(c0), -br * rk[t].lo() * e0, -br * rk[t].hi() * e1);
+        }
         kb0[t] = rk[t].lo() * E2a[t] * eK0;
         kb1[t] = rk[t].hi() * E2b[t] * eK1;
         bv0[t] = br * rv[t].lo();
         bv1[t] = br * rv[t].hi();
       }
-      // transposed rows: 16 consecutive tokens of one channel, 16-byte stores
+      // transposed rows: 8 consecutive tokens of one channel
+      const int tc = 16 * st + 8 * th;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        store4<OpT>(KbT + c0 * L::LD_C + 16 * w + 4 * q4,
+      for (int q4 = 0; q4 < 2; ++q4) {
+        store4<OpT>(KbT + c0 * L::LD_C + skpos(tc + 4 * q4),
                     f32x4{kb0[4 * q4], kb0[4 * q4 + 1], kb0[4 * q4 + 2], kb0[4 * q4 + 3]});
-        store4<OpT>(KbT + (c0 + 1) * L::LD_C + 16 * w + 4 * q4,
+        store4<OpT>(KbT + (c0 + 1) * L::LD_C + skpos(tc + 4 * q4),
                     f32x4{kb1[4 * q4], kb1[4 * q4 + 1], kb1[4 * q4 + 2], kb1[4 * q4 + 3]});
         if (has_v) {
-          store4<OpT>(BVT + c0 * L::LD_C + 16 * w + 4 * q4,
+          store4<OpT>(BVT + c0 * L::LD_C + tc + 4 * q4,
                       f32x4{bv0[4 * q4], bv0[4 * q4 + 1], bv0[4 * q4 + 2], bv0[4 * q4 + 3]});
-          store4<OpT>(BVT + (c0 + 1) * L::LD_C + 16 * w + 4 * q4,
+          store4<OpT>(BVT + (c0 + 1) * L::LD_C + tc + 4 * q4,
                       f32x4{bv1[4 * q4], bv1[4 * q4 + 1], bv1[4 * q4 + 2], bv1[4 * q4 + 3]});
         }
       }
@@ -438,118 +501,95 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
     if (j + 1 < nchunks) prefetch(j + 1);
     block_sync();
 
-    // ===== recurrence on this wave's value columns
-    // Y = beta V - beta K~ S        (lane holds Y[s = 16 st + 4 g4 + i][v])
-    f32x4 accY[4][L::NVT];
+    // ===== recurrence on this wave's 16 value columns
+    f32x4 accOT[4];
+    if (rec_wave) {
+      // Y = beta V - beta K~ S        (lane holds Y[s = 16 st + 4 g4 + i][v])
+      f32x4 accY[4];
 #pragma unroll
-    for (int vt = 0; vt < L::NVT; ++vt) {
-      const int vc = vw - vblk + 16 * vt + l16;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int s4 = 0; s4 < 4; ++s4) {
         Frag4<OpT> b4;
-        lds_frag4(b4, BVT, L::LD_C, vc, 16 * st, g4);
+        lds_frag4(b4, BVT, L::LD_C, vloc + l16, 16 * s4, g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) accY[st][vt][i] = to_f32(b4.v[i]);
+        for (int i = 0; i < 4; ++i) accY[s4][i] = to_f32(b4.v[i]);
       }
-    }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      Frag<OpT> sf[L::NVT];
+      for (int kk = 0; kk < 4; ++kk) {
+        Frag<OpT> sf;
+        acc_frag_sk(sf, S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt) acc_frag_sk(sf[vt], S[2 * kk][vt], S[2 * kk + 1][vt]);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        Frag<OpT> xb;
-        lds_frag_sk(xb, nBKt, L::LD_D, 16 * st + l16, 32 * kk, g4);
-#pragma unroll
-        for (int vt = 0; vt < L::NVT; ++vt) mma(accY[st][vt], xb, sf[vt]);
-      }
-    }
-    // U = (I + A)^{-1} Y by block forward substitution:
-    //   U_i = X_ii (Y_i - sum_{k<i} A_ik U_k)
-    f32x4 accU[4][L::NVT];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int k = 0; k < i; ++k) {
-        Frag4<OpT> la;
-        lds_frag4(la, Lm, L::LD_C, 16 * i + l16, 16 * k, g4);
-#pragma unroll
-        for (int vt = 0; vt < L::NVT; ++vt) {
-          Frag4<OpT> uk;
-          acc_frag4(uk, accU[k][vt]);
-          mma16(accY[i][vt], la, uk);
+        for (int s4 = 0; s4 < 4; ++s4) {
+          Frag<OpT> xb;
+          lds_frag_ck(xb, nBKt, L::LD_D, 16 * s4 + l16, 32 * kk, g4);
+          mma(accY[s4], xb, sf);
         }
       }
-      Frag4<OpT> xd;
-      lds_frag4(xd, Lm, L::LD_C, 16 * i + l16, 16 * i, g4);
+      // U = (I + A)^{-1} Y by block forward substitution:
+      //   U_i = X_ii (Y_i - sum_{k<i} A_ik U_k)
+      f32x4 accU[4];
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt) {
-        Frag4<OpT> yi;
-        acc_frag4(yi, accY[i][vt]);
-        accU[i][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma16(accU[i][vt], xd, yi);
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < i; ++k) {
+          Frag4<OpT> la, uk;
+          lds_frag4(la, Lm, L::LD_C, 16 * i + l16, 16 * k, g4);
+          acc_frag4(uk, accU[k]);
+          mma16(accY[i], la, uk);
+        }
+        Frag4<OpT> xd, yi;
+        lds_frag4(xd, Lm, L::LD_C, 16 * i + l16, 16 * i, g4);
+        acc_frag4(yi, accY[i]);
+        accU[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mma16(accU[i], xd, yi);
       }
-    }
-    Frag<OpT> uf[2][L::NVT];
+      Frag<OpT> uf[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[kk], accU[2 * kk], accU[2 * kk + 1]);
+      // O^T = S^T Q~^T + U^T P^T      (lane holds O[r = 16 rt + l16][v = .. + 4 g4 + i])
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt)
-        acc_frag_sk(uf[kk][vt], accU[2 * kk][vt], accU[2 * kk + 1][vt]);
-    // O^T = S^T Q~^T + U^T P^T      (lane holds O[r = 16 rt + l16][v = .. + 4 g4 + i])
-    f32x4 accOT[L::NVT][4];
+      for (int rt = 0; rt < 4; ++rt) accOT[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int vt = 0; vt < L::NVT; ++vt)
+      for (int kk = 0; kk < 4; ++kk) {
+        Frag<OpT> sf;
+        acc_frag_sk(sf, S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) accOT[vt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      Frag<OpT> sf[L::NVT];
-#pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt) acc_frag_sk(sf[vt], S[2 * kk][vt], S[2 * kk + 1][vt]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        Frag<OpT> xq;
-        lds_frag_sk(xq, Qt, L::LD_D, 16 * rt + l16, 32 * kk, g4);
-#pragma unroll
-        for (int vt = 0; vt < L::NVT; ++vt) mma(accOT[vt][rt], sf[vt], xq);
-      }
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk <= rt / 2) {
-          Frag<OpT> xp;
-          lds_frag_sk(xp, Pm, L::LD_C, 16 * rt + l16, 32 * kk, g4);
-#pragma unroll
-          for (int vt = 0; vt < L::NVT; ++vt) mma(accOT[vt][rt], uf[kk][vt], xp);
+        for (int rt = 0; rt < 4; ++rt) {
+          Frag<OpT> xq;
+          lds_frag_ck(xq, Qt, L::LD_D, 16 * rt + l16, 32 * kk, g4);
+          mma(accOT[rt], sf, xq);
         }
       }
-    // S <- Gamma S + Kbar^T U
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const f32x4 gm = *reinterpret_cast<const f32x4 *>(sgam + 16 * ct + 4 * g4);
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt) S[ct][vt] *= gm;
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk <= rt / 2) {
+            Frag<OpT> xp;
+            lds_frag_ck(xp, Pm, L::LD_C, 16 * rt + l16, 32 * kk, g4);
+            mma(accOT[rt], uf[kk], xp);
+          }
+        }
+      // S <- Gamma S + Kbar^T U
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<OpT> xk;
-        lds_frag_sk(xk, KbT, L::LD_C, 16 * ct + l16, 32 * kk, g4);
+      for (int ct = 0; ct < 8; ++ct) {
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sgam + 16 * ct + 4 * g4);
+        S[ct] *= gm;
 #pragma unroll
-        for (int vt = 0; vt < L::NVT; ++vt) mma(S[ct][vt], xk, uf[kk][vt]);
+        for (int kk = 0; kk < 2; ++kk) {
+          Frag<OpT> xk;
+          lds_frag_ck(xk, KbT, L::LD_C, 16 * ct + l16, 32 * kk, g4);
+          mma(S[ct], xk, uf[kk]);
+        }
       }
     }
     block_sync();
 
     // ===== output: stage O (scaled, io dtype) in LDS, then row-contiguous stores
-#pragma unroll
-    for (int vt = 0; vt < L::NVT; ++vt)
+    if (rec_wave) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        store4<OpT>(Ost + (16 * rt + l16) * L::LD_O + (vw - vblk) + 16 * vt + 4 * g4,
-                    accOT[vt][rt] * p.scale);
+        store4<OpT>(Ost + (16 * rt + l16) * L::LD_O + vloc + 4 * g4, accOT[rt] * p.scale);
+    }
     block_sync();
     {
       constexpr int kVec = 16 / (int)sizeof(OpT);       // elements per 16-byte store
@@ -566,15 +606,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkParams p) {
     // (the next chunk's first barrier orders these LDS reads before its writes)
   }
 
-  if (p.sfinal) {
+  if (p.sfinal && rec_wave) {
     float *sf = p.sfinal + ((int64_t)n * H + h) * (kD * kD);
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int vt = 0; vt < L::NVT; ++vt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sf[(16 * ct + 4 * g4 + i) * kD + vw + 16 * vt + l16] = S[ct][vt][i];
+      for (int i = 0; i < 4; ++i)
+        sf[(16 * ct + 4 * g4 + i) * kD + vblk + vloc + l16] = S[ct][i];
   }
 }
 

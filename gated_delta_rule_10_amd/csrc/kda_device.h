@@ -150,11 +150,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            0x00020000);
 }
 constexpr int kNonTemporal = 2;  // streaming access: do not keep in the caches
-__device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+// `off` is the per-lane byte offset, `soff` a wave-uniform byte offset (scalar).
+__device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                 uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kNonTemporal);
 }
-__device__ __forceinline__ f32x2 buf_load_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+__device__ __forceinline__ f32x2 buf_load_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                uint32_t soff = 0) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kNonTemporal));
 }
 __device__ __forceinline__ void buf_store_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4 &v) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
