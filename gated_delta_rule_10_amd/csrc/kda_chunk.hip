@@ -81,6 +81,10 @@ __device__ __forceinline__ int tri_index(int i, int j) { return i * (i + 1) / 2 
 __device__ __forceinline__ int skpos(int c) {
   return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
 }
+// Column held at position p (inverse of skpos).
+__device__ __forceinline__ int skcol(int p) {
+  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
 
 template <class OpT, int DV>
 struct Layout {
@@ -93,27 +97,35 @@ struct Layout {
   static constexpr int LD_O = DV + PADE;
   static constexpr int NRW = DV / 16;                    // waves running the recurrence
   static_assert(NRW <= kWaves, "value block too wide");
-  // Region R: three phases reuse the same bytes.
+  // EARLY (bf16): the transposed operands Kbar^T and (beta V)^T get buffers of
+  // their own and are written with the Gram operands, so the raw inputs are
+  // dead -- and the next chunk's loads can be issued -- before the Gram
+  // products start.  fp32 operands do not leave room for that; there they
+  // share the region and are written after the inverse.
+  static constexpr bool EARLY = sizeof(OpT) == 2;
+  // Region R: phases reuse the same bytes.
   //  Gram:       Kr[64][LD_KH], Qr[64][LD_KH], Kc[160][LD_KH]                 (OpT)
-  //  recurrence: Qt[64][LD_D], nBKt[64][LD_D], KbT[128][LD_C], BVT[DV][LD_C]  (OpT)
+  //  recurrence: nBKt[64][LD_D], Qt[64][LD_D] (+ KbT[128][LD_C], BVT[DV][LD_C] unless EARLY)
   //  output:     Ost[64][LD_O]                                               (OpT)
   static constexpr size_t kGram = (size_t)(64 + 64 + 160) * LD_KH * sizeof(OpT);
-  static constexpr size_t kRec =
-      ((size_t)2 * 64 * LD_D + (size_t)128 * LD_C + (size_t)DV * LD_C) * sizeof(OpT);
+  static constexpr size_t kKV = ((size_t)128 * LD_C + (size_t)DV * LD_C) * sizeof(OpT);
+  static constexpr size_t kRec = (size_t)2 * 64 * LD_D * sizeof(OpT) + (EARLY ? 0 : kKV);
   static constexpr size_t kOut = (size_t)64 * LD_O * sizeof(OpT);
   static constexpr size_t kGramOut = kGram > kOut ? kGram : kOut;
   static constexpr size_t kRegion = kGramOut > kRec ? kGramOut : kRec;
+  static constexpr size_t kKVOff = EARLY ? kRegion : 2 * 64 * LD_D * sizeof(OpT);
+  static constexpr size_t kAfterKV = EARLY ? kRegion + kKV : kRegion;
   // half-sub-tile totals and first values of the log-decay ([2][8][128] fp32):
   // inside the region when the recurrence view leaves room past the Gram view
   static constexpr size_t kHalf = (size_t)2 * kWaves * 128 * 4;
   static constexpr bool kHalfInRegion = kRegion - kGramOut >= kHalf;
-  static constexpr size_t kHalfOff = kHalfInRegion ? kGramOut : kRegion;
-  static constexpr size_t kAfterRegion = kHalfInRegion ? kRegion : kRegion + kHalf;
+  static constexpr size_t kHalfOff = kHalfInRegion ? kGramOut : kAfterKV;
+  static constexpr size_t kAfterRegion = kHalfInRegion ? kAfterKV : kAfterKV + kHalf;
   // Lm: the unit-lower-triangular system, -A in the strictly lower 16x16 blocks
   // and the inverse of each diagonal block on the diagonal; Pm: the P matrix.
   static constexpr size_t kLm = (size_t)64 * LD_C * sizeof(OpT);
   static constexpr size_t kP = kLm;
-  static constexpr size_t kSmall = (size_t)(64 + 128) * 4;
+  static constexpr size_t kSmall = (size_t)(64 + 128 + 4 * 128) * 4;
   static constexpr size_t kTotal = kAfterRegion + kLm + kP + kSmall;
   static_assert(kTotal <= 160 * 1024, "LDS budget exceeded");
 };
@@ -170,6 +182,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   OpT *Pm = reinterpret_cast<OpT *>(smem + L::kAfterRegion + L::kLm);
   float *sbeta = reinterpret_cast<float *>(smem + L::kAfterRegion + L::kLm + L::kP);
   float *sgam = sbeta + 64;
+  float *eBt = sgam + 128;  // [4][128] e^{G_ref} per sub-tile and channel
 
   // Gram phase views
   OpT *Kr = reinterpret_cast<OpT *>(region);
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   // rescalings of Kr and Qr in place: nBKt aliases Kr and Qt aliases Qr.
   OpT *nBKt = reinterpret_cast<OpT *>(region);
   OpT *Qt = nBKt + 64 * L::LD_D;
-  OpT *KbT = Qt + 64 * L::LD_D;
+  OpT *KbT = reinterpret_cast<OpT *>(smem + L::kKVOff);
   OpT *BVT = KbT + 128 * L::LD_C;
   constexpr bool kInPlace = L::NH == 1 && L::LD_D == L::LD_KH;
   // output staging
@@ -338,6 +351,36 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       E2b[t] = fast_exp2(-d1);
     }
 
+    // Kbar^T (rows = channels) and (beta V)^T (rows = value columns), 8
+    // consecutive tokens per row: Kbar = k e^{G_C - G} = k E2 e^{G_C - G_ref}
+    auto write_kv = [&](const float *e2a, const float *e2b) {
+      const float eK0 = fast_exp2(glast0 - gref0[st]);
+      const float eK1 = fast_exp2(glast1 - gref1[st]);
+      float kb0[8], kb1[8], bv0[8], bv1[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float br = sbeta[16 * st + 8 * th + t];
+        kb0[t] = rk[t].lo() * e2a[t] * eK0;
+        kb1[t] = rk[t].hi() * e2b[t] * eK1;
+        bv0[t] = br * rv[t].lo();
+        bv1[t] = br * rv[t].hi();
+      }
+      const int tc = 16 * st + 8 * th;
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4) {
+        store4<OpT>(KbT + c0 * L::LD_C + skpos(tc + 4 * q4),
+                    f32x4{kb0[4 * q4], kb0[4 * q4 + 1], kb0[4 * q4 + 2], kb0[4 * q4 + 3]});
+        store4<OpT>(KbT + (c0 + 1) * L::LD_C + skpos(tc + 4 * q4),
+                    f32x4{kb1[4 * q4], kb1[4 * q4 + 1], kb1[4 * q4 + 2], kb1[4 * q4 + 3]});
+        if (has_v) {
+          store4<OpT>(BVT + c0 * L::LD_C + tc + 4 * q4,
+                      f32x4{bv0[4 * q4], bv0[4 * q4 + 1], bv0[4 * q4 + 2], bv0[4 * q4 + 3]});
+          store4<OpT>(BVT + (c0 + 1) * L::LD_C + tc + 4 * q4,
+                      f32x4{bv1[4 * q4], bv1[4 * q4 + 1], bv1[4 * q4 + 2], bv1[4 * q4 + 3]});
+        }
+      }
+    };
+
     // ===== P1 + Gram
     f32x4 acc[4];
 #pragma unroll
@@ -370,6 +413,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
                           b1 * F1[i]);
         }
       }
+      if (L::EARLY) {
+        write_kv(E2a, E2b);
+        if (th == 0)
+          *reinterpret_cast<f32x2 *>(eBt + st * 128 + c0) =
+              f32x2{fast_exp2(gref0[st]), fast_exp2(gref1[st])};
+        if (w == 0)
+          *reinterpret_cast<f32x2 *>(sgam + c0) = f32x2{fast_exp2(glast0), fast_exp2(glast1)};
+        // raw registers are dead: start loading the next chunk
+        if (j + 1 < nchunks) prefetch(j + 1);
+      }
       block_sync();
       if (w < 4) {
         // A_ww as [r][s] (acc[0]) and [s][r] (acc[1])
@@ -401,6 +454,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       }
       if (L::NH > 1) block_sync();  // the next channel pass rewrites the Gram region
     }
+    if (L::EARLY) block_sync();  // Gram operands read: Kr, Qr may be rescaled in place
 
     if (w < 4) {
       // inverse of the diagonal block (I + A_ww), in registers.  R layout: lane
@@ -449,15 +503,38 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           store4<OpT>(Pm + r * L::LD_C + skpos(16 * tj + 4 * g4), pv);
         }
       }
+      if (L::EARLY) {
+        // Q~ = Qr e^{G_ref}, -beta K~ = -beta Kr e^{G_ref}: every row, in place,
+        // four stored columns (four consecutive channels) at a time
+        const int lt = tid - 4 * 64;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int e = lt + 256 * k;             // granule index: 64 rows x 32
+          const int r = e >> 5, pos = (e & 31) * 4;
+          const f32x4 eb = *reinterpret_cast<const f32x4 *>(eBt + (r >> 4) * 128 + skcol(pos));
+          const float nb = -sbeta[r];
+          OpT *pq = Qt + r * L::LD_D + pos;
+          OpT *pk = nBKt + r * L::LD_D + pos;
+          Frag4<OpT> fq, fk;
+          fq.v = *reinterpret_cast<const decltype(fq.v) *>(pq);
+          fk.v = *reinterpret_cast<const decltype(fk.v) *>(pk);
+          f32x4 vq, vk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vq[i] = to_f32(fq.v[i]) * eb[i];
+            vk[i] = to_f32(fk.v[i]) * eb[i] * nb;
+          }
+          store4<OpT>(pq, vq);
+          store4<OpT>(pk, vk);
+        }
+      }
     }
     block_sync();  // Gram region free; Lm / Pm written
 
-    // ===== P2: operands of the state products (region now holds the recurrence views)
-    {
+    // ===== P2 (fp32 operands): operands of the state products (region now holds
+    // the recurrence views)
+    if (!L::EARLY) {
       const float eB0 = fast_exp2(gref0[st]), eB1 = fast_exp2(gref1[st]);  // e^{G_ref}
-      const float eK0 = fast_exp2(glast0 - gref0[st]);                      // e^{G_C - G_ref}
-      const float eK1 = fast_exp2(glast1 - gref1[st]);
-      float kb0[8], kb1[8], bv0[8], bv1[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int r = 16 * st + 8 * th + t;
@@ -475,31 +552,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           store2<OpT>(Qt + r * L::LD_D + skpos(c0), rq[t].lo() * e0, rq[t].hi() * e1);
           store2<OpT>(nBKt + r * L::LD_D + skpos(c0), -br * rk[t].lo() * e0, -br * rk[t].hi() * e1);
         }
-        kb0[t] = rk[t].lo() * E2a[t] * eK0;
-        kb1[t] = rk[t].hi() * E2b[t] * eK1;
-        bv0[t] = br * rv[t].lo();
-        bv1[t] = br * rv[t].hi();
       }
-      // transposed rows: 8 consecutive tokens of one channel
-      const int tc = 16 * st + 8 * th;
-#pragma unroll
-      for (int q4 = 0; q4 < 2; ++q4) {
-        store4<OpT>(KbT + c0 * L::LD_C + skpos(tc + 4 * q4),
-                    f32x4{kb0[4 * q4], kb0[4 * q4 + 1], kb0[4 * q4 + 2], kb0[4 * q4 + 3]});
-        store4<OpT>(KbT + (c0 + 1) * L::LD_C + skpos(tc + 4 * q4),
-                    f32x4{kb1[4 * q4], kb1[4 * q4 + 1], kb1[4 * q4 + 2], kb1[4 * q4 + 3]});
-        if (has_v) {
-          store4<OpT>(BVT + c0 * L::LD_C + tc + 4 * q4,
-                      f32x4{bv0[4 * q4], bv0[4 * q4 + 1], bv0[4 * q4 + 2], bv0[4 * q4 + 3]});
-          store4<OpT>(BVT + (c0 + 1) * L::LD_C + tc + 4 * q4,
-                      f32x4{bv1[4 * q4], bv1[4 * q4 + 1], bv1[4 * q4 + 2], bv1[4 * q4 + 3]});
-        }
-      }
+      write_kv(E2a, E2b);
       if (w == 0) *reinterpret_cast<f32x2 *>(sgam + c0) = f32x2{fast_exp2(glast0), fast_exp2(glast1)};
+      // raw registers are free: start loading the next chunk
+      if (j + 1 < nchunks) prefetch(j + 1);
+      block_sync();
     }
-    // raw registers are free: start loading the next chunk
-    if (j + 1 < nchunks) prefetch(j + 1);
-    block_sync();
 
     // ===== recurrence on this wave's 16 value columns
     f32x4 accOT[4];
@@ -513,15 +572,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) accY[s4][i] = to_f32(b4.v[i]);
       }
+      // O^T = S^T Q~^T first, sharing the S fragments with Y
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) accOT[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         Frag<OpT> sf;
         acc_frag_sk(sf, S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          Frag<OpT> xb;
+          Frag<OpT> xb, xq;
           lds_frag_ck(xb, nBKt, L::LD_D, 16 * s4 + l16, 32 * kk, g4);
+          lds_frag_ck(xq, Qt, L::LD_D, 16 * s4 + l16, 32 * kk, g4);
           mma(accY[s4], xb, sf);
+          mma(accOT[s4], sf, xq);
         }
       }
       // U = (I + A)^{-1} Y by block forward substitution:
@@ -545,20 +609,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       Frag<OpT> uf[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[kk], accU[2 * kk], accU[2 * kk + 1]);
-      // O^T = S^T Q~^T + U^T P^T      (lane holds O[r = 16 rt + l16][v = .. + 4 g4 + i])
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) accOT[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        Frag<OpT> sf;
-        acc_frag_sk(sf, S[2 * kk], S[2 * kk + 1]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          Frag<OpT> xq;
-          lds_frag_ck(xq, Qt, L::LD_D, 16 * rt + l16, 32 * kk, g4);
-          mma(accOT[rt], sf, xq);
-        }
-      }
+      // O^T += U^T P^T      (lane holds O[r = 16 rt + l16][v = .. + 4 g4 + i])
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
