@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains-per-core", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="repeat the oracle sample until this much wall time has passed")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, copy a state pool of this many MiB once (the plain "
+                         "copy kernel whose hardware byte counters scale the prefill's)")
     ap.add_argument("--workload", default=PREFILL_WORKLOAD)
     return ap.parse_args()
 
@@ -119,8 +124,11 @@ def time_decode(kda, ki, steps, warmup=10):
                 bytes_per_step=heads * DECODE_BYTES_PER_HEAD, batch=cfg.batch, heads=cfg.heads)
 
 
-def cpu_baseline(x, chains_per_core):
-    """Time the fp64 oracle on a bounded sample of the same workload's chains."""
+def cpu_baseline(x, chains_per_core, seconds):
+    """Time the fp64 oracle on a bounded sample of the same workload's chains.
+
+    The sample (cores x chains_per_core whole (sequence, head) chains) is run
+    repeatedly until `seconds` of wall time have passed; the rate is the mean."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
@@ -138,15 +146,61 @@ def cpu_baseline(x, chains_per_core):
     cat = lambda xs: np.concatenate(xs, axis=0)[:, None]
     args = (cat(qs), cat(ks), cat(vs), cat(gs), np.concatenate(bs)[:, None])
     oracle.load()
-    t0 = time.perf_counter()
-    oracle.recurrent(*args, cu_seqlens=cu2, nthreads=cores)
-    dt = time.perf_counter() - t0
-    token_heads = int(cu2[-1])
-    return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    threads = min(cores, oracle.max_threads(), nchains)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrent(*args, cu_seqlens=cu2, nthreads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    token_heads = int(cu2[-1]) * passes
+    return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{nchains} (sequence, head) chains of {lens[0]} tokens each "
-                      f"({token_heads} token-heads, fp64 token loop, OpenMP over chains); "
-                      f"value = token-heads/s divided by {H} heads",
+                      f"({int(cu2[-1])} token-heads, fp64 token loop, OpenMP over chains), "
+                      f"run {passes} times; value = token-heads/s divided by {H} heads",
             "token_heads_per_s": token_heads / dt, "seconds": dt}
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE readings,
+    or None when they were taken on other kernel sources or another workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_b4_t8192_h96_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"] or rec["workload"] != workload:
+        return None
+    return rec["traffic_bytes"]
+
+
+def copy_calibration(kda, mib):
+    """One fp32 state-pool copy of `mib` MiB read + `mib` MiB written: the plain
+    copy kernel whose FETCH_SIZE / WRITE_SIZE readings scale the prefill's."""
+    import torch
+    H = 96
+    slots = max(1, (mib << 20) // (H * D * D * 4))
+    src = torch.ones((slots, H, D, D), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    kda.state_io(kda.STATE_COPY, dst, src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    start.record(stream)
+    for _ in range(reps):
+        kda.state_io(kda.STATE_COPY, dst, src)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    nbytes = src.numel() * 4
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "kernel": "state_io_kernel",
+            "ms": ms, "gb_per_s": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
 def main():
@@ -188,7 +242,8 @@ def main():
         "tflops": tflops,
         "mfma_peak_frac": tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload),
                      "kernel": "chunk_fwd_kernel<bf16,128>",
                      "bytes_per_launch": alg_bytes},
     }
@@ -196,7 +251,9 @@ def main():
         line["decode"] = time_decode(kda, ki, args.decode_steps)
         line["decode"]["workload"] = DECODE_WORKLOAD
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core)
+        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds)
+    if args.copy_calibration_mib > 0:
+        line["copy_calibration"] = copy_calibration(kda, args.copy_calibration_mib)
     print(json.dumps(line), flush=True)
 
 
