@@ -53,10 +53,12 @@ def parse():
                     help="after timing, copy a state pool of this many MiB once (the plain "
                          "copy kernel whose hardware byte counters scale the prefill's)")
     ap.add_argument("--workload", default=PREFILL_WORKLOAD)
+    ap.add_argument("--segments", type=int, default=0,
+                    help="segments per sequence (0 = the library's automatic choice)")
     return ap.parse_args()
 
 
-def time_prefill(kda, ki, workload, steps, warmup):
+def time_prefill(kda, ki, workload, steps, warmup, segments=0):
     import torch
     cfg = ki.CONFIGS[workload]
     x = ki.make_prefill(cfg, device="cuda", seed=1002)
@@ -65,7 +67,8 @@ def time_prefill(kda, ki, workload, steps, warmup):
     o = torch.empty_like(x["q"])
     sf = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
     ws_bytes = kda.chunk_fwd_workspace_size(
-        x["q"], num_seqs=N, cu_seqlens_host=x["cu_seqlens_host"] if varlen else None)
+        x["q"], num_seqs=N, cu_seqlens_host=x["cu_seqlens_host"] if varlen else None,
+        segments=segments)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def step():
@@ -73,7 +76,7 @@ def time_prefill(kda, ki, workload, steps, warmup):
                       cu_seqlens=x["cu_seqlens"] if varlen else None,
                       cu_seqlens_host=x["cu_seqlens_host"] if varlen else None,
                       initial_state=x["initial_state"], num_seqs=N, out=o, final_state=sf,
-                      workspace=ws)
+                      workspace=ws, segments=segments)
 
     for _ in range(warmup):
         step()
@@ -216,7 +219,7 @@ def main():
     kda.library()
     torch.cuda.set_device(0)
 
-    pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup)
+    pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup, args.segments)
     H, tokens, N = pre["heads"], pre["tokens"], pre["seqs"]
     ms = pre["ms"]
     tok_s = tokens / (ms * 1e-3)
@@ -238,7 +241,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": N, "seq_len": tokens // N,
-                   "heads": H, "head_dim": D, "chunk": C, "state": "fp32"},
+                   "heads": H, "head_dim": D, "chunk": C, "state": "fp32",
+                   "segments": args.segments},
         "tflops": tflops,
         "mfma_peak_frac": tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,

@@ -56,6 +56,7 @@ constexpr int kD = KDA_HEAD_DIM;  // 128 channels
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRef = 8;           // reference token inside each 16-token sub-tile
+constexpr int kMaxSegments = 64;  // segments per sequence (segment parallelism)
 
 struct ChunkParams {
   const void *q, *k, *v;
@@ -69,7 +70,27 @@ struct ChunkParams {
   int32_t H;
   int32_t seq_len;
   float scale;
+  // segment parallelism: each sequence is split into seg_P segments of whole
+  // chunks; pass 0 = no split, 1 = first pass, 2 = second pass
+  int32_t seg_P;
+  int32_t pass;
+  float *ws;             // [N H][3 seg_P][128 x 128] fp32 segment states
 };
+
+// Work of one workgroup: a (sequence, head) chain, or one segment of it.
+enum SegMode { kRun = 0, kTrackM = 1, kTrackS = 2 };
+enum SegKind { kSin = 0, kM = 1, kSt = 2 };  // workspace state kinds
+
+// Segment p of a sequence of nch chunks (P_n segments) covers chunks
+// [p nch / P_n, (p + 1) nch / P_n).
+__device__ __forceinline__ int seg_count(int P, int nch) {
+  const int pn = P < nch ? P : nch;
+  return pn < 1 ? 1 : pn;
+}
+__device__ __forceinline__ float *seg_state(const ChunkParams &p, int64_t chain, int kind,
+                                            int seg) {
+  return p.ws + ((chain * 3 + kind) * p.seg_P + seg) * (int64_t)(kD * kD);
+}
 
 // Tile list of the 10 lower (row-tile i, column-tile j) pairs and their owner wave.
 __device__ __forceinline__ int tri_index(int i, int j) { return i * (i + 1) / 2 + j; }
@@ -206,12 +227,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   const int st = w >> 1;  // elementwise: 16-token sub-tile of this wave
   const int th = w & 1;   //              and its half (tokens 8 th .. 8 th + 7)
 
-  // ---- work item: (sequence rank, head, value block)
+  // ---- work item: (sequence rank, head, segment item, value block)
+  const int items = p.pass == 1 ? 2 * p.seg_P - 3 : (p.pass == 2 ? p.seg_P - 1 : 1);
   const int item = blockIdx.x;
   const int vs = item % VS;
-  const int chain = item / VS;
-  const int srank = chain / p.H;
-  const int h = chain - srank * p.H;
+  const int cit = item / VS;
+  const int it = cit % items;
+  const int crank = cit / items;
+  const int srank = crank / p.H;
+  const int h = crank - srank * p.H;
   const int n = p.order ? p.order[srank] : srank;
   int64_t bos = (int64_t)n * p.seq_len, len = p.seq_len;
   if (p.cu) {  // device offsets, clamped to the validated token range
@@ -220,6 +244,38 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     const int64_t e = b < bos ? bos : (b > p.total_tokens ? p.total_tokens : b);
     len = e - bos;
   }
+  const int64_t chain = (int64_t)n * p.H + h;
+  // segment, mode, incoming / outgoing state of this item
+  int seg = 0, mode = kRun;
+  if (p.pass == 1 && it > 0) {
+    seg = 1 + (it - 1) / 2;
+    mode = (it & 1) ? kTrackM : kTrackS;
+  } else if (p.pass == 2) {
+    seg = 1 + it;
+  }
+  const float *s0p = p.s0 ? p.s0 + chain * (kD * kD) : nullptr;
+  float *sfp = p.sfinal ? p.sfinal + chain * (kD * kD) : nullptr;
+  if (p.pass != 0) {
+    const int nch_all = (int)((len + kC - 1) / kC);
+    const int pn = seg_count(p.seg_P, nch_all);
+    // trackers exist for the segments 1 .. P_n - 2, runs for 0 .. P_n - 1
+    if (mode == kRun ? seg >= pn : seg >= pn - 1) return;  // uniform: whole workgroup
+    const int c_lo = (int)((int64_t)seg * nch_all / pn);
+    const int c_hi = (int)((int64_t)(seg + 1) * nch_all / pn);
+    const int64_t t_lo = (int64_t)c_lo * kC;
+    const int64_t t_hi = (int64_t)c_hi * kC < len ? (int64_t)c_hi * kC : len;
+    bos += t_lo;
+    len = t_hi - t_lo;
+    if (mode == kRun) {
+      if (seg > 0) s0p = seg_state(p, chain, kSin, seg);
+      sfp = seg == pn - 1 ? sfp : (p.pass == 1 ? seg_state(p, chain, kSin, 1) : nullptr);
+    } else {
+      s0p = nullptr;
+      sfp = seg_state(p, chain, mode == kTrackM ? kM : kSt, seg);
+    }
+  }
+  const bool write_o = mode == kRun;
+  const bool zero_v = mode == kTrackM;  // M = the map of the incoming state: v = 0, S0 = I
   const int nchunks = (int)((len + kC - 1) / kC);
   const int H = p.H;
   const int64_t rowstride = (int64_t)H * kD;  // elements between consecutive tokens
@@ -244,12 +300,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   //      S[ct] holds S[16 ct + 4 g4 + i][vblk + vloc + l16]
   f32x4 S[8];
   {
-    const float *s0 = (p.s0 && rec_wave) ? p.s0 + ((int64_t)n * H + h) * (kD * kD) : nullptr;
+    const float *s0 = rec_wave ? s0p : nullptr;
+    const int col = vblk + vloc + l16;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * kD + vblk + vloc + l16] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ct + 4 * g4 + i;
+        S[ct][i] = s0 ? s0[row * kD + col] : (zero_v && row == col ? 1.f : 0.f);
+      }
   }
 
   // ---- register prefetch of a chunk's raw inputs: wave w = tokens
@@ -259,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   f32x2 rg[8];
   float rb = 0.f;
   const int c0 = 2 * lane;
-  const bool has_v = (DV == 128) || (lane < 32);
+  const bool has_v = (DV == 128) || (lane < 32);  // this lane's value columns exist
   const uint32_t lane_off_qk = (uint32_t)c0 * (uint32_t)sizeof(OpT);  // byte offsets
   const uint32_t lane_off_g = (uint32_t)c0 * 4u;
   const uint32_t row_qk = (uint32_t)rowstride * (uint32_t)sizeof(OpT);  // bytes per token
@@ -274,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     // descriptors cover exactly this wave's valid rows of its head
     rq_s = make_rsrc(qg + t0 * rowstride, nv * row_qk);
     rk_s = make_rsrc(kg + t0 * rowstride, nv * row_qk);
-    rv_s = make_rsrc(vg + t0 * rowstride, has_v ? nv * row_qk : 0u);
+    rv_s = make_rsrc(vg + t0 * rowstride, (has_v && !zero_v) ? nv * row_qk : 0u);
     rg_s = make_rsrc(gg + t0 * rowstride, nv * row_g);
     rb = (lane < 8 && (uint32_t)lane < nv) ? p.beta[(t0 + lane) * H + h] : 0.f;
   };
@@ -285,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       const uint32_t so_g = __builtin_amdgcn_readfirstlane(t * row_g);
       raw_load(rq[t], rq_s, lane_off_qk, so_qk);
       raw_load(rk[t], rk_s, lane_off_qk, so_qk);
-      raw_load(rv[t], rv_s, lane_off_qk, so_qk);  // zero where has_v is false
+      raw_load(rv[t], rv_s, lane_off_qk, so_qk);  // reads as zero outside the descriptor
       rg[t] = buf_load_f32x2(rg_s, lane_off_g, so_g);
     } else {
       raw_zero(rq[t]); raw_zero(rk[t]); raw_zero(rv[t]);
@@ -636,6 +695,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     block_sync();
 
     // ===== output: stage O (scaled, io dtype) in LDS, then row-contiguous stores
+    if (!write_o) continue;  // uniform; the next chunk's first barrier still orders LDS
     if (rec_wave) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -657,8 +717,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     // (the next chunk's first barrier orders these LDS reads before its writes)
   }
 
-  if (p.sfinal && rec_wave) {
-    float *sf = p.sfinal + ((int64_t)n * H + h) * (kD * kD);
+  if (sfp && rec_wave) {
+    float *sf = sfp;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -704,6 +764,66 @@ __global__ __launch_bounds__(1024) void order_longest_first_kernel(const int32_t
   for (int i = threadIdx.x; i < N; i += blockDim.x) order[i] = (int32_t)(key[i] & 0xffffffffu);
 }
 
+// Composition of segment transitions ([P3] section 4.1): for each chain, in
+// order, S_in[s + 1] = M_s S_in[s] + S~_s for s = 1 .. P_n - 2 (S_in[1] is the
+// final state of segment 0's run).  One workgroup of 256 threads per chain; each
+// thread owns an 8 x 8 block of the 128 x 128 product, fp32 throughout.
+__global__ __launch_bounds__(256) void segment_combine_kernel(ChunkParams p) {
+  constexpr int kK = 16;  // reduction slice staged in LDS
+  __shared__ __attribute__((aligned(16))) float Ms[kK][kD];  // M[:, k0 + kk] by row
+  __shared__ __attribute__((aligned(16))) float Bs[kK][kD];  // S_in[k0 + kk, :]
+  const int64_t chain = blockIdx.x;
+  const int n = (int)(chain / p.H);
+  int64_t len = p.seq_len;
+  if (p.cu) {
+    const int64_t a = p.cu[n], b = p.cu[n + 1];
+    const int64_t lo = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+    const int64_t hi = b < lo ? lo : (b > p.total_tokens ? p.total_tokens : b);
+    len = hi - lo;
+  }
+  const int pn = seg_count(p.seg_P, (int)((len + kC - 1) / kC));
+  const int t = threadIdx.x;
+  const int r0 = (t >> 4) * 8, c0 = (t & 15) * 8;
+  for (int sg = 1; sg + 2 <= pn; ++sg) {
+    const float *M = seg_state(p, chain, kM, sg);
+    const float *B = seg_state(p, chain, kSin, sg);
+    const float *St = seg_state(p, chain, kSt, sg);
+    float *out = seg_state(p, chain, kSin, sg + 1);
+    float acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = St[(r0 + i) * kD + c0 + j];
+    for (int k0 = 0; k0 < kD; k0 += kK) {
+      __syncthreads();
+      for (int e = t; e < kK * kD; e += 256) {
+        const int kk = e & (kK - 1), r = e / kK;  // M row r, column k0 + kk
+        Ms[kk][r] = M[r * kD + k0 + kk];
+        const int br = e / kD, bc = e & (kD - 1);
+        Bs[br][bc] = B[(k0 + br) * kD + bc];
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int kk = 0; kk < kK; ++kk) {
+        float a[8], b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = Ms[kk][r0 + i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = Bs[kk][c0 + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[(r0 + i) * kD + c0 + j] = acc[i][j];
+    __syncthreads();  // S_in[sg + 1] complete before the next step reads it
+  }
+}
+
 template <class OpT, int DV>
 hipError_t launch_typed(const ChunkParams &p, int64_t items, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_fwd_kernel<OpT, DV>), dim3((unsigned)items), dim3(kThreads), 0,
@@ -730,12 +850,23 @@ kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
     maxlen = a.seq_len;
   }
   pl.max_chunks = (maxlen + KDA_CHUNK - 1) / KDA_CHUNK;
-  pl.segments = 1;
+  // segments per sequence: explicit, or 1 in automatic mode (splitting a chain
+  // repeats its chunk-local work in two passes, which the measured runs never
+  // recovered from the extra CUs)
+  int64_t P = a.segments > 1 ? a.segments : 1;
+  if (P > kMaxSegments) P = kMaxSegments;
+  if (P > pl.max_chunks) P = pl.max_chunks < 1 ? 1 : pl.max_chunks;
+  pl.segments = (int32_t)P;
   size_t off = 0;
   if (pl.varlen && a.num_seqs > 1 && a.num_seqs <= 4096) {
     pl.order_off = off;
     pl.order_bytes = (size_t)a.num_seqs * sizeof(int32_t);
     off += (pl.order_bytes + 255) & ~(size_t)255;
+  }
+  if (pl.segments > 1) {
+    pl.seg_state_off = off;
+    pl.seg_state_bytes = (size_t)a.num_seqs * a.num_heads * 3 * pl.segments * kD * kD * 4;
+    off += pl.seg_state_bytes;
   }
   pl.total_bytes = off;
   *plan = pl;
@@ -768,8 +899,31 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
     p.order = order;
   }
   const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
-  if (a.io_dtype == KDA_BF16) return launch_typed<bf16, 128>(p, chains, stream);
-  return launch_typed<float, 64>(p, chains * 2, stream);
+  const int VS = a.io_dtype == KDA_BF16 ? 1 : 2;  // value blocks per chain
+  auto run = [&](int64_t items) {
+    return a.io_dtype == KDA_BF16 ? launch_typed<bf16, 128>(p, items, stream)
+                                  : launch_typed<float, 64>(p, items, stream);
+  };
+  p.seg_P = plan.segments;
+  p.ws = nullptr;
+  if (plan.segments <= 1) {
+    p.pass = 0;
+    return run(chains * VS);
+  }
+  // segmented: first pass (segment 0 runs; transitions of segments 1 .. P-2),
+  // composition, second pass (segments 1 .. P-1 from their exact incoming states)
+  p.ws = reinterpret_cast<float *>((char *)a.workspace + plan.seg_state_off);
+  const int P = plan.segments;
+  p.pass = 1;
+  hipError_t e = run(chains * (2 * P - 3) * VS);
+  if (e != hipSuccess) return e;
+  if (P > 2) {
+    hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)chains), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  p.pass = 2;
+  return run(chains * (P - 1) * VS);
 }
 
 }  // namespace kda

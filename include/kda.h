@@ -93,10 +93,13 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * rounded to nearest-even).
  *
  * Intra-device segment parallelism ([P3] section 4.1): with `segments` > 1
- * (or 0 = chosen automatically) long sequences are split into segments whose
- * transitions are evaluated from a zero incoming state in parallel, composed in
- * order, and then re-run from their exact incoming states.  The result is the
- * same recurrence.
+ * every sequence is split into that many segments of whole chunks (at most one
+ * per chunk, at most 64).  The transition of each inner segment (the map M of
+ * its incoming state and the state S~ it produces from zero) is evaluated in
+ * parallel, the transitions are composed in order, and every segment is then
+ * run from its exact incoming state.  The result is the same recurrence up to
+ * rounding.  The workspace holds 3 x segments fp32 states per (sequence,
+ * head).  segments = 0 lets the library choose (currently: no split).
  * ---------------------------------------------------------------------- */
 typedef struct kda_chunk_fwd_args {
   int32_t num_seqs;               /* N >= 1                                              */

@@ -145,6 +145,36 @@ def test_decode_steps_equal_prefill(kda):
     assert rel_err(to64(state), to64(sf)) <= TOL[torch.bfloat16]
 
 
+# ------------------------------------------------- intra-device segment parallelism
+@pytest.mark.parametrize("dtype,segments", [("bf16", 2), ("bf16", 3), ("bf16", 5), ("f32", 3)])
+def test_segments_match_oracle(kda, dtype, segments):
+    """Sequences split into segments whose transitions are evaluated from a zero
+    state, composed in order and re-run ("Kimi K3 -- Training and Infrastructure
+    Notes", section 4.1) give the token loop's result.  The lengths include
+    sequences shorter than the segment count (fewer, or a single segment), an
+    empty one, and ragged ends."""
+    announce(f"chunk segments={segments} dtype={dtype}")
+    lens = (1, 63, 64, 65, 130, 0, 300, 17, 1000, 333)
+    cfg = ki.PrefillConfig("t", lens, 3, dtype, init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=31)
+    o, sf = run(kda, inp, scale=0.9, segments=segments)
+    torch.cuda.synchronize()
+    chains = [(n, h) for n in range(len(lens)) for h in range(3)]
+    check_chains(inp, o, sf, chains, inp["dtype"], scale=0.9)
+
+
+def test_segments_fixed_batch_without_initial_state(kda):
+    announce("chunk segments fixed batch")
+    cfg = ki.PrefillConfig("t", (777, 777), 4, "bf16")
+    inp = ki.make_prefill(cfg, device="cuda", seed=33)
+    o1, s1 = run(kda, inp, varlen=False, segments=4)
+    o0, s0 = run(kda, inp, varlen=False, segments=1)
+    torch.cuda.synchronize()
+    check_chains(inp, o1, s1, [(0, 0), (1, 3)], torch.bfloat16)
+    assert rel_err(to64(o1), to64(o0)) <= TOL[torch.bfloat16]
+    assert rel_err(to64(s1), to64(s0)) <= TOL[torch.bfloat16]
+
+
 # ----------------------------------------------------------- full-size workloads
 def test_full_b4_t8192_h96_sampled(kda):
     """B=4, T=8192, H=96, bf16, zero initial state -- the benchmark workload, in the
@@ -166,6 +196,18 @@ def test_full_t65536_h96_initial_state_sampled(kda):
     o, sf = run(kda, inp, varlen=False)
     torch.cuda.synchronize()
     check_chains(inp, o, sf, [(0, 0), (0, 47), (0, 95)], torch.bfloat16)
+
+
+@pytest.mark.parametrize("segments", [0, 8])
+def test_full_t65536_h96_segmented_sampled(kda, segments):
+    """The 65,536-token workload with its chains split into segments (0 = the
+    library's automatic choice), against the oracle on sampled heads."""
+    announce(f"chunk full t65536 h96 s0 segments={segments}")
+    cfg = ki.CONFIGS["kda_prefill_t65536_h96_bf16_s0_gclamp5"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1003)
+    o, sf = run(kda, inp, varlen=False, segments=segments)
+    torch.cuda.synchronize()
+    check_chains(inp, o, sf, [(0, 5), (0, 64)], torch.bfloat16)
 
 
 def test_full_varlen32_t1m_h96_sampled(kda):
