@@ -45,67 +45,18 @@
 //    workgroup so the operand buffers fit in the 160 KiB of LDS.
 #include <type_traits>
 
-#include "kda_device.h"
+#include "kda_chunk_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kC = KDA_CHUNK;     // 64 tokens per chunk
-constexpr int kD = KDA_HEAD_DIM;  // 128 channels
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRef = 8;           // reference token inside each 16-token sub-tile
-constexpr int kMaxSegments = 64;  // segments per sequence (segment parallelism)
-
-struct ChunkParams {
-  const void *q, *k, *v;
-  const float *g, *beta;
-  const float *s0;
-  float *sfinal;
-  void *o;
-  const int32_t *cu;     // device cu_seqlens or null
-  const int32_t *order;  // device sequence order (longest first) or null
-  int64_t total_tokens;  // T_total from the host-validated sizes
-  int32_t H;
-  int32_t seq_len;
-  float scale;
-  // segment parallelism: each sequence is split into seg_P segments of whole
-  // chunks; pass 0 = no split, 1 = first pass, 2 = second pass
-  int32_t seg_P;
-  int32_t pass;
-  float *ws;             // [N H][3 seg_P][128 x 128] fp32 segment states
-};
-
-// Work of one workgroup: a (sequence, head) chain, or one segment of it.
-enum SegMode { kRun = 0, kTrackM = 1, kTrackS = 2 };
-enum SegKind { kSin = 0, kM = 1, kSt = 2 };  // workspace state kinds
-
-// Segment p of a sequence of nch chunks (P_n segments) covers chunks
-// [p nch / P_n, (p + 1) nch / P_n).
-__device__ __forceinline__ int seg_count(int P, int nch) {
-  const int pn = P < nch ? P : nch;
-  return pn < 1 ? 1 : pn;
-}
-__device__ __forceinline__ float *seg_state(const ChunkParams &p, int64_t chain, int kind,
-                                            int seg) {
-  return p.ws + ((chain * 3 + kind) * p.seg_P + seg) * (int64_t)(kD * kD);
-}
 
 // Tile list of the 10 lower (row-tile i, column-tile j) pairs and their owner wave.
 __device__ __forceinline__ int tri_index(int i, int j) { return i * (i + 1) / 2 + j; }
-
-// Column order of the matrices read as split-k fragments (k = 4g+i and
-// 16+4g+i of each 32-column block): stored so that those eight k-values are
-// adjacent, each fragment is one 16-byte LDS read.  Groups of four aligned
-// columns stay contiguous.
-__device__ __forceinline__ int skpos(int c) {
-  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
-}
-// Column held at position p (inverse of skpos).
-__device__ __forceinline__ int skcol(int p) {
-  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
-}
 
 template <class OpT, int DV>
 struct Layout {
@@ -228,54 +179,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   const int th = w & 1;   //              and its half (tokens 8 th .. 8 th + 7)
 
   // ---- work item: (sequence rank, head, segment item, value block)
-  const int items = p.pass == 1 ? 2 * p.seg_P - 3 : (p.pass == 2 ? p.seg_P - 1 : 1);
-  const int item = blockIdx.x;
-  const int vs = item % VS;
-  const int cit = item / VS;
-  const int it = cit % items;
-  const int crank = cit / items;
-  const int srank = crank / p.H;
-  const int h = crank - srank * p.H;
-  const int n = p.order ? p.order[srank] : srank;
-  int64_t bos = (int64_t)n * p.seq_len, len = p.seq_len;
-  if (p.cu) {  // device offsets, clamped to the validated token range
-    const int64_t a = p.cu[n], b = p.cu[n + 1];
-    bos = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
-    const int64_t e = b < bos ? bos : (b > p.total_tokens ? p.total_tokens : b);
-    len = e - bos;
-  }
-  const int64_t chain = (int64_t)n * p.H + h;
-  // segment, mode, incoming / outgoing state of this item
-  int seg = 0, mode = kRun;
-  if (p.pass == 1 && it > 0) {
-    seg = 1 + (it - 1) / 2;
-    mode = (it & 1) ? kTrackM : kTrackS;
-  } else if (p.pass == 2) {
-    seg = 1 + it;
-  }
-  const float *s0p = p.s0 ? p.s0 + chain * (kD * kD) : nullptr;
-  float *sfp = p.sfinal ? p.sfinal + chain * (kD * kD) : nullptr;
-  if (p.pass != 0) {
-    const int nch_all = (int)((len + kC - 1) / kC);
-    const int pn = seg_count(p.seg_P, nch_all);
-    // trackers exist for the segments 1 .. P_n - 2, runs for 0 .. P_n - 1
-    if (mode == kRun ? seg >= pn : seg >= pn - 1) return;  // uniform: whole workgroup
-    const int c_lo = (int)((int64_t)seg * nch_all / pn);
-    const int c_hi = (int)((int64_t)(seg + 1) * nch_all / pn);
-    const int64_t t_lo = (int64_t)c_lo * kC;
-    const int64_t t_hi = (int64_t)c_hi * kC < len ? (int64_t)c_hi * kC : len;
-    bos += t_lo;
-    len = t_hi - t_lo;
-    if (mode == kRun) {
-      if (seg > 0) s0p = seg_state(p, chain, kSin, seg);
-      sfp = seg == pn - 1 ? sfp : (p.pass == 1 ? seg_state(p, chain, kSin, 1) : nullptr);
-    } else {
-      s0p = nullptr;
-      sfp = seg_state(p, chain, mode == kTrackM ? kM : kSt, seg);
-    }
-  }
-  const bool write_o = mode == kRun;
-  const bool zero_v = mode == kTrackM;  // M = the map of the incoming state: v = 0, S0 = I
+  const ChunkItem itm = decode_item(p, VS);
+  if (itm.skip) return;  // uniform: the whole workgroup
+  const int vs = itm.vs, h = itm.h;
+  const int64_t bos = itm.bos, len = itm.len;
+  const float *s0p = itm.s0;
+  float *sfp = itm.sf;
+  const bool write_o = itm.write_o;
+  const bool zero_v = itm.zero_v;  // M = the map of the incoming state: v = 0, S0 = I
   const int nchunks = (int)((len + kC - 1) / kC);
   const int H = p.H;
   const int64_t rowstride = (int64_t)H * kD;  // elements between consecutive tokens
@@ -901,7 +812,7 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
   const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
   const int VS = a.io_dtype == KDA_BF16 ? 1 : 2;  // value blocks per chain
   auto run = [&](int64_t items) {
-    return a.io_dtype == KDA_BF16 ? launch_typed<bf16, 128>(p, items, stream)
+    return a.io_dtype == KDA_BF16 ? launch_chunk_fwd_pipe(p, items, stream)
                                   : launch_typed<float, 64>(p, items, stream);
   };
   p.seg_P = plan.segments;

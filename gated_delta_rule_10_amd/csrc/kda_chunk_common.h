@@ -1,0 +1,133 @@
+// kda_chunk_common.h -- what the prefill kernels share: launch parameters, the
+// mapping of a workgroup to its (sequence, head[, segment]) work item, and the
+// column permutation of the split-k operand layout.
+#pragma once
+
+#include "kda.h"
+#include "kda_device.h"
+
+namespace kda {
+
+constexpr int kC = KDA_CHUNK;     // 64 tokens per chunk
+constexpr int kD = KDA_HEAD_DIM;  // 128 channels
+constexpr int kMaxSegments = 64;  // segments per sequence (segment parallelism)
+
+struct ChunkParams {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const float *s0;
+  float *sfinal;
+  void *o;
+  const int32_t *cu;     // device cu_seqlens or null
+  const int32_t *order;  // device sequence order (longest first) or null
+  int64_t total_tokens;  // T_total from the host-validated sizes
+  int32_t H;
+  int32_t seq_len;
+  float scale;
+  // segment parallelism: each sequence is split into seg_P segments of whole
+  // chunks; pass 0 = no split, 1 = first pass, 2 = second pass
+  int32_t seg_P;
+  int32_t pass;
+  float *ws;             // [N H][3 seg_P][128 x 128] fp32 segment states
+};
+
+// Segment items ("Kimi K3 -- Training and Infrastructure Notes", section 4.1):
+// a run evaluates a segment from its incoming state; the two trackers of a
+// segment give its transition, M (from S0 = I with v = 0) and S~ (from S0 = 0).
+enum SegMode { kRun = 0, kTrackM = 1, kTrackS = 2 };
+enum SegKind { kSin = 0, kM = 1, kSt = 2 };  // workspace state kinds
+
+// Segment p of a sequence of nch chunks (P_n segments) covers chunks
+// [p nch / P_n, (p + 1) nch / P_n).
+__device__ __forceinline__ int seg_count(int P, int nch) {
+  const int pn = P < nch ? P : nch;
+  return pn < 1 ? 1 : pn;
+}
+__device__ __forceinline__ float *seg_state(const ChunkParams &p, int64_t chain, int kind,
+                                            int seg) {
+  return p.ws + ((chain * 3 + kind) * p.seg_P + seg) * (int64_t)(kD * kD);
+}
+
+// Work item of one workgroup: the token range [bos, bos + len) of head h, the
+// incoming state (null = zero, or the identity when zero_v), where the final
+// state goes (null = nowhere), whether o is written, and the value block.
+struct ChunkItem {
+  int64_t bos, len, chain;
+  int h, vs;
+  const float *s0;
+  float *sf;
+  bool write_o, zero_v, skip;
+};
+
+// blockIdx.x = ((sequence rank * H + head) * items + segment item) * VS + value block.
+__device__ __forceinline__ ChunkItem decode_item(const ChunkParams &p, int VS) {
+  ChunkItem r;
+  const int items = p.pass == 1 ? 2 * p.seg_P - 3 : (p.pass == 2 ? p.seg_P - 1 : 1);
+  const int item = blockIdx.x;
+  r.vs = item % VS;
+  const int cit = item / VS;
+  const int it = cit % items;
+  const int crank = cit / items;
+  const int srank = crank / p.H;
+  r.h = crank - srank * p.H;
+  const int n = p.order ? p.order[srank] : srank;
+  int64_t bos = (int64_t)n * p.seq_len, len = p.seq_len;
+  if (p.cu) {  // device offsets, clamped to the validated token range
+    const int64_t a = p.cu[n], b = p.cu[n + 1];
+    bos = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+    const int64_t e = b < bos ? bos : (b > p.total_tokens ? p.total_tokens : b);
+    len = e - bos;
+  }
+  r.chain = (int64_t)n * p.H + r.h;
+  int seg = 0, mode = kRun;
+  if (p.pass == 1 && it > 0) {
+    seg = 1 + (it - 1) / 2;
+    mode = (it & 1) ? kTrackM : kTrackS;
+  } else if (p.pass == 2) {
+    seg = 1 + it;
+  }
+  r.s0 = p.s0 ? p.s0 + r.chain * (kD * kD) : nullptr;
+  r.sf = p.sfinal ? p.sfinal + r.chain * (kD * kD) : nullptr;
+  r.skip = false;
+  if (p.pass != 0) {
+    const int nch_all = (int)((len + kC - 1) / kC);
+    const int pn = seg_count(p.seg_P, nch_all);
+    // trackers exist for the segments 1 .. P_n - 2, runs for 0 .. P_n - 1
+    r.skip = mode == kRun ? seg >= pn : seg >= pn - 1;
+    const int c_lo = (int)((int64_t)seg * nch_all / pn);
+    const int c_hi = (int)((int64_t)(seg + 1) * nch_all / pn);
+    const int64_t t_lo = (int64_t)c_lo * kC;
+    const int64_t t_hi = (int64_t)c_hi * kC < len ? (int64_t)c_hi * kC : len;
+    bos += t_lo;
+    len = t_hi > t_lo ? t_hi - t_lo : 0;
+    if (mode == kRun) {
+      if (seg > 0) r.s0 = seg_state(p, r.chain, kSin, seg);
+      r.sf = seg == pn - 1 ? r.sf : (p.pass == 1 ? seg_state(p, r.chain, kSin, 1) : nullptr);
+    } else {
+      r.s0 = nullptr;
+      r.sf = seg_state(p, r.chain, mode == kTrackM ? kM : kSt, seg);
+    }
+  }
+  r.bos = bos;
+  r.len = len;
+  r.write_o = mode == kRun;
+  r.zero_v = mode == kTrackM;
+  return r;
+}
+
+// Column order of the matrices read as split-k fragments (k = 4g+i and
+// 16+4g+i of each 32-column block): stored so that those eight k-values are
+// adjacent, each fragment is one 16-byte LDS read.  Groups of four aligned
+// columns stay contiguous.
+__device__ __forceinline__ int skpos(int c) {
+  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+// Column held at position p (inverse of skpos).
+__device__ __forceinline__ int skcol(int p) {
+  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
+
+// Host launchers of the two prefill kernels.
+hipError_t launch_chunk_fwd_pipe(const ChunkParams &p, int64_t items, hipStream_t stream);
+
+}  // namespace kda
