@@ -48,7 +48,7 @@ namespace {
 
 constexpr int kLDK = 136;            // operand row stride: 128 bf16 + 16 bytes
 constexpr int kLDC = 72;             // 64-wide matrices (Lm, Pm): 64 bf16 + 16 bytes
-constexpr float kMaxRange = 128.f;   // largest log2 range of G over a 64-token window
+constexpr float kMaxHalf = 64.f;     // largest log2-decay over each 32-token half of a window
 
 struct Buf {                   // one window's operands
   bf16 nkr[64 * kLDK];         // -beta k 2^{G - Gm}      rows = tokens, columns skpos
@@ -64,7 +64,8 @@ struct Buf {                   // one window's operands
 struct Smem {
   Buf buf[2];
   bf16 v[64 * kLDK];           // v of the current chunk (rows = tokens, natural columns)
-  int flag[4];                 // per producer wave: the next chunk fits one reference
+  float qtot[4][128];          // next chunk: sum of log2-decay over each 16-token quarter
+  int flag[4];                 // next chunk: no positive log-decay in quarter pw
 };
 static_assert(sizeof(Buf) % 16 == 0, "buffer alignment");
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget exceeded");
@@ -86,71 +87,52 @@ __device__ __forceinline__ float bperm(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
 }
 
-// Gram jobs of producer wave P: (kind, row tile i, column tile j).
-// kind 0: -beta A tile (i > j) -> Lm;  1: P tile -> Pm;  2, 3: the diagonal tile
-// (i, i) of -beta A as [r][s] and as [s][r] (for the inverse).  Each wave owns
-// one diagonal block; the off-diagonal tiles are spread so a wave's tiles share
-// operands.
-struct Job { int kind, i, j; };
-__device__ constexpr Job kJobs[4][6] = {
-    {{2, 0, 0}, {3, 0, 0}, {1, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}},
-    {{2, 3, 3}, {3, 3, 3}, {1, 3, 3}, {1, 2, 0}, {0, 3, 0}, {1, 3, 0}},
-    {{2, 1, 1}, {3, 1, 1}, {1, 1, 1}, {0, 2, 1}, {1, 2, 1}, {0, 3, 1}},
-    {{2, 2, 2}, {3, 2, 2}, {1, 2, 2}, {1, 3, 1}, {0, 3, 2}, {1, 3, 2}}};
+// Lower 16x16 tiles (i, j), i >= j, of -beta A = nKr Kc^T computed by producer
+// wave P: the tiles of a wave share their Kc column block.
+__device__ constexpr int kTileI[4][3] = {{0, 1, 2}, {1, 2, 3}, {2, 3, -1}, {3, 3, -1}};
+__device__ constexpr int kTileJ[4][3] = {{0, 0, 0}, {1, 1, 1}, {2, 2, -1}, {3, 0, -1}};
 
-// Gram products of one window and the inverse of this wave's diagonal block;
-// writes Lm and Pm.
+// Gram products -beta A of one window into Lm (bf16, row-major).  The diagonal
+// tiles are stored whole; the consumer that inverts a diagonal block reads only
+// its strictly lower part.
 template <int P>
-__device__ __forceinline__ void gram_and_inverse(Buf &B, int l16, int g4) {
-  f32x4 acc[6];
+__device__ __forceinline__ void gram_a(Buf &B, int l16, int g4) {
+  constexpr int nt = kTileI[P][2] < 0 ? 2 : 3;
+  f32x4 acc[3];
 #pragma unroll
-  for (int u = 0; u < 6; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < nt; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const Job jb = kJobs[P][u];
+    for (int u = 0; u < nt; ++u) {
+      // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
       Frag<bf16> fx, fy;
-      if (jb.kind == 2) {         // [r][s]: rows of nKr_i against Kc_i
-        lds_frag_ck(fx, B.nkr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-        lds_frag_ck(fy, B.kc, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-      } else if (jb.kind == 3) {  // [s][r]
-        lds_frag_ck(fx, B.kc, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-        lds_frag_ck(fy, B.nkr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-      } else {                    // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
-        lds_frag_ck(fx, B.kc, kLDK, 16 * jb.j + l16, 32 * kk, g4);
-        lds_frag_ck(fy, jb.kind == 0 ? B.nkr : B.qr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-      }
+      lds_frag_ck(fx, B.kc, kLDK, 16 * kTileJ[P][u] + l16, 32 * kk, g4);
+      lds_frag_ck(fy, B.nkr, kLDK, 16 * kTileI[P][u] + l16, 32 * kk, g4);
       mma(acc[u], fx, fy);
     }
   }
-  // off-diagonal -beta A and P tiles
 #pragma unroll
-  for (int u = 2; u < 6; ++u) {
-    const Job jb = kJobs[P][u];
-    const int r = 16 * jb.i + l16;
-    if (jb.kind == 0) {
-      store4<bf16>(B.lm + r * kLDC + 16 * jb.j + 4 * g4, acc[u]);
-    } else {
-      f32x4 pv = acc[u];
-      if (jb.i == jb.j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e) <= l16 ? pv[e] : 0.f;
-      }
-      store4<bf16>(B.pm + r * kLDC + skpos(16 * jb.j + 4 * g4), pv);
-    }
-  }
-  // inverse of the diagonal block (I + N), N = beta A_ii strictly lower, in the
-  // result layout (lane holds M[4 g4 + e][l16]):
-  //   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0.
-  // rr_tn(B, C) = B^T C, so each power is paired with its transpose.
-  constexpr int d = kJobs[P][0].i;
+  for (int u = 0; u < nt; ++u)
+    store4<bf16>(B.lm + (16 * kTileI[P][u] + l16) * kLDC + 16 * kTileJ[P][u] + 4 * g4, acc[u]);
+}
+
+// In place on diagonal block d of Lm: -beta A_dd (strictly lower part) becomes
+// X_dd = (I + N)^{-1}, N = beta A_dd.  Result layout (lane holds M[4 g4 + e][l16]):
+//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0.
+// rr_tn(B, C) = B^T C on fp32 matrix cores, so each power is paired with its
+// transpose.
+__device__ __forceinline__ void invert_diag(Buf &B, int d, int l16, int g4) {
+  bf16 *blk = B.lm + 16 * d * kLDC + 16 * d;
+  // T[4 g4 + e][l16] by a transposing load; T^T[4 g4 + e][l16] = T[l16][4 g4 + e] directly
+  const bf16x4 t = lds_read_tr(blk + (4 * g4 + (l16 >> 2)) * kLDC + 4 * (l16 & 3));
+  const bf16x4 tt = *reinterpret_cast<const bf16x4 *>(blk + l16 * kLDC + 4 * g4);
   f32x4 N, NT;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int a = 4 * g4 + e;
-    N[e] = l16 < a ? -acc[0][e] : 0.f;
-    NT[e] = a < l16 ? -acc[1][e] : 0.f;
+    N[e] = l16 < a ? -(float)t[e] : 0.f;
+    NT[e] = a < l16 ? -(float)tt[e] : 0.f;
   }
   const f32x4 N2 = rr_tn(NT, N), T2 = rr_tn(N, NT);
   const f32x4 N3 = rr_tn(NT, N2), T3 = rr_tn(N, T2);
@@ -166,15 +148,24 @@ __device__ __forceinline__ void gram_and_inverse(Buf &B, int l16, int g4) {
   const f32x4 P2 = P1 + rr_tn(P1T, N4);
   const f32x4 P2T = P1T + rr_tn(N4, P1T);
   const f32x4 Xd = P2 + rr_tn(P2T, N8);
+  // every lane has read its operands before any writes (one wave, in order)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) B.lm[(16 * d + 4 * g4 + e) * kLDC + 16 * d + l16] = (bf16)Xd[e];
+  for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * kLDC + l16] = (bf16)Xd[e];
 }
 
 // ---------------------------------------------------------------- producers
-// Lane = (token quarter tq, channel pair cp) of producer wave pw: channels
-// 32 pw + 2 cp and + 1, tokens 16 tq .. 16 tq + 15 of the chunk.  A chunk's q,
-// k, v, g and beta are loaded into registers one chunk ahead (g two ahead, so
-// that whether a chunk fits one reference is known before its window starts).
+// Producer wave pw handles tokens 16 pw .. 16 pw + 15 (quarter pw) of a chunk,
+// all 128 channels: lane = (ts, co) holds tokens 16 pw + 4 ts + j (j < 4) and
+// channels 8 co .. 8 co + 7, so every load instruction reads four whole
+// 256-byte token rows.  A chunk's q, k, v, beta are loaded one chunk ahead, its
+// g two ahead: its cumulative decay and whether one reference fits it are known
+// before its first window starts.
+//
+// One reference per 64-token window is used when, on every channel, the
+// decay over tokens 0..31 and over 32..63 each stay within 2^64 and no
+// log-decay is positive; then Gm = G_31 and every factor is within 2^{+-64}.
+// Otherwise the chunk runs as four 16-token windows, window w with the
+// reference at its token 8.
 __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkItem &itm,
                                               Smem &sm, const int pw, const int lane,
                                               const int nblk) {
@@ -184,18 +175,18 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   const int64_t rowstride = (int64_t)H * kD;          // elements between tokens
   const uint32_t row_b16 = (uint32_t)rowstride * 2u;  // bytes between bf16 rows
   const uint32_t row_f32 = (uint32_t)rowstride * 4u;  // bytes between fp32 rows
-  const int tq = lane >> 4, cp = lane & 15;
+  const uint32_t row_beta = (uint32_t)H * 4u;         // bytes between beta rows
+  const int ts = lane >> 4, co = lane & 15;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int c0 = 32 * pw + 2 * cp;
-  const int pc0 = skpos(c0);  // stored column of c0 (c0 + 1 follows it)
+  const int r0 = 16 * pw + 4 * ts;                    // this lane's first row in the chunk
+  const int pA = skpos(8 * co), pB = skpos(8 * co + 4);  // stored columns of the two channel quads
 
-  uint32_t Rq[16], Rk[16], Rv[16];  // bf16 channel pairs
-  f32x2 Rg[16];
-  float G0[16], G1[16];             // chunk-relative cumulative log2-decay
-  float pre0 = 0.f, pre1 = 0.f;     // its value before this lane's quarter
-  float gm0 = 0.f, gm1 = 0.f, ge0 = 0.f, ge1 = 0.f;  // one-reference window of the chunk
-  float post0 = 1.f, post1 = 1.f;   // previous window's 2^{G_end - Gm}
-  float bl = 0.f;                   // beta of token 16 tq + cp
+  u32x4 Rq[4], Rk[4], Rv[4];   // 8 bf16 channels per token
+  f32x4 Rg[4][2];              // 8 fp32 channels per token
+  float Rb[4];                 // beta per token
+  float Gl[4][8];              // log2-decay summed from the quarter's start (inclusive)
+  float qp[8];                 // of the earlier quarters of the chunk
+  float gref[8], gend[8];      // reference and end of a 64-token window (chunk-relative)
   int blk = 0, win = 0;
   bool slow = false;
 
@@ -203,8 +194,8 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   const bf16 *kg = reinterpret_cast<const bf16 *>(p.k) + (int64_t)h * kD;
   const bf16 *vg = reinterpret_cast<const bf16 *>(p.v) + (int64_t)h * kD;
   const float *gg = p.g + (int64_t)h * kD;
-  const uint32_t voff_b16 = (uint32_t)tq * 16u * row_b16 + (uint32_t)c0 * 2u;
-  const uint32_t voff_f32 = (uint32_t)tq * 16u * row_f32 + (uint32_t)c0 * 4u;
+  const uint32_t voff_b16 = (uint32_t)r0 * row_b16 + 16u * co;
+  const uint32_t voff_f32 = (uint32_t)r0 * row_f32 + 32u * co;
   auto rows_of = [&](int b) -> uint32_t {
     const int64_t rem = len - (int64_t)b * kC;
     return rem >= kC ? (uint32_t)kC : (uint32_t)(rem > 0 ? rem : 0);
@@ -216,192 +207,218 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     const uint32_t nr = rows_of(b);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + t0 * rowstride, nr * row_b16);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + t0 * rowstride, nr * row_b16);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + t0 * H + h, nr * row_beta);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t so = (uint32_t)t * row_b16;
-      Rq[t] = buf_load_b32(rq, voff_b16, so);
-      Rk[t] = buf_load_b32(rk, voff_b16, so);
+    for (int j = 0; j < 4; ++j) {
+      Rq[j] = buf_load_b128(rq, voff_b16, (uint32_t)j * row_b16);
+      Rk[j] = buf_load_b128(rk, voff_b16, (uint32_t)j * row_b16);
+      Rb[j] = __uint_as_float(buf_load_b32(rb, (uint32_t)r0 * row_beta, (uint32_t)j * row_beta));
     }
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + t0 * H + h, nr * (uint32_t)H * 4u);
-    bl = __uint_as_float(buf_load_b32(rb, (uint32_t)(16 * tq + cp) * (uint32_t)H * 4u));
   };
   auto issue_v = [&](int b) {
     const int64_t t0 = bos + (int64_t)b * kC;
     const uint32_t nr = itm.zero_v ? 0u : rows_of(b);  // the M tracker runs with v = 0
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + t0 * rowstride, nr * row_b16);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Rv[t] = buf_load_b32(rv, voff_b16, (uint32_t)t * row_b16);
+    for (int j = 0; j < 4; ++j) Rv[j] = buf_load_b128(rv, voff_b16, (uint32_t)j * row_b16);
   };
   auto issue_g = [&](int b) {
     const int64_t t0 = bos + (int64_t)b * kC;
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gg + t0 * rowstride, rows_of(b) * row_f32);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Rg[t] = buf_load_f32x2(rg, voff_f32, (uint32_t)t * row_f32);
+    for (int j = 0; j < 4; ++j) {
+      Rg[j][0] = __builtin_bit_cast(f32x4, buf_load_b128(rg, voff_f32, (uint32_t)j * row_f32));
+      Rg[j][1] = __builtin_bit_cast(f32x4, buf_load_b128(rg, voff_f32 + 16u, (uint32_t)j * row_f32));
+    }
   };
-  // Cumulative log2-decay of a chunk from Rg, its one-reference window (Gm =
-  // middle of the range of G, G_end), and whether that range fits; the wave's
-  // verdict goes to sm.flag[pw].
+  // Log2-decay of a chunk from Rg: Gl (from the quarter's start), the quarter's
+  // totals to sm.qtot[pw], and whether no log-decay of the quarter is positive
+  // to sm.flag[pw].
   auto digest_g = [&]() {
-    float a0 = 0.f, a1 = 0.f;
+    bool ok = true;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      a0 = fmaf(Rg[t][0], kLog2e, a0);
-      a1 = fmaf(Rg[t][1], kLog2e, a1);
-      G0[t] = a0;
-      G1[t] = a1;
-    }
-    float q0[4], q1[4];  // quarter totals of this channel pair
+    for (int i = 0; i < 8; ++i) {
+      float a = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      q0[q] = bperm(a0, 16 * q + cp);
-      q1[q] = bperm(a1, 16 * q + cp);
-    }
-    pre0 = 0.f;
-    pre1 = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const float gv = Rg[j][i >> 2][i & 3];
+        ok = ok && gv <= 0.f;  // false on NaN
+        a = fmaf(gv, kLog2e, a);
+        Gl[j][i] = a;
+      }
+      // scan over the four lanes (stride 16) that share the channel
+      float x = a;
+      const float y1 = bperm(x, lane - 16);
+      x += ts >= 1 ? y1 : 0.f;
+      const float y2 = bperm(x, lane - 32);
+      x += ts >= 2 ? y2 : 0.f;
+      const float excl = x - a;
+      const float tot = bperm(x, 48 + co);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      pre0 += q < tq ? q0[q] : 0.f;
-      pre1 += q < tq ? q1[q] : 0.f;
+      for (int j = 0; j < 4; ++j) Gl[j][i] += excl;
+      if (ts == 0) sm.qtot[pw][8 * co + i] = tot;
     }
-    ge0 = q0[0] + q0[1] + q0[2] + q0[3];
-    ge1 = q1[0] + q1[1] + q1[2] + q1[3];
-    float mx0 = -INFINITY, mn0 = INFINITY, mx1 = -INFINITY, mn1 = INFINITY;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      G0[t] += pre0;
-      G1[t] += pre1;
-      mx0 = fmaxf(mx0, G0[t]);
-      mn0 = fminf(mn0, G0[t]);
-      mx1 = fmaxf(mx1, G1[t]);
-      mn1 = fminf(mn1, G1[t]);
-    }
-#pragma unroll
-    for (int x = 16; x < 64; x <<= 1) {
-      mx0 = fmaxf(mx0, bperm(mx0, lane ^ x));
-      mn0 = fminf(mn0, bperm(mn0, lane ^ x));
-      mx1 = fmaxf(mx1, bperm(mx1, lane ^ x));
-      mn1 = fminf(mn1, bperm(mn1, lane ^ x));
-    }
-    gm0 = 0.5f * (mx0 + mn0);
-    gm1 = 0.5f * (mx1 + mn1);
-    const bool ok = (mx0 - mn0 <= kMaxRange) && (mx1 - mn1 <= kMaxRange);  // false on NaN
     const bool wave_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
     if (lane == 0) sm.flag[pw] = wave_ok ? 1 : 0;
   };
+  // After the barrier that follows digest_g: chunk-relative prefix of this
+  // quarter, the one-reference window, and whether it fits (same on all waves).
+  auto decide = [&]() -> bool {
+    f32x4 t[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      t[q][0] = *reinterpret_cast<const f32x4 *>(&sm.qtot[q][8 * co]);
+      t[q][1] = *reinterpret_cast<const f32x4 *>(&sm.qtot[q][8 * co + 4]);
+    }
+    bool ok = sm.flag[0] && sm.flag[1] && sm.flag[2] && sm.flag[3];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = t[0][i >> 2][i & 3], q1 = t[1][i >> 2][i & 3];
+      const float q2 = t[2][i >> 2][i & 3], q3 = t[3][i >> 2][i & 3];
+      qp[i] = (pw > 0 ? q0 : 0.f) + (pw > 1 ? q1 : 0.f) + (pw > 2 ? q2 : 0.f);
+      gref[i] = q0 + q1;
+      gend[i] = q0 + q1 + q2 + q3;
+      ok = ok && (-gref[i] <= kMaxHalf) && (gref[i] - gend[i] <= kMaxHalf);
+    }
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+  };
 
-  if (nblk > 0) {
-    issue_g(0);
-    digest_g();  // waits for g of chunk 0
-    issue_qk(0);
-    issue_v(0);
-    if (nblk > 1) issue_g(1);
-  }
+  // Every iteration issues the same loads in the same order -- q, k, beta in
+  // the first phase; v, then g in the second -- so the hardware's in-order load
+  // counter lets each use wait for exactly its own group.  Loads of a chunk past
+  // the sequence read nothing (empty buffer range); a group that is not due yet
+  // (the next window is in the same chunk) reloads the chunk it already holds.
+  issue_g(0);
+  digest_g();  // waits for g of chunk 0
+  issue_qk(0);
+  issue_v(0);
+  issue_g(1);
   block_sync();
-  if (nblk > 0) slow = !(sm.flag[0] && sm.flag[1] && sm.flag[2] && sm.flag[3]);
+  slow = !decide();
 
   for (int it = 0;; ++it) {
     Buf &B = sm.buf[it & 1];
+    const Buf &Bprev = sm.buf[(it + 1) & 1];
+    const int Lc = (int)rows_of(blk);
+    const int nwin = slow ? (Lc + 15) / 16 : 1;
+    const bool last = win == nwin - 1;  // last window of the chunk
     // ====================== phase 1: operands of window it
     if (blk < nblk) {
-      const int Lc = (int)rows_of(blk);
-      const int nwin = slow ? (Lc + 15) / 16 : 1;
       const int row_lo = slow ? 16 * win : 0;
       const int row_hi = slow ? (16 * win + 16 < Lc ? 16 * win + 16 : Lc) : Lc;
-      // the window's reference and end, per channel; a 16-token window is the
-      // quarter tq == win, measured from its start
-      const bool mine = !slow || tq == win;
-      float off0 = 0.f, off1 = 0.f, wm0 = gm0, wm1 = gm1, we0 = ge0, we1 = ge1;
-      if (slow) {
-        off0 = pre0;
-        off1 = pre1;
-        float mx0 = -INFINITY, mn0 = INFINITY, mx1 = -INFINITY, mn1 = INFINITY;
+      // this window's reference and end per channel, relative to its start; the
+      // lanes' offset to it (a 16-token window is quarter win, so only its wave
+      // holds its tokens)
+      const bool mine = !slow || pw == win;
+      float off[8], wref[8], wend[8];
+      if (!slow) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          mx0 = fmaxf(mx0, G0[t]);
-          mn0 = fminf(mn0, G0[t]);
-          mx1 = fmaxf(mx1, G1[t]);
-          mn1 = fminf(mn1, G1[t]);
+        for (int i = 0; i < 8; ++i) {
+          wref[i] = gref[i];
+          wend[i] = gend[i];
+          off[i] = qp[i] - gref[i];
         }
-        // computed on every lane, taken from the window's lanes
-        wm0 = bperm(0.5f * (mx0 + mn0) - off0, 16 * win + cp);
-        wm1 = bperm(0.5f * (mx1 + mn1) - off1, 16 * win + cp);
-        we0 = bperm(G0[15] - off0, 16 * win + cp);
-        we1 = bperm(G1[15] - off1, 16 * win + cp);
-      }
-      if (tq == 0)
-        *reinterpret_cast<f32x2 *>(B.mfac + c0) = f32x2{post0 * fast_exp2(wm0), post1 * fast_exp2(wm1)};
-      post0 = fast_exp2(we0 - wm0);
-      post1 = fast_exp2(we1 - wm1);
-      if (tq == 0) *reinterpret_cast<f32x2 *>(B.post + c0) = f32x2{post0, post1};
-      if (pw == 0) {
-        const int r = 16 * tq + cp;
-        B.beta[r] = (r >= row_lo && r < row_hi) ? bl : 0.f;
-        if (lane == 0) {
-          B.info[0] = row_lo;
-          B.info[1] = row_hi;
-          B.info[2] = blk * kC;
-          B.info[3] = 1;
-        }
-      }
+      } else {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float nb = -bperm(bl, 16 * tq + t);
-        const int r = 16 * tq + t;
-        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, k20 = 0.f, k21 = 0.f;
-        if (mine) {
-          const float d0 = G0[t] - off0 - wm0, d1 = G1[t] - off1 - wm1;
-          const float e10 = fast_exp2(d0), e11 = fast_exp2(d1);
-          const float e20 = fast_exp2(-d0), e21 = fast_exp2(-d1);
-          const float k0 = __uint_as_float(Rk[t] << 16), k1 = __uint_as_float(Rk[t] & 0xffff0000u);
-          const float x0 = __uint_as_float(Rq[t] << 16), x1 = __uint_as_float(Rq[t] & 0xffff0000u);
-          a0 = k0 * e10 * nb;
-          a1 = k1 * e11 * nb;
-          b0 = x0 * e10;
-          b1 = x1 * e11;
-          k20 = k0 * e20;
-          k21 = k1 * e21;
+        for (int i = 0; i < 8; ++i) {
+          wref[i] = bperm(Gl[0][i], 32 + co);  // token 8 of the quarter
+          wend[i] = bperm(Gl[3][i], 48 + co);  // token 15
+          off[i] = -wref[i];
         }
-        store2<bf16>(B.nkr + r * kLDK + pc0, a0, a1);
-        store2<bf16>(B.qr + r * kLDK + pc0, b0, b1);
-        store2<bf16>(B.kc + r * kLDK + pc0, k20, k21);
       }
-      // the chunk's q, k, beta are dead after its last window: load the next
-      if (win == nwin - 1 && blk + 1 < nblk) issue_qk(blk + 1);
+      const bool writer = (slow ? pw == win : pw == 0) && ts == 0;
+      if (writer) {
+        f32x4 mf[2], po[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float prev = it > 0 ? Bprev.post[8 * co + i] : 1.f;
+          mf[i >> 2][i & 3] = prev * fast_exp2(wref[i]);
+          po[i >> 2][i & 3] = fast_exp2(wend[i] - wref[i]);
+        }
+        *reinterpret_cast<f32x4 *>(B.mfac + 8 * co) = mf[0];
+        *reinterpret_cast<f32x4 *>(B.mfac + 8 * co + 4) = mf[1];
+        *reinterpret_cast<f32x4 *>(B.post + 8 * co) = po[0];
+        *reinterpret_cast<f32x4 *>(B.post + 8 * co + 4) = po[1];
+      }
+      if (co == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) B.beta[r0 + j] = mine ? Rb[j] : 0.f;
+      }
+      if (pw == 0 && lane == 0) {
+        B.info[0] = row_lo;
+        B.info[1] = row_hi;
+        B.info[2] = blk * kC;
+        B.info[3] = 1;
+      }
+      // one window's operands; in a 16-token window the other waves write zeros
+      auto operands = [&](bool keep) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = r0 + j;
+          const float nb = -Rb[j];
+          const u32x4 kr = keep ? Rk[j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 qr = keep ? Rq[j] : u32x4{0u, 0u, 0u, 0u};
+          float a[8], b[8], c[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float d = keep ? Gl[j][i] + off[i] : 0.f;
+            const float e1 = fast_exp2(d), e2 = fast_exp2(-d);
+            const uint32_t kw = kr[i >> 1], qw = qr[i >> 1];
+            const float kv = __uint_as_float((i & 1) ? (kw & 0xffff0000u) : (kw << 16));
+            const float qv = __uint_as_float((i & 1) ? (qw & 0xffff0000u) : (qw << 16));
+            a[i] = kv * e1 * nb;
+            b[i] = qv * e1;
+            c[i] = kv * e2;
+          }
+          store4<bf16>(B.nkr + r * kLDK + pA, f32x4{a[0], a[1], a[2], a[3]});
+          store4<bf16>(B.nkr + r * kLDK + pB, f32x4{a[4], a[5], a[6], a[7]});
+          store4<bf16>(B.qr + r * kLDK + pA, f32x4{b[0], b[1], b[2], b[3]});
+          store4<bf16>(B.qr + r * kLDK + pB, f32x4{b[4], b[5], b[6], b[7]});
+          store4<bf16>(B.kc + r * kLDK + pA, f32x4{c[0], c[1], c[2], c[3]});
+          store4<bf16>(B.kc + r * kLDK + pB, f32x4{c[4], c[5], c[6], c[7]});
+        }
+      };
+      if (!slow)
+        operands(true);
+      else
+        operands(mine);
     } else if (pw == 0 && lane == 0) {
       B.info[3] = 0;  // no window: the consumers finish with the previous one
     }
+    // q, k, beta of the next window's chunk
+    issue_qk(last ? blk + 1 : blk);
     block_sync();
-    // ====================== phase 2: Gram products and inverses of window it
+    // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
-      const int Lc = (int)rows_of(blk);
-      const int nwin = slow ? (Lc + 15) / 16 : 1;
       switch (pw) {
-        case 0: gram_and_inverse<0>(B, l16, g4); break;
-        case 1: gram_and_inverse<1>(B, l16, g4); break;
-        case 2: gram_and_inverse<2>(B, l16, g4); break;
-        default: gram_and_inverse<3>(B, l16, g4); break;
+        case 0: gram_a<0>(B, l16, g4); break;
+        case 1: gram_a<1>(B, l16, g4); break;
+        case 2: gram_a<2>(B, l16, g4); break;
+        default: gram_a<3>(B, l16, g4); break;
       }
       if (win == 0) {
         // v of this chunk for the consumers (their reads of the previous chunk's v
-        // were in the phase before the last barrier); then load the next chunk's
+        // were in the phase before the last barrier)
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-          *reinterpret_cast<uint32_t *>(sm.v + (16 * tq + t) * kLDK + c0) = Rv[t];
-        if (blk + 1 < nblk) issue_v(blk + 1);
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x4 *>(sm.v + (r0 + j) * kLDK + 8 * co) = Rv[j];
       }
-      if (win == nwin - 1) {
-        if (blk + 1 < nblk) {
-          digest_g();  // the next chunk; its verdict is read after the barrier
-          if (blk + 2 < nblk) issue_g(blk + 2);
-        }
+    }
+    issue_v(blk + 1);  // v of the next chunk (written at its first window)
+    if (blk < nblk && last && blk + 1 < nblk) digest_g();  // read after the barrier
+    issue_g(blk < nblk && last ? blk + 2 : blk + 1);
+    bool fresh = false;  // a new chunk starts at the next window
+    if (blk < nblk) {
+      if (last) {
         ++blk;
         win = 0;
+        fresh = blk < nblk;
       } else {
         ++win;
       }
     }
     block_sync();
-    if (blk < nblk && win == 0) slow = !(sm.flag[0] && sm.flag[1] && sm.flag[2] && sm.flag[3]);
+    if (fresh) slow = !decide();
     if (!sm.buf[it & 1].info[3]) break;
   }
 }
@@ -414,15 +431,24 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   const int vcol = 32 * cw;
   const int64_t rowstride = (int64_t)p.H * kD;
   f32x4 acc[2][8];  // acc[c2][ct] = S'[16 ct + 4 g4 + e][vcol + 16 c2 + l16]
+  if (itm.s0) {
 #pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+      for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * ct + 4 * g4 + e, col = vcol + 16 * c2 + l16;
-        acc[c2][ct][e] = itm.s0 ? itm.s0[row * kD + col] : (itm.zero_v && row == col ? 1.f : 0.f);
-      }
+        for (int e = 0; e < 4; ++e)
+          acc[c2][ct][e] = itm.s0[(16 * ct + 4 * g4 + e) * kD + vcol + 16 * c2 + l16];
+  } else {
+    const float diag = itm.zero_v ? 1.f : 0.f;  // identity for the M tracker
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[c2][ct][e] = (16 * ct + 4 * g4 + e) == (vcol + 16 * c2 + l16) ? diag : 0.f;
+  }
   block_sync();
 
   int it = 0;
@@ -470,6 +496,36 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
             mma(accOT[c2][s4], sf[c2][kk], xq);
           }
         }
+      // row block cw of P = Qr Kc^T (tiles j <= cw; lane holds [16 cw + l16][16 j + 4 g4 + e])
+      f32x4 accP[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) accP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        Frag<bf16> xq;
+        lds_frag_ck(xq, B.qr, kLDK, 16 * cw + l16, 32 * kk, g4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j <= cw) {
+            Frag<bf16> xk;
+            lds_frag_ck(xk, B.kc, kLDK, 16 * j + l16, 32 * kk, g4);
+            mma(accP[j], xk, xq);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j <= cw) {
+          f32x4 pv = accP[j];
+          if (j == cw) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e) <= l16 ? pv[e] : 0.f;
+          }
+          store4<bf16>(B.pm + (16 * cw + l16) * kLDC + skpos(16 * j + 4 * g4), pv);
+        }
+      }
+      // the inverse of diagonal block cw of the triangular system
+      invert_diag(B, cw, l16, g4);
     }
     block_sync();
     // ====================== phase 2: U, O, state update, o stores

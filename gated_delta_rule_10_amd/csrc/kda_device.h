@@ -26,6 +26,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -159,8 +160,11 @@ __device__ __forceinline__ f32x2 buf_load_f32x2(__amdgpu_buffer_rsrc_t r, uint32
                                                 uint32_t soff = 0) {
   return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kNonTemporal));
 }
+__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kNonTemporal);
+}
 __device__ __forceinline__ void buf_store_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4 &v) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kNonTemporal);
 }
 
