@@ -87,57 +87,101 @@ __device__ __forceinline__ float bperm(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
 }
 
-// Lower 16x16 tiles (i, j), i >= j, of -beta A = nKr Kc^T computed by producer
-// wave P: the tiles of a wave share their Kc column block.
-__device__ constexpr int kTileI[4][3] = {{0, 1, 2}, {1, 2, 3}, {2, 3, -1}, {3, 3, -1}};
-__device__ constexpr int kTileJ[4][3] = {{0, 0, 0}, {1, 1, 1}, {2, 2, -1}, {3, 0, -1}};
-
-// Gram products -beta A of one window into Lm (bf16, row-major).  The diagonal
-// tiles are stored whole; the consumer that inverts a diagonal block reads only
-// its strictly lower part.
-template <int P>
-__device__ __forceinline__ void gram_a(Buf &B, int l16, int g4) {
-  constexpr int nt = kTileI[P][2] < 0 ? 2 : 3;
-  f32x4 acc[3];
+// B^T C for 16x16 fp32 tiles in the result layout (lane holds M[4 g4 + e][l16]),
+// on bf16 matrix cores with each operand split into a bf16 head and a bf16 tail
+// (x = h + t): B^T C ~ Bh^T Ch + Bh^T Ct + Bt^T Ch, relative error ~2^-16.  The
+// result layout is directly the operand layout of V_MFMA_F32_16X16X16_BF16 for
+// a transposed left factor, so no data moves between lanes.
+struct Split { Frag4<bf16> h, t; };
+__device__ __forceinline__ Split split(const f32x4 &x) {
+  Split s;
 #pragma unroll
-  for (int u = 0; u < nt; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 4; ++e) {
+    const bf16 h = (bf16)x[e];
+    s.h.v[e] = h;
+    s.t.v[e] = (bf16)(x[e] - (float)h);
+  }
+  return s;
+}
+__device__ __forceinline__ f32x4 tn(const Split &b, const Split &c) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  mma16(acc, b.h, c.t);
+  mma16(acc, b.t, c.h);
+  mma16(acc, b.h, c.h);
+  return acc;
+}
+
+// Gram jobs of producer wave P: (kind, row tile i, column tile j).
+// kind 0: -beta A tile (i > j) -> Lm;  1: P tile -> Pm;  2, 3: the diagonal tile
+// (i, i) of -beta A as [r][s] and as [s][r] (for the inverse).  Each wave owns
+// one diagonal block; the off-diagonal tiles are spread so a wave's tiles share
+// operands.
+struct Job { int kind, i, j; };
+__device__ constexpr Job kJobs[4][6] = {
+    {{2, 0, 0}, {3, 0, 0}, {1, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}},
+    {{2, 3, 3}, {3, 3, 3}, {1, 3, 3}, {1, 2, 0}, {0, 3, 0}, {1, 3, 0}},
+    {{2, 1, 1}, {3, 1, 1}, {1, 1, 1}, {0, 2, 1}, {1, 2, 1}, {0, 3, 1}},
+    {{2, 2, 2}, {3, 2, 2}, {1, 2, 2}, {1, 3, 1}, {0, 3, 2}, {1, 3, 2}}};
+
+// Gram products of one window (-beta A into Lm, P into Pm) and the inverse of
+// this wave's diagonal block, X_dd = (I + N)^{-1} with N = beta A_dd strictly
+// lower, in the result layout:
+//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0;
+// each power is paired with its transpose because the products are B^T C.
+template <int P>
+__device__ __forceinline__ void gram_and_inverse(Buf &B, int l16, int g4) {
+  f32x4 acc[6];
+#pragma unroll
+  for (int u = 0; u < 6; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int u = 0; u < nt; ++u) {
-      // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
+    for (int u = 0; u < 6; ++u) {
+      const Job jb = kJobs[P][u];
       Frag<bf16> fx, fy;
-      lds_frag_ck(fx, B.kc, kLDK, 16 * kTileJ[P][u] + l16, 32 * kk, g4);
-      lds_frag_ck(fy, B.nkr, kLDK, 16 * kTileI[P][u] + l16, 32 * kk, g4);
+      if (jb.kind == 2) {         // [r][s]: rows of nKr_i against Kc_i
+        lds_frag_ck(fx, B.nkr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+        lds_frag_ck(fy, B.kc, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+      } else if (jb.kind == 3) {  // [s][r]
+        lds_frag_ck(fx, B.kc, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+        lds_frag_ck(fy, B.nkr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+      } else {                    // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
+        lds_frag_ck(fx, B.kc, kLDK, 16 * jb.j + l16, 32 * kk, g4);
+        lds_frag_ck(fy, jb.kind == 0 ? B.nkr : B.qr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+      }
       mma(acc[u], fx, fy);
     }
   }
 #pragma unroll
-  for (int u = 0; u < nt; ++u)
-    store4<bf16>(B.lm + (16 * kTileI[P][u] + l16) * kLDC + 16 * kTileJ[P][u] + 4 * g4, acc[u]);
-}
-
-// In place on diagonal block d of Lm: -beta A_dd (strictly lower part) becomes
-// X_dd = (I + N)^{-1}, N = beta A_dd.  Result layout (lane holds M[4 g4 + e][l16]):
-//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0.
-// rr_tn(B, C) = B^T C on fp32 matrix cores, so each power is paired with its
-// transpose.
-__device__ __forceinline__ void invert_diag(Buf &B, int d, int l16, int g4) {
-  bf16 *blk = B.lm + 16 * d * kLDC + 16 * d;
-  // T[4 g4 + e][l16] by a transposing load; T^T[4 g4 + e][l16] = T[l16][4 g4 + e] directly
-  const bf16x4 t = lds_read_tr(blk + (4 * g4 + (l16 >> 2)) * kLDC + 4 * (l16 & 3));
-  const bf16x4 tt = *reinterpret_cast<const bf16x4 *>(blk + l16 * kLDC + 4 * g4);
+  for (int u = 2; u < 6; ++u) {
+    const Job jb = kJobs[P][u];
+    const int r = 16 * jb.i + l16;
+    if (jb.kind == 0) {
+      store4<bf16>(B.lm + r * kLDC + 16 * jb.j + 4 * g4, acc[u]);
+    } else {
+      f32x4 pv = acc[u];
+      if (jb.i == jb.j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e) <= l16 ? pv[e] : 0.f;
+      }
+      store4<bf16>(B.pm + r * kLDC + skpos(16 * jb.j + 4 * g4), pv);
+    }
+  }
+  constexpr int d = kJobs[P][0].i;
   f32x4 N, NT;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int a = 4 * g4 + e;
-    N[e] = l16 < a ? -(float)t[e] : 0.f;
-    NT[e] = a < l16 ? -(float)tt[e] : 0.f;
+    N[e] = l16 < a ? -acc[0][e] : 0.f;
+    NT[e] = a < l16 ? -acc[1][e] : 0.f;
   }
-  const f32x4 N2 = rr_tn(NT, N), T2 = rr_tn(N, NT);
-  const f32x4 N3 = rr_tn(NT, N2), T3 = rr_tn(N, T2);
-  const f32x4 N4 = rr_tn(T2, N2), T4 = rr_tn(N2, T2);
-  const f32x4 N8 = rr_tn(T4, N4);
+  const Split sN = split(N), sNT = split(NT);
+  const f32x4 N2 = tn(sNT, sN), T2 = tn(sN, sNT);
+  const Split sN2 = split(N2), sT2 = split(T2);
+  const f32x4 N3 = tn(sNT, sN2), T3 = tn(sN, sT2);
+  const f32x4 N4 = tn(sT2, sN2), T4 = tn(sN2, sT2);
+  const Split sN4 = split(N4), sT4 = split(T4);
+  const f32x4 N8 = tn(sT4, sN4);
   f32x4 P1, P1T;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -145,12 +189,12 @@ __device__ __forceinline__ void invert_diag(Buf &B, int d, int l16, int g4) {
     P1[e] = id - N[e] + N2[e] - N3[e];
     P1T[e] = id - NT[e] + T2[e] - T3[e];
   }
-  const f32x4 P2 = P1 + rr_tn(P1T, N4);
-  const f32x4 P2T = P1T + rr_tn(N4, P1T);
-  const f32x4 Xd = P2 + rr_tn(P2T, N8);
-  // every lane has read its operands before any writes (one wave, in order)
+  const Split sP1T = split(P1T);
+  const f32x4 P2 = P1 + tn(sP1T, sN4);
+  const f32x4 P2T = P1T + tn(sN4, sP1T);
+  const f32x4 Xd = P2 + tn(split(P2T), split(N8));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * kLDC + l16] = (bf16)Xd[e];
+  for (int e = 0; e < 4; ++e) B.lm[(16 * d + 4 * g4 + e) * kLDC + 16 * d + l16] = (bf16)Xd[e];
 }
 
 // ---------------------------------------------------------------- producers
@@ -236,27 +280,39 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   // to sm.flag[pw].
   auto digest_g = [&]() {
     bool ok = true;
+    float a[8], x[8], y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float a = 0.f;
+      a[i] = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float gv = Rg[j][i >> 2][i & 3];
         ok = ok && gv <= 0.f;  // false on NaN
-        a = fmaf(gv, kLog2e, a);
-        Gl[j][i] = a;
+        a[i] = fmaf(gv, kLog2e, a[i]);
+        Gl[j][i] = a[i];
       }
-      // scan over the four lanes (stride 16) that share the channel
-      float x = a;
-      const float y1 = bperm(x, lane - 16);
-      x += ts >= 1 ? y1 : 0.f;
-      const float y2 = bperm(x, lane - 32);
-      x += ts >= 2 ? y2 : 0.f;
-      const float excl = x - a;
-      const float tot = bperm(x, 48 + co);
+    }
+    // inclusive scan over the four lanes (stride 16) that share a channel, all
+    // eight channels at once so the lane exchanges overlap
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = bperm(a[i], lane - 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = a[i] + (ts >= 1 ? y[i] : 0.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = bperm(x[i], lane - 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] += ts >= 2 ? y[i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = bperm(x[i], 48 + co);  // quarter total
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float excl = x[i] - a[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) Gl[j][i] += excl;
-      if (ts == 0) sm.qtot[pw][8 * co + i] = tot;
+    }
+    if (ts == 0) {
+      *reinterpret_cast<f32x4 *>(&sm.qtot[pw][8 * co]) = f32x4{y[0], y[1], y[2], y[3]};
+      *reinterpret_cast<f32x4 *>(&sm.qtot[pw][8 * co + 4]) = f32x4{y[4], y[5], y[6], y[7]};
     }
     const bool wave_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
     if (lane == 0) sm.flag[pw] = wave_ok ? 1 : 0;
@@ -391,10 +447,10 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
       switch (pw) {
-        case 0: gram_a<0>(B, l16, g4); break;
-        case 1: gram_a<1>(B, l16, g4); break;
-        case 2: gram_a<2>(B, l16, g4); break;
-        default: gram_a<3>(B, l16, g4); break;
+        case 0: gram_and_inverse<0>(B, l16, g4); break;
+        case 1: gram_and_inverse<1>(B, l16, g4); break;
+        case 2: gram_and_inverse<2>(B, l16, g4); break;
+        default: gram_and_inverse<3>(B, l16, g4); break;
       }
       if (win == 0) {
         // v of this chunk for the consumers (their reads of the previous chunk's v
@@ -451,12 +507,14 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   }
   block_sync();
 
+  // Window it - 1 in iteration it: Y and O^T products in the first phase, the
+  // substitution, state update and o stores in the second.
   int it = 0;
   for (;; ++it) {
-    Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
     f32x4 accY[2][4], accOT[2][4];
     // ====================== phase 1: Y and O^T products
     if (it > 0) {
+      Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
       // bring the state to this window's scale
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
@@ -496,40 +554,11 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
             mma(accOT[c2][s4], sf[c2][kk], xq);
           }
         }
-      // row block cw of P = Qr Kc^T (tiles j <= cw; lane holds [16 cw + l16][16 j + 4 g4 + e])
-      f32x4 accP[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) accP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        Frag<bf16> xq;
-        lds_frag_ck(xq, B.qr, kLDK, 16 * cw + l16, 32 * kk, g4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j <= cw) {
-            Frag<bf16> xk;
-            lds_frag_ck(xk, B.kc, kLDK, 16 * j + l16, 32 * kk, g4);
-            mma(accP[j], xk, xq);
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j <= cw) {
-          f32x4 pv = accP[j];
-          if (j == cw) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e) <= l16 ? pv[e] : 0.f;
-          }
-          store4<bf16>(B.pm + (16 * cw + l16) * kLDC + skpos(16 * j + 4 * g4), pv);
-        }
-      }
-      // the inverse of diagonal block cw of the triangular system
-      invert_diag(B, cw, l16, g4);
     }
     block_sync();
     // ====================== phase 2: U, O, state update, o stores
     if (it > 0) {
+      Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
       const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
       // U = (I + beta A)^{-1} Y by block forward substitution:
       //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
@@ -588,18 +617,25 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
         }
-      // o rows of this window
+      // o rows of this window: staged through this wave's own 32 columns of the
+      // window's nKr rows (read by no one after phase 1), so each store writes
+      // 64 contiguous bytes of a row
       if (itm.write_o) {
-        bf16 *og = reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride +
-                   (int64_t)itm.h * kD + vcol + 4 * g4;
+        bf16 *stage = B.nkr + vcol;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int r = 16 * rt + l16;
-          if (r >= row_lo && r < row_hi) {
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-              store4<bf16>(og + (int64_t)r * rowstride + 16 * c2, accOT[c2][rt] * p.scale);
-          }
+          for (int c2 = 0; c2 < 2; ++c2)
+            store4<bf16>(stage + (16 * rt + l16) * kLDK + 16 * c2 + 4 * g4, accOT[c2][rt] * p.scale);
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+            reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
+            (uint32_t)row_hi * (uint32_t)rowstride * 2u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int r = 16 * k + l16;
+          const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
+          if (r >= row_lo)
+            buf_store_b128(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
         }
       }
     }
