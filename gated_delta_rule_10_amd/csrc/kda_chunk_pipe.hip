@@ -117,19 +117,18 @@ __device__ __forceinline__ f32x4 tn(const Split &b, const Split &c) {
 // one diagonal block; the off-diagonal tiles are spread so a wave's tiles share
 // operands.
 struct Job { int kind, i, j; };
+__device__ constexpr int kDiag[4] = {0, 3, 1, 2};  // diagonal block of each wave
 __device__ constexpr Job kJobs[4][6] = {
     {{2, 0, 0}, {3, 0, 0}, {1, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}},
     {{2, 3, 3}, {3, 3, 3}, {1, 3, 3}, {1, 2, 0}, {0, 3, 0}, {1, 3, 0}},
     {{2, 1, 1}, {3, 1, 1}, {1, 1, 1}, {0, 2, 1}, {1, 2, 1}, {0, 3, 1}},
     {{2, 2, 2}, {3, 2, 2}, {1, 2, 2}, {1, 3, 1}, {0, 3, 2}, {1, 3, 2}}};
 
-// Gram products of one window (-beta A into Lm, P into Pm) and the inverse of
-// this wave's diagonal block, X_dd = (I + N)^{-1} with N = beta A_dd strictly
-// lower, in the result layout:
-//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0;
-// each power is paired with its transpose because the products are B^T C.
+// Gram products of one window: -beta A into Lm and P into Pm, except this
+// wave's diagonal block of -beta A, returned in both orientations (dA[r][s],
+// dAT[s][r]) for its inverse.
 template <int P>
-__device__ __forceinline__ void gram_and_inverse(Buf &B, int l16, int g4) {
+__device__ __forceinline__ void gram(Buf &B, int l16, int g4, f32x4 &dA, f32x4 &dAT) {
   f32x4 acc[6];
 #pragma unroll
   for (int u = 0; u < 6; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -167,13 +166,23 @@ __device__ __forceinline__ void gram_and_inverse(Buf &B, int l16, int g4) {
       store4<bf16>(B.pm + r * kLDC + skpos(16 * jb.j + 4 * g4), pv);
     }
   }
-  constexpr int d = kJobs[P][0].i;
+  dA = acc[0];
+  dAT = acc[1];
+}
+
+// Diagonal block d of the triangular system from -beta A_dd (both
+// orientations, in the result layout: lane holds M[4 g4 + e][l16]):
+// X_dd = (I + N)^{-1} with N = beta A_dd strictly lower, into Lm,
+//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0;
+// each power is paired with its transpose because the products are B^T C.
+__device__ __forceinline__ void inverse(Buf &B, int d, const f32x4 &dA, const f32x4 &dAT, int l16,
+                                        int g4) {
   f32x4 N, NT;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int a = 4 * g4 + e;
-    N[e] = l16 < a ? -acc[0][e] : 0.f;
-    NT[e] = a < l16 ? -acc[1][e] : 0.f;
+    N[e] = l16 < a ? -dA[e] : 0.f;
+    NT[e] = a < l16 ? -dAT[e] : 0.f;
   }
   const Split sN = split(N), sNT = split(NT);
   const f32x4 N2 = tn(sNT, sN), T2 = tn(sN, sNT);
@@ -233,6 +242,8 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   float gref[8], gend[8];      // reference and end of a 64-token window (chunk-relative)
   int blk = 0, win = 0;
   bool slow = false;
+  f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA;  // diagonal block awaiting its inverse
+  bool pend = false;
 
   const bf16 *qg = reinterpret_cast<const bf16 *>(p.q) + (int64_t)h * kD;
   const bf16 *kg = reinterpret_cast<const bf16 *>(p.k) + (int64_t)h * kD;
@@ -358,7 +369,13 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     const int Lc = (int)rows_of(blk);
     const int nwin = slow ? (Lc + 15) / 16 : 1;
     const bool last = win == nwin - 1;  // last window of the chunk
-    // ====================== phase 1: operands of window it
+    // ====================== phase 1: operands of window it, and the inverse of
+    // this wave's diagonal block of window it - 1 (its Gram products were the
+    // last phase's; the consumers read it in the next phase)
+    if (pend) {
+      inverse(sm.buf[(it + 1) & 1], kDiag[pw], dA, dAT, l16, g4);
+      pend = false;
+    }
     if (blk < nblk) {
       const int row_lo = slow ? 16 * win : 0;
       const int row_hi = slow ? (16 * win + 16 < Lc ? 16 * win + 16 : Lc) : Lc;
@@ -447,11 +464,12 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
       switch (pw) {
-        case 0: gram_and_inverse<0>(B, l16, g4); break;
-        case 1: gram_and_inverse<1>(B, l16, g4); break;
-        case 2: gram_and_inverse<2>(B, l16, g4); break;
-        default: gram_and_inverse<3>(B, l16, g4); break;
+        case 0: gram<0>(B, l16, g4, dA, dAT); break;
+        case 1: gram<1>(B, l16, g4, dA, dAT); break;
+        case 2: gram<2>(B, l16, g4, dA, dAT); break;
+        default: gram<3>(B, l16, g4, dA, dAT); break;
       }
+      pend = true;
       if (win == 0) {
         // v of this chunk for the consumers (their reads of the previous chunk's v
         // were in the phase before the last barrier)
