@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--workload", default=PREFILL_WORKLOAD)
     ap.add_argument("--segments", type=int, default=0,
                     help="segments per sequence (0 = the library's automatic choice)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from rocprofv3 --pmc FETCH_SIZE and "
+                         "WRITE_SIZE counter_collection.csv files (taken with "
+                         "--copy-calibration-mib) and exit; needs no GPU")
     return ap.parse_args()
 
 
@@ -165,20 +169,73 @@ def cpu_baseline(x, chains_per_core, seconds):
             "token_heads_per_s": token_heads / dt, "seconds": dt}
 
 
+PREFILL_KERNEL = "chunk_fwd_pipe_kernel"
+PREFILL_SOURCES = ["gated_delta_rule_10_amd/csrc/kda_chunk_pipe.hip",
+                   "gated_delta_rule_10_amd/csrc/kda_chunk_common.h",
+                   "gated_delta_rule_10_amd/csrc/kda_device.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_b4_t8192_h96_traffic.json")
+
+
+def sources_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE readings,
     or None when they were taken on other kernel sources or another workload."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_b4_t8192_h96_traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_RECORD):
         return None
-    rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec["source_sha256"] or rec["workload"] != workload:
+    rec = json.load(open(TRAFFIC_RECORD))
+    if sources_digest(rec["sources"]) != rec["source_sha256"] or rec["workload"] != workload:
         return None
     return rec["traffic_bytes"]
+
+
+def copy_bytes_for(mib, heads=96):
+    """Bytes the calibration copy moves each way for a pool of `mib` MiB."""
+    return max(1, (mib << 20) // (heads * D * D * 4)) * heads * D * D * 4
+
+
+def record_traffic(fetch_csv, write_csv, workload, mib):
+    """Scale the prefill kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
+    what the same counters read for the state-pool copy of known size, and store
+    the result with a digest of the kernel's sources."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("prefill" if PREFILL_KERNEL in name else
+                   "copy" if "state_io_kernel" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_bytes_for(mib)
+    fscale = copy_bytes / 1024 / (sum(f["copy"]) / len(f["copy"]))
+    wscale = copy_bytes / 1024 / (sum(w["copy"]) / len(w["copy"]))
+    fk = sum(f["prefill"]) / len(f["prefill"])
+    wk = sum(w["prefill"]) / len(w["prefill"])
+    rec = {"kernel": PREFILL_KERNEL, "workload": workload, "sources": PREFILL_SOURCES,
+           "source_sha256": sources_digest(PREFILL_SOURCES),
+           "fetch_size_kib": fk, "write_size_kib": wk, "dispatches": len(f["prefill"]),
+           "copy_calibration": {"bytes_each_way": copy_bytes,
+                                "fetch_size_kib": sum(f["copy"]) / len(f["copy"]),
+                                "write_size_kib": sum(w["copy"]) / len(w["copy"]),
+                                "fetch_scale": fscale, "write_scale": wscale},
+           "read_bytes": round(fk * 1024 * fscale), "write_bytes": round(wk * 1024 * wscale)}
+    rec["traffic_bytes"] = rec["read_bytes"] + rec["write_bytes"]
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def copy_calibration(kda, mib):
@@ -208,6 +265,9 @@ def copy_calibration(kda, mib):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, args.workload, args.copy_calibration_mib or 1536)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -248,7 +308,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(args.workload),
-                     "kernel": "chunk_fwd_kernel<bf16,128>",
+                     "kernel": PREFILL_KERNEL,
                      "bytes_per_launch": alg_bytes},
     }
     if not args.no_decode:

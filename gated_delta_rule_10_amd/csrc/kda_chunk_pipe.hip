@@ -51,7 +51,7 @@ constexpr int kLDC = 72;             // 64-wide matrices (Lm, Pm): 64 bf16 + 16 
 constexpr float kMaxHalf = 64.f;     // largest log2-decay over each 32-token half of a window
 
 struct Buf {                   // one window's operands
-  bf16 nkr[64 * kLDK];         // -beta k 2^{G - Gm}      rows = tokens, columns skpos
+  bf16 nkr[64 * kLDK];         // -beta k 2^{G - Gm}      rows = tokens, columns chpos
   bf16 qr[64 * kLDK];          // q 2^{G - Gm}
   bf16 kc[64 * kLDK];          // k 2^{Gm - G}
   bf16 lm[64 * kLDC];          // -beta A below the diagonal blocks, X_ii on them
@@ -85,6 +85,48 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
 
 __device__ __forceinline__ float bperm(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+// Exchanges between the four 16-lane rows of a wave on the vector unit, without
+// the LDS crossbar (gfx950's V_PERMLANE16_SWAP / V_PERMLANE32_SWAP with both
+// operands equal): every lane gets the value of the same lane in the even and
+// the odd row of its pair (rows 0,1 or 2,3), resp. in rows 0..31 and 32..63.
+__device__ __forceinline__ void rows_of_pair(float v, float &even, float &odd) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  even = __uint_as_float(r[0]);
+  odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void halves(float v, float &lower, float &upper) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lower = __uint_as_float(r[0]);
+  upper = __uint_as_float(r[1]);
+}
+
+// Column order of the channel-indexed operands (nKr, Qr, Kc).  A matrix-core
+// fragment over channels 32 kk .. 32 kk + 31 holds, in lane group g, the quad
+// 4 g .. 4 g + 3 of the lower and of the upper 16 channels (the rows of two
+// state tiles); those 8 channels form one 16-byte chunk, chunk kk + 4 g of the
+// row, so a fragment is one 16-byte read.  In chunks with odd g the upper quad
+// comes first: then the transposing reads of Kc (8 rows x the 4 quads of a
+// 16-channel tile) and the producers' row stores touch every LDS bank once.
+__device__ __forceinline__ int chpos(int c) {
+  const int kk = c >> 5, h = (c >> 4) & 1, q = (c >> 2) & 3;
+  return 8 * (kk + 4 * q) + 4 * (h ^ (q & 1)) + (c & 3);
+}
+__device__ __forceinline__ void lds_frag_ch(Frag<bf16> &f, const bf16 *base, int row, int kk,
+                                            int g) {
+  f.v = *reinterpret_cast<const bf16x8 *>(base + row * kLDK + 8 * kk + 32 * g);
+}
+// The state fragment matching lds_frag_ch: tiles lo (channels 32 kk + 4 g + e)
+// and hi (+16), in the chunk's order.
+__device__ __forceinline__ void acc_frag_ch(Frag<bf16> &f, const f32x4 &lo, const f32x4 &hi, int g) {
+  Frag<bf16> t;
+  acc_frag_sk(t, lo, hi);
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, t.v);
+  const bool sw = g & 1;
+  const u32x4_t r = {sw ? w[2] : w[0], sw ? w[3] : w[1], sw ? w[0] : w[2], sw ? w[1] : w[3]};
+  f.v = __builtin_bit_cast(bf16x8, r);
 }
 
 // B^T C for 16x16 fp32 tiles in the result layout (lane holds M[4 g4 + e][l16]),
@@ -139,14 +181,14 @@ __device__ __forceinline__ void gram(Buf &B, int l16, int g4, f32x4 &dA, f32x4 &
       const Job jb = kJobs[P][u];
       Frag<bf16> fx, fy;
       if (jb.kind == 2) {         // [r][s]: rows of nKr_i against Kc_i
-        lds_frag_ck(fx, B.nkr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-        lds_frag_ck(fy, B.kc, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+        lds_frag_ch(fx, B.nkr, 16 * jb.i + l16, kk, g4);
+        lds_frag_ch(fy, B.kc, 16 * jb.i + l16, kk, g4);
       } else if (jb.kind == 3) {  // [s][r]
-        lds_frag_ck(fx, B.kc, kLDK, 16 * jb.i + l16, 32 * kk, g4);
-        lds_frag_ck(fy, B.nkr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+        lds_frag_ch(fx, B.kc, 16 * jb.i + l16, kk, g4);
+        lds_frag_ch(fy, B.nkr, 16 * jb.i + l16, kk, g4);
       } else {                    // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
-        lds_frag_ck(fx, B.kc, kLDK, 16 * jb.j + l16, 32 * kk, g4);
-        lds_frag_ck(fy, jb.kind == 0 ? B.nkr : B.qr, kLDK, 16 * jb.i + l16, 32 * kk, g4);
+        lds_frag_ch(fx, B.kc, 16 * jb.j + l16, kk, g4);
+        lds_frag_ch(fy, jb.kind == 0 ? B.nkr : B.qr, 16 * jb.i + l16, kk, g4);
       }
       mma(acc[u], fx, fy);
     }
@@ -232,7 +274,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   const int ts = lane >> 4, co = lane & 15;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int r0 = 16 * pw + 4 * ts;                    // this lane's first row in the chunk
-  const int pA = skpos(8 * co), pB = skpos(8 * co + 4);  // stored columns of the two channel quads
+  const int pA = chpos(8 * co), pB = chpos(8 * co + 4);  // stored columns of the two channel quads
 
   u32x4 Rq[4], Rk[4], Rv[4];   // 8 bf16 channels per token
   f32x4 Rg[4][2];              // 8 fp32 channels per token
@@ -291,7 +333,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   // to sm.flag[pw].
   auto digest_g = [&]() {
     bool ok = true;
-    float a[8], x[8], y[8];
+    float a[8], y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       a[i] = 0.f;
@@ -303,21 +345,15 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
         Gl[j][i] = a[i];
       }
     }
-    // inclusive scan over the four lanes (stride 16) that share a channel, all
-    // eight channels at once so the lane exchanges overlap
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = bperm(a[i], lane - 16);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = a[i] + (ts >= 1 ? y[i] : 0.f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = bperm(x[i], lane - 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] += ts >= 2 ? y[i] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = bperm(x[i], 48 + co);  // quarter total
+    // exclusive scan over the four lanes (rows) that share a channel: the pair's
+    // even row, then the total of rows 0,1 for rows 2,3
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float excl = x[i] - a[i];
+      float ev, od, lo, hi;
+      rows_of_pair(a[i], ev, od);
+      halves(ev + od, lo, hi);
+      y[i] = lo + hi;  // quarter total
+      const float excl = ((ts & 1) ? ev : 0.f) + (ts >= 2 ? lo : 0.f);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Gl[j][i] += excl;
     }
@@ -544,7 +580,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc_frag_sk(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1]);
+        for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], g4);
       // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16])
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
@@ -564,8 +600,8 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           Frag<bf16> xb, xq;
-          lds_frag_ck(xb, B.nkr, kLDK, 16 * s4 + l16, 32 * kk, g4);
-          lds_frag_ck(xq, B.qr, kLDK, 16 * s4 + l16, 32 * kk, g4);
+          lds_frag_ch(xb, B.nkr, 16 * s4 + l16, kk, g4);
+          lds_frag_ch(xq, B.qr, 16 * s4 + l16, kk, g4);
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
             mma(accY[c2][s4], xb, sf[c2][kk]);
@@ -626,7 +662,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16 *base = B.kc + skpos(16 * ct + 4 * (l16 & 3));
+          const bf16 *base = B.kc + chpos(16 * ct + 4 * (l16 & 3));
           const int r0 = 32 * kk + 4 * g4 + (l16 >> 2);
           const bf16x4 lo = lds_read_tr(base + r0 * kLDK);
           const bf16x4 hi = lds_read_tr(base + (r0 + 16) * kLDK);
