@@ -154,47 +154,36 @@ __device__ __forceinline__ f32x4 tn(const Split &b, const Split &c) {
 }
 
 // Gram jobs of producer wave P: (kind, row tile i, column tile j).
-// kind 0: -beta A tile (i > j) -> Lm;  1: P tile -> Pm;  2, 3: the diagonal tile
-// (i, i) of -beta A as [r][s] and as [s][r] (for the inverse).  Each wave owns
-// one diagonal block; the off-diagonal tiles are spread so a wave's tiles share
+// kind 0: -beta A tile (i >= j) -> Lm;  1: P tile -> Pm.  Each wave owns one
+// diagonal block; the off-diagonal tiles are spread so a wave's tiles share
 // operands.
 struct Job { int kind, i, j; };
-__device__ constexpr int kDiag[4] = {0, 3, 1, 2};  // diagonal block of each wave
-__device__ constexpr Job kJobs[4][6] = {
-    {{2, 0, 0}, {3, 0, 0}, {1, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}},
-    {{2, 3, 3}, {3, 3, 3}, {1, 3, 3}, {1, 2, 0}, {0, 3, 0}, {1, 3, 0}},
-    {{2, 1, 1}, {3, 1, 1}, {1, 1, 1}, {0, 2, 1}, {1, 2, 1}, {0, 3, 1}},
-    {{2, 2, 2}, {3, 2, 2}, {1, 2, 2}, {1, 3, 1}, {0, 3, 2}, {1, 3, 2}}};
+__device__ constexpr Job kJobs[4][5] = {
+    {{0, 0, 0}, {1, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}},
+    {{0, 3, 3}, {1, 3, 3}, {1, 2, 0}, {0, 3, 0}, {1, 3, 0}},
+    {{0, 1, 1}, {1, 1, 1}, {0, 2, 1}, {1, 2, 1}, {0, 3, 1}},
+    {{0, 2, 2}, {1, 2, 2}, {1, 3, 1}, {0, 3, 2}, {1, 3, 2}}};
 
-// Gram products of one window: -beta A into Lm and P into Pm, except this
-// wave's diagonal block of -beta A, returned in both orientations (dA[r][s],
-// dAT[s][r]) for its inverse.
+// Gram products of one window: -beta A into Lm and P into Pm.
 template <int P>
-__device__ __forceinline__ void gram(Buf &B, int l16, int g4, f32x4 &dA, f32x4 &dAT) {
-  f32x4 acc[6];
+__device__ __forceinline__ void gram(Buf &B, int l16, int g4) {
+  f32x4 acc[5];
 #pragma unroll
-  for (int u = 0; u < 6; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 5; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
+    for (int u = 0; u < 5; ++u) {
       const Job jb = kJobs[P][u];
+      // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
       Frag<bf16> fx, fy;
-      if (jb.kind == 2) {         // [r][s]: rows of nKr_i against Kc_i
-        lds_frag_ch(fx, B.nkr, 16 * jb.i + l16, kk, g4);
-        lds_frag_ch(fy, B.kc, 16 * jb.i + l16, kk, g4);
-      } else if (jb.kind == 3) {  // [s][r]
-        lds_frag_ch(fx, B.kc, 16 * jb.i + l16, kk, g4);
-        lds_frag_ch(fy, B.nkr, 16 * jb.i + l16, kk, g4);
-      } else {                    // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
-        lds_frag_ch(fx, B.kc, 16 * jb.j + l16, kk, g4);
-        lds_frag_ch(fy, jb.kind == 0 ? B.nkr : B.qr, 16 * jb.i + l16, kk, g4);
-      }
+      lds_frag_ch(fx, B.kc, 16 * jb.j + l16, kk, g4);
+      lds_frag_ch(fy, jb.kind == 0 ? B.nkr : B.qr, 16 * jb.i + l16, kk, g4);
       mma(acc[u], fx, fy);
     }
   }
 #pragma unroll
-  for (int u = 2; u < 6; ++u) {
+  for (int u = 0; u < 5; ++u) {
     const Job jb = kJobs[P][u];
     const int r = 16 * jb.i + l16;
     if (jb.kind == 0) {
@@ -208,23 +197,24 @@ __device__ __forceinline__ void gram(Buf &B, int l16, int g4, f32x4 &dA, f32x4 &
       store4<bf16>(B.pm + r * kLDC + skpos(16 * jb.j + 4 * g4), pv);
     }
   }
-  dA = acc[0];
-  dAT = acc[1];
 }
 
-// Diagonal block d of the triangular system from -beta A_dd (both
-// orientations, in the result layout: lane holds M[4 g4 + e][l16]):
-// X_dd = (I + N)^{-1} with N = beta A_dd strictly lower, into Lm,
+// In place on diagonal block d of Lm: -beta A_dd (its strictly lower part)
+// becomes X_dd = (I + N)^{-1}, N = beta A_dd.  In the result layout (lane holds
+// M[4 g4 + e][l16]):
 //   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0;
 // each power is paired with its transpose because the products are B^T C.
-__device__ __forceinline__ void inverse(Buf &B, int d, const f32x4 &dA, const f32x4 &dAT, int l16,
-                                        int g4) {
+__device__ __forceinline__ void inverse(Buf &B, int d, int l16, int g4) {
+  bf16 *blk = B.lm + 16 * d * kLDC + 16 * d;
+  // T[4 g4 + e][l16] by a transposing load; T^T[4 g4 + e][l16] = T[l16][4 g4 + e] directly
+  const bf16x4 t = lds_read_tr(blk + (4 * g4 + (l16 >> 2)) * kLDC + 4 * (l16 & 3));
+  const bf16x4 tt = *reinterpret_cast<const bf16x4 *>(blk + l16 * kLDC + 4 * g4);
   f32x4 N, NT;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int a = 4 * g4 + e;
-    N[e] = l16 < a ? -dA[e] : 0.f;
-    NT[e] = a < l16 ? -dAT[e] : 0.f;
+    N[e] = l16 < a ? -(float)t[e] : 0.f;
+    NT[e] = a < l16 ? -(float)tt[e] : 0.f;
   }
   const Split sN = split(N), sNT = split(NT);
   const f32x4 N2 = tn(sNT, sN), T2 = tn(sN, sNT);
@@ -244,8 +234,9 @@ __device__ __forceinline__ void inverse(Buf &B, int d, const f32x4 &dA, const f3
   const f32x4 P2 = P1 + tn(sP1T, sN4);
   const f32x4 P2T = P1T + tn(sN4, sP1T);
   const f32x4 Xd = P2 + tn(split(P2T), split(N8));
+  // every lane has read its operands before any writes (one wave, in order)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) B.lm[(16 * d + 4 * g4 + e) * kLDC + 16 * d + l16] = (bf16)Xd[e];
+  for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * kLDC + l16] = (bf16)Xd[e];
 }
 
 // ---------------------------------------------------------------- producers
@@ -284,8 +275,6 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   float gref[8], gend[8];      // reference and end of a 64-token window (chunk-relative)
   int blk = 0, win = 0;
   bool slow = false;
-  f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA;  // diagonal block awaiting its inverse
-  bool pend = false;
 
   const bf16 *qg = reinterpret_cast<const bf16 *>(p.q) + (int64_t)h * kD;
   const bf16 *kg = reinterpret_cast<const bf16 *>(p.k) + (int64_t)h * kD;
@@ -405,13 +394,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     const int Lc = (int)rows_of(blk);
     const int nwin = slow ? (Lc + 15) / 16 : 1;
     const bool last = win == nwin - 1;  // last window of the chunk
-    // ====================== phase 1: operands of window it, and the inverse of
-    // this wave's diagonal block of window it - 1 (its Gram products were the
-    // last phase's; the consumers read it in the next phase)
-    if (pend) {
-      inverse(sm.buf[(it + 1) & 1], kDiag[pw], dA, dAT, l16, g4);
-      pend = false;
-    }
+    // ====================== phase 1: operands of window it
     if (blk < nblk) {
       const int row_lo = slow ? 16 * win : 0;
       const int row_hi = slow ? (16 * win + 16 < Lc ? 16 * win + 16 : Lc) : Lc;
@@ -500,12 +483,11 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
       switch (pw) {
-        case 0: gram<0>(B, l16, g4, dA, dAT); break;
-        case 1: gram<1>(B, l16, g4, dA, dAT); break;
-        case 2: gram<2>(B, l16, g4, dA, dAT); break;
-        default: gram<3>(B, l16, g4, dA, dAT); break;
+        case 0: gram<0>(B, l16, g4); break;
+        case 1: gram<1>(B, l16, g4); break;
+        case 2: gram<2>(B, l16, g4); break;
+        default: gram<3>(B, l16, g4); break;
       }
-      pend = true;
       if (win == 0) {
         // v of this chunk for the consumers (their reads of the previous chunk's v
         // were in the phase before the last barrier)
@@ -566,7 +548,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   int it = 0;
   for (;; ++it) {
     f32x4 accY[2][4], accOT[2][4];
-    // ====================== phase 1: Y and O^T products
+    // ====================== phase 1: Y and O^T products, one diagonal inverse
     if (it > 0) {
       Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
       // bring the state to this window's scale
@@ -608,6 +590,8 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
             mma(accOT[c2][s4], sf[c2][kk], xq);
           }
         }
+      // diagonal block cw of the triangular system, for the next phase
+      inverse(B, cw, l16, g4);
     }
     block_sync();
     // ====================== phase 2: U, O, state update, o stores
