@@ -146,9 +146,13 @@ __device__ __forceinline__ Split split(const f32x4 &x) {
   return s;
 }
 __device__ __forceinline__ f32x4 tn(const Split &b, const Split &c) {
+  // Bh^T Ct + Bt^T Ch as one 32-deep product (the two 16-deep operand pairs
+  // side by side in each lane's 8 k-slots), then Bh^T Ch
+  Frag<bf16> x, y;
+  x.v = __builtin_shufflevector(b.h.v, b.t.v, 0, 1, 2, 3, 4, 5, 6, 7);
+  y.v = __builtin_shufflevector(c.t.v, c.h.v, 0, 1, 2, 3, 4, 5, 6, 7);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  mma16(acc, b.h, c.t);
-  mma16(acc, b.t, c.h);
+  mma(acc, x, y);
   mma16(acc, b.h, c.h);
   return acc;
 }
