@@ -677,7 +677,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
           const int r = 16 * k + l16;
           const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
           if (r >= row_lo)
-            buf_store_b128(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
+            buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
         }
       }
     }

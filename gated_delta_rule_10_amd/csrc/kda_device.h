@@ -167,6 +167,12 @@ __device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ void buf_store_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4 &v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kNonTemporal);
 }
+// The same through the caches (no streaming hint): partial lines written by
+// different waves can merge in L2 before they reach memory.
+__device__ __forceinline__ void buf_store_b128_cached(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                      const f32x4 &v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
 
 // Two consecutive elements of a row, widened to fp32.
 __device__ __forceinline__ f32x2 load2(const bf16 *p) {
