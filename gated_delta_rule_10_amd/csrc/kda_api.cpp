@@ -17,6 +17,8 @@ kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_SUCCESS : 
 
 // Shared checks of the prefill arguments; fills the token count on success.
 // The workspace query reads sizes only, so it skips the pointer checks.
+constexpr int32_t kMaxHeads = 65536;
+
 kda_status check_chunk_args(const kda_chunk_fwd_args *a, int64_t *total_tokens,
                             bool check_pointers) {
   if (!a) return KDA_ERROR_INVALID_VALUE;
@@ -37,8 +39,11 @@ kda_status check_chunk_args(const kda_chunk_fwd_args *a, int64_t *total_tokens,
     T = (int64_t)a->num_seqs * a->seq_len;
     if (T > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
   }
-  // every element offset must fit comfortably in 64-bit index math; tokens in int32
+  // tokens and (sequence, head) chains in int32; a 64-token chunk of one tensor
+  // (64 rows of H x 128 fp32) must stay below 2^32 bytes for the kernels'
+  // 32-bit buffer offsets
   if ((int64_t)a->num_seqs * a->num_heads > INT32_MAX / 2) return KDA_ERROR_INVALID_VALUE;
+  if (a->num_heads > kMaxHeads) return KDA_ERROR_INVALID_VALUE;
   if (T > 0 && check_pointers) {
     const void *req[] = {a->q, a->k, a->v, a->g, a->o};
     for (const void *p : req)

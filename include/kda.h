@@ -135,7 +135,8 @@ kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *args, size_t *
 
 /* Enqueue the prefill forward on `stream`.  Errors: KDA_ERROR_INVALID_VALUE for
  * null required pointers, negative sizes, misaligned pointers, cu_seqlens_host
- * that is not 0-based and non-decreasing, or T_total * H * 128 beyond 2^31;
+ * that is not 0-based and non-decreasing, T_total beyond 2^31 - 1 tokens,
+ * num_seqs * num_heads beyond 2^30 - 1, or num_heads beyond 65,536;
  * KDA_ERROR_UNSUPPORTED for head_dim != 128 or chunk_size != 64;
  * KDA_ERROR_WORKSPACE when the workspace is smaller than queried. */
 kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args, void *stream);
