@@ -677,14 +677,21 @@ __global__ __launch_bounds__(1024) void order_longest_first_kernel(const int32_t
 
 // Composition of segment transitions ([P3] section 4.1): for each chain, in
 // order, S_in[s + 1] = M_s S_in[s] + S~_s for s = 1 .. P_n - 2 (S_in[1] is the
-// final state of segment 0's run).  One workgroup of 256 threads per chain; each
-// thread owns an 8 x 8 block of the 128 x 128 product, fp32 throughout.
+// final state of segment 0's run).  Columns of the states compose independently,
+// so one workgroup of 256 threads takes 32 columns of one chain (four per
+// chain); each thread owns a 4 x 4 block of the 128 x 32 product, fp32
+// throughout.
+constexpr int kCombineCols = 32;
 __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkParams p) {
   constexpr int kK = 16;  // reduction slice staged in LDS
-  __shared__ __attribute__((aligned(16))) float Ms[kK][kD];  // M[:, k0 + kk] by row
-  __shared__ __attribute__((aligned(16))) float Bs[kK][kD];  // S_in[k0 + kk, :]
-  const int64_t chain = blockIdx.x;
-  const int n = (int)(chain / p.H);
+  constexpr int NB = kD / kCombineCols;
+  __shared__ __attribute__((aligned(16))) float Ms[kK][kD];            // M[:, k0 + kk] by row
+  __shared__ __attribute__((aligned(16))) float Bs[kK][kCombineCols];  // S_in[k0 + kk, cols]
+  const int crank = p.chain0 + (int)(blockIdx.x / NB);
+  const int cb = (int)(blockIdx.x % NB) * kCombineCols;
+  const int srank = crank / p.H;
+  const int n = p.order ? p.order[srank] : srank;
+  const int64_t chain = (int64_t)n * p.H + (crank - srank * p.H);
   int64_t len = p.seq_len;
   if (p.cu) {
     const int64_t a = p.cu[n], b = p.cu[n + 1];
@@ -694,44 +701,46 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkParams p) {
   }
   const int pn = seg_count(p.seg_P, (int)((len + kC - 1) / kC));
   const int t = threadIdx.x;
-  const int r0 = (t >> 4) * 8, c0 = (t & 15) * 8;
+  const int r0 = (t >> 3) * 4, c0 = (t & 7) * 4;  // rows r0 .. r0+3, columns cb + c0 .. +3
   for (int sg = 1; sg + 2 <= pn; ++sg) {
     const float *M = seg_state(p, chain, kM, sg);
     const float *B = seg_state(p, chain, kSin, sg);
     const float *St = seg_state(p, chain, kSt, sg);
     float *out = seg_state(p, chain, kSin, sg + 1);
-    float acc[8][8];
+    float acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = St[(r0 + i) * kD + c0 + j];
+      for (int j = 0; j < 4; ++j) acc[i][j] = St[(r0 + i) * kD + cb + c0 + j];
     for (int k0 = 0; k0 < kD; k0 += kK) {
       __syncthreads();
       for (int e = t; e < kK * kD; e += 256) {
         const int kk = e & (kK - 1), r = e / kK;  // M row r, column k0 + kk
         Ms[kk][r] = M[r * kD + k0 + kk];
-        const int br = e / kD, bc = e & (kD - 1);
-        Bs[br][bc] = B[(k0 + br) * kD + bc];
+      }
+      for (int e = t; e < kK * kCombineCols; e += 256) {
+        const int br = e / kCombineCols, bc = e % kCombineCols;
+        Bs[br][bc] = B[(k0 + br) * kD + cb + bc];
       }
       __syncthreads();
 #pragma unroll 4
       for (int kk = 0; kk < kK; ++kk) {
-        float a[8], b[8];
+        float a[4], b[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = Ms[kk][r0 + i];
+        for (int i = 0; i < 4; ++i) a[i] = Ms[kk][r0 + i];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = Bs[kk][c0 + j];
+        for (int j = 0; j < 4; ++j) b[j] = Bs[kk][c0 + j];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) out[(r0 + i) * kD + c0 + j] = acc[i][j];
-    __syncthreads();  // S_in[sg + 1] complete before the next step reads it
+      for (int j = 0; j < 4; ++j) out[(r0 + i) * kD + cb + c0 + j] = acc[i][j];
+    __syncthreads();  // this block of S_in[sg + 1] complete before the next step reads it
   }
 }
 
@@ -761,10 +770,29 @@ kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
     maxlen = a.seq_len;
   }
   pl.max_chunks = (maxlen + KDA_CHUNK - 1) / KDA_CHUNK;
-  // segments per sequence: explicit, or 1 in automatic mode (splitting a chain
-  // repeats its chunk-local work in two passes, which the measured runs never
-  // recovered from the extra CUs)
+  // segments per sequence: explicit, or chosen in automatic mode (bf16 only).
+  // A split repeats the chunk-local work of the transition items, so it only
+  // pays where chains would otherwise leave compute units idle: with C <= U
+  // chains on U units, every chain is split into three segments with shares
+  // 2:1:1; the first pass (the runs of segment 0 and the two transitions of
+  // segment 1, 3C workgroups whose short ones finish in time for the rest) and
+  // the second (segments 1 and 2) then take about 3/4 of an unsplit chain
+  // (measured: 65,536 tokens x 96 heads, 5.16 -> 4.06 ms).  For U < C < 2U
+  // splitting the chains past the first U measured no gain: a chain alone on
+  // a less busy device already runs ~20% faster than in a full round.
   int64_t P = a.segments > 1 ? a.segments : 1;
+  pl.seg_front = false;
+  const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
+  if (a.segments == 0 && a.io_dtype == KDA_BF16 && pl.max_chunks >= 8) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 0;
+    if (cus > 0 && chains <= cus) {
+      P = 3;
+      pl.seg_front = true;
+    }
+  }
   if (P > kMaxSegments) P = kMaxSegments;
   if (P > pl.max_chunks) P = pl.max_chunks < 1 ? 1 : pl.max_chunks;
   pl.segments = (int32_t)P;
@@ -816,25 +844,30 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
                                   : launch_typed<float, 64>(p, items, stream);
   };
   p.seg_P = plan.segments;
+  p.seg_front = plan.seg_front ? 1 : 0;
   p.ws = nullptr;
+  p.chain0 = 0;
+  p.nchains = (int32_t)chains;
   if (plan.segments <= 1) {
     p.pass = 0;
     return run(chains * VS);
   }
   // segmented: first pass (segment 0 runs; transitions of segments 1 .. P-2),
   // composition, second pass (segments 1 .. P-1 from their exact incoming states)
+  hipError_t e = hipSuccess;
   p.ws = reinterpret_cast<float *>((char *)a.workspace + plan.seg_state_off);
   const int P = plan.segments;
   p.pass = 1;
-  hipError_t e = run(chains * (2 * P - 3) * VS);
+  e = run(p.nchains * (int64_t)(2 * P - 3) * VS);
   if (e != hipSuccess) return e;
   if (P > 2) {
-    hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)chains), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)p.nchains * (kD / kCombineCols)),
+                       dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   p.pass = 2;
-  return run(chains * (P - 1) * VS);
+  return run(p.nchains * (int64_t)(P - 1) * VS);
 }
 
 }  // namespace kda

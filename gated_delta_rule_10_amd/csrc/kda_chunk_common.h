@@ -29,6 +29,12 @@ struct ChunkParams {
   int32_t seg_P;
   int32_t pass;
   float *ws;             // [N H][3 seg_P][128 x 128] fp32 segment states
+  // chains of this launch: ranks chain0 .. chain0 + nchains - 1 in the
+  // (sequence rank, head) order; seg_front: segment 0 takes two shares of the
+  // chunks, the others one each (the first pass's runs then last as long as
+  // two rounds of its transition items)
+  int32_t chain0, nchains;
+  int32_t seg_front;
 };
 
 // Segment items ("Kimi K3 -- Training and Infrastructure Notes", section 4.1):
@@ -37,8 +43,8 @@ struct ChunkParams {
 enum SegMode { kRun = 0, kTrackM = 1, kTrackS = 2 };
 enum SegKind { kSin = 0, kM = 1, kSt = 2 };  // workspace state kinds
 
-// Segment p of a sequence of nch chunks (P_n segments) covers chunks
-// [p nch / P_n, (p + 1) nch / P_n).
+// A sequence of nch chunks is split into P_n = min(P, nch) segments of whole
+// chunks (equal shares, or two shares for segment 0, see seg_bounds).
 __device__ __forceinline__ int seg_count(int P, int nch) {
   const int pn = P < nch ? P : nch;
   return pn < 1 ? 1 : pn;
@@ -59,15 +65,27 @@ struct ChunkItem {
   bool write_o, zero_v, skip;
 };
 
-// blockIdx.x = ((sequence rank * H + head) * items + segment item) * VS + value block.
+// Chunks [lo, hi) of segment seg of a sequence of nch chunks split into pn.
+__device__ __forceinline__ void seg_bounds(const ChunkParams &p, int seg, int pn, int nch,
+                                           int &lo, int &hi) {
+  if (p.seg_front) {  // shares 2, 1, 1, ...
+    lo = seg == 0 ? 0 : (int)((int64_t)(seg + 1) * nch / (pn + 1));
+    hi = (int)((int64_t)(seg + 2) * nch / (pn + 1));
+  } else {
+    lo = (int)((int64_t)seg * nch / pn);
+    hi = (int)((int64_t)(seg + 1) * nch / pn);
+  }
+}
+
+// blockIdx.x = (segment item * nchains + chain rank - chain0) * VS + value
+// block: item-major, so a pass's long runs (item 0) are dispatched first.
 __device__ __forceinline__ ChunkItem decode_item(const ChunkParams &p, int VS) {
   ChunkItem r;
-  const int items = p.pass == 1 ? 2 * p.seg_P - 3 : (p.pass == 2 ? p.seg_P - 1 : 1);
   const int item = blockIdx.x;
   r.vs = item % VS;
   const int cit = item / VS;
-  const int it = cit % items;
-  const int crank = cit / items;
+  const int it = cit / p.nchains;
+  const int crank = p.chain0 + (cit - it * p.nchains);
   const int srank = crank / p.H;
   r.h = crank - srank * p.H;
   const int n = p.order ? p.order[srank] : srank;
@@ -94,8 +112,8 @@ __device__ __forceinline__ ChunkItem decode_item(const ChunkParams &p, int VS) {
     const int pn = seg_count(p.seg_P, nch_all);
     // trackers exist for the segments 1 .. P_n - 2, runs for 0 .. P_n - 1
     r.skip = mode == kRun ? seg >= pn : seg >= pn - 1;
-    const int c_lo = (int)((int64_t)seg * nch_all / pn);
-    const int c_hi = (int)((int64_t)(seg + 1) * nch_all / pn);
+    int c_lo, c_hi;
+    seg_bounds(p, seg, pn, nch_all, c_lo, c_hi);
     const int64_t t_lo = (int64_t)c_lo * kC;
     const int64_t t_hi = (int64_t)c_hi * kC < len ? (int64_t)c_hi * kC : len;
     bos += t_lo;

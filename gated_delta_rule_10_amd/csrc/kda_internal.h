@@ -26,6 +26,7 @@ struct ChunkPlan {
   int64_t total_tokens = 0;
   bool varlen = false;
   int32_t segments = 1;          // segments per sequence (1 = no split)
+  bool seg_front = false;        // segment 0 takes two shares of the chunks
   int64_t max_chunks = 0;        // chunks of the longest sequence
   // workspace layout (byte offsets)
   size_t order_off = 0, order_bytes = 0;      // int32 [N] longest-first sequence order

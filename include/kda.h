@@ -99,7 +99,10 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * parallel, the transitions are composed in order, and every segment is then
  * run from its exact incoming state.  The result is the same recurrence up to
  * rounding.  The workspace holds 3 x segments fp32 states per (sequence,
- * head).  segments = 0 lets the library choose (currently: no split).
+ * head).  segments = 0 lets the library choose: for bf16 I/O, sequences of
+ * at least 8 chunks and no more num_seqs * num_heads chains than the current
+ * device has compute units, every sequence is split into three segments whose
+ * first one takes half of the chunks; otherwise no split.
  * ---------------------------------------------------------------------- */
 typedef struct kda_chunk_fwd_args {
   int32_t num_seqs;               /* N >= 1                                              */
@@ -130,7 +133,8 @@ typedef struct kda_chunk_fwd_args {
 } kda_chunk_fwd_args;
 
 /* Bytes of workspace kda_chunk_fwd needs for these arguments (pointers are not
- * read; only sizes, cu_seqlens_host and segments).  Host only, no HIP call. */
+ * read; only sizes, cu_seqlens_host and segments).  Host only: no GPU work; in
+ * automatic mode it reads the current device's compute-unit count. */
 kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *args, size_t *bytes);
 
 /* Enqueue the prefill forward on `stream`.  Errors: KDA_ERROR_INVALID_VALUE for
