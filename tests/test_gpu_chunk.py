@@ -163,6 +163,29 @@ def test_segments_match_oracle(kda, dtype, segments):
     check_chains(inp, o, sf, chains, inp["dtype"], scale=0.9)
 
 
+def test_automatic_split_matches_oracle(kda):
+    """Automatic mode on a batch that leaves compute units idle splits every
+    sequence of at least 8 chunks into three segments with shares 2:1:1; the
+    outputs match the token loop and the unsplit run (short sequences, an empty
+    one and ragged ends are mixed in)."""
+    announce("chunk automatic split")
+    lens = (1000, 17, 0, 513, 4100, 64)
+    cfg = ki.PrefillConfig("t", lens, 2, "bf16", init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=37)
+    ws_auto = kda.chunk_fwd_workspace_size(inp["q"], num_seqs=len(lens),
+                                           cu_seqlens_host=inp["cu_seqlens_host"], segments=0)
+    ws_one = kda.chunk_fwd_workspace_size(inp["q"], num_seqs=len(lens),
+                                          cu_seqlens_host=inp["cu_seqlens_host"], segments=1)
+    assert ws_auto > ws_one  # the split's segment states are in the workspace
+    o0, s0 = run(kda, inp, segments=0)
+    o1, s1 = run(kda, inp, segments=1)
+    torch.cuda.synchronize()
+    chains = [(n, h) for n in range(len(lens)) for h in range(2)]
+    check_chains(inp, o0, s0, chains, torch.bfloat16)
+    assert rel_err(to64(o0), to64(o1)) <= TOL[torch.bfloat16]
+    assert rel_err(to64(s0), to64(s1)) <= TOL[torch.bfloat16]
+
+
 def test_segments_fixed_batch_without_initial_state(kda):
     announce("chunk segments fixed batch")
     cfg = ki.PrefillConfig("t", (777, 777), 4, "bf16")
