@@ -27,6 +27,8 @@ __all__ = [
     "chunked",
     "decode_step",
     "transition",
+    "lowerbound_gate",
+    "sigmoid",
     "max_threads",
     "load",
     "open_library",
@@ -82,9 +84,14 @@ def open_library(path):
     lib.kda_oracle_transition.argtypes = [
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, _DP, _DP, _DP,
     ]
+    lib.kda_oracle_lowerbound_gate.argtypes = [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, ctypes.c_double, _DP,
+    ]
+    lib.kda_oracle_sigmoid.argtypes = [ctypes.c_int64, _DP, _DP]
     lib.kda_oracle_max_threads.argtypes = []
     for fn in ("kda_oracle_recurrent", "kda_oracle_chunked", "kda_oracle_decode_step",
-               "kda_oracle_transition", "kda_oracle_max_threads"):
+               "kda_oracle_transition", "kda_oracle_lowerbound_gate", "kda_oracle_sigmoid",
+               "kda_oracle_max_threads"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -209,6 +216,43 @@ def transition(k, v, g, beta):
                                    _ptr(M), _ptr(St))
     _check(rc, "kda_oracle_transition")
     return M, St
+
+
+def lowerbound_gate(x, A_log, dt_bias=None, lower_bound=-5.0):
+    """K3's lower-bounded gate: g = lower_bound * sigmoid(exp(A_log[h]) * (x + dt_bias[h])).
+
+    x: [..., H, K] raw gate logits; A_log: [H]; dt_bias: [H, K] (or anything of
+    H*K values) or None.  Returns fp64 g of x's shape.
+    """
+    lib = load()
+    x = _f64(x, "x")
+    if x.ndim < 2:
+        raise ValueError("x must be [..., H, K]")
+    H, K = x.shape[-2:]
+    A = _f64(A_log, "A_log").reshape(-1)
+    if A.shape != (H,):
+        raise ValueError(f"A_log must hold {H} values")
+    dt = _f64(dt_bias, "dt_bias")
+    if dt is not None:
+        dt = np.ascontiguousarray(dt.reshape(-1))
+        if dt.shape != (H * K,):
+            raise ValueError(f"dt_bias must hold {H * K} values")
+    T = x.size // (H * K)
+    g = np.empty_like(x)
+    rc = lib.kda_oracle_lowerbound_gate(T, H, K, _ptr(x), _ptr(A), _ptr(dt),
+                                        float(lower_bound), _ptr(g))
+    _check(rc, "kda_oracle_lowerbound_gate")
+    return g
+
+
+def sigmoid(x):
+    """beta from beta logits: 1 / (1 + exp(-x)), elementwise, fp64."""
+    lib = load()
+    x = _f64(x, "x")
+    y = np.empty_like(x)
+    rc = lib.kda_oracle_sigmoid(x.size, _ptr(x), _ptr(y))
+    _check(rc, "kda_oracle_sigmoid")
+    return y
 
 
 def max_threads() -> int:

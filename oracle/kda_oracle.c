@@ -23,7 +23,12 @@
  *  [P4] "Kimi K3: a 2.8T open model ...", section "Kimi Delta Attention:
  *       constant-size memory over a million tokens" (same equation) and
  *       subsection "FlashKDA: the equation, shipped as a kernel" (optional state
- *       in and out, variable-length batches through cumulative sequence lengths).
+ *       in and out, variable-length batches through cumulative sequence lengths;
+ *       beta arrives as logits that pass through a sigmoid).
+ *  [P1] section "How KDA updates its state", the part on how the decay logit
+ *       becomes a decay: K3's lower-bounded gate (flash-linear-attention's
+ *       gate.py) turns a raw per-channel gate logit into a log-decay in
+ *       (lower_bound, 0); lower_bound defaults to -5.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - No query scale appears in any formula; `scale` multiplies o and the pages'
@@ -318,6 +323,40 @@ int kda_oracle_transition(int64_t T, int K, int V, const double *k, const double
   if (S_tilde) memcpy(S_tilde, S, sizeof(double) * K * V);
   free(Mt);
   free(S);
+  return KDA_ORACLE_OK;
+}
+
+/*
+ * K3's lower-bounded gate ([P1] section "How KDA updates its state"), elementwise over tokens t,
+ * heads h and key channels c of x [T, H, K]:
+ *   g[t,h,c] = lower_bound * sigmoid(exp(A_log[h]) * (x[t,h,c] + dt_bias[h,c]))
+ * with sigmoid(z) = 1 / (1 + exp(-z)).  A_log: [H]; dt_bias: [H, K] or NULL
+ * (no bias).  g may equal x (in place).
+ */
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+int kda_oracle_lowerbound_gate(int64_t T, int H, int K, const double *x, const double *A_log,
+                               const double *dt_bias, double lower_bound, double *g) {
+  if (T < 0 || H <= 0 || K <= 0 || !A_log || (T > 0 && (!x || !g))) return KDA_ORACLE_EINVAL;
+  for (int64_t t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      const double a = exp(A_log[h]);
+      for (int c = 0; c < K; ++c) {
+        const size_t i = ((size_t)t * H + h) * K + c;
+        const double z = x[i] + (dt_bias ? dt_bias[(size_t)h * K + c] : 0.0);
+        g[i] = lower_bound * sigmoid(a * z);
+      }
+    }
+  return KDA_ORACLE_OK;
+}
+
+/*
+ * beta from its logits ([P4] subsection "FlashKDA: the equation, shipped as a
+ * kernel": beta logits pass through a sigmoid), elementwise over n values.
+ */
+int kda_oracle_sigmoid(int64_t n, const double *x, double *y) {
+  if (n < 0 || (n > 0 && (!x || !y))) return KDA_ORACLE_EINVAL;
+  for (int64_t i = 0; i < n; ++i) y[i] = sigmoid(x[i]);
   return KDA_ORACLE_OK;
 }
 

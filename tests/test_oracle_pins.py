@@ -11,7 +11,12 @@ Pages (cited by title and section):
   [P2] "Kimi K3: Open Frontier Intelligence", section 6 (the KDA equation).
   [P3] "Kimi K3 -- Training and Infrastructure Notes", section 4.1 (segment
        transition M and zero-start state S~ compose exactly).
-  [P4] "Kimi K3: a 2.8T open model ...", "Kimi Delta Attention" (same equation).
+  [P4] "Kimi K3: a 2.8T open model ...", "Kimi Delta Attention" (same equation);
+       "FlashKDA: the equation, shipped as a kernel" (beta logits pass through a
+       sigmoid).
+  The lower-bounded gate: [P1] "How KDA updates its state" (K3's gate from
+  flash-linear-attention's gate.py: g = lower_bound * sigmoid(exp(A_log) *
+  (x + dt_bias)), so g stays in (lower_bound, 0) and exp(g) above exp(-5)).
 """
 import json
 import math
@@ -312,6 +317,93 @@ def test_decode_steps_equal_token_loop():
     assert np.all(np.isnan(np.array(outs)[:, 2]))
 
 
+# ------------------------------------------------ gate and beta front end
+def _gate_case(rng, T=5, H=3, K=4):
+    return (rng.standard_normal((T, H, K)), rng.standard_normal(H) * 0.7,
+            rng.standard_normal((H, K)))
+
+
+def test_gate_zero_argument_gives_half_the_bound():
+    """sigmoid(0) = 1/2 exactly: with x = -dt_bias[h, c] every g is lower_bound / 2
+    whatever A_log is (pins the bias indexing [h, c] against a transposed read)."""
+    rng = np.random.default_rng(11)
+    T, H, K = 4, 3, 5
+    dt = rng.standard_normal((H, K))
+    x = np.broadcast_to(-dt, (T, H, K)).copy()
+    A = rng.standard_normal(H) * 2.0
+    for lb in (-5.0, -1.25):
+        g = oracle.lowerbound_gate(x, A, dt, lb)
+        assert np.array_equal(g, np.full((T, H, K), lb / 2))
+
+
+def test_gate_closed_form_per_head():
+    """With x + dt_bias = 1 and A_log[h] = ln(ln m_h), the gate's argument is ln m_h and
+    sigmoid(ln m) = m / (1 + m): g = lower_bound m_h / (1 + m_h), a different exact
+    value per head (pins exp(A_log) rather than A_log, the head index and the sign
+    inside the sigmoid)."""
+    rng = np.random.default_rng(12)
+    T, H, K = 3, 4, 6
+    m = np.array([2.0, 3.0, 5.0, 9.0])
+    A = np.log(np.log(m))
+    dt = rng.standard_normal((H, K))
+    x = 1.0 - dt[None]
+    x = np.broadcast_to(x, (T, H, K)).copy()
+    lb = -5.0
+    g = oracle.lowerbound_gate(x, A, dt, lb)
+    want = lb * m / (1.0 + m)
+    np.testing.assert_allclose(g, np.broadcast_to(want[None, :, None], g.shape),
+                               rtol=1e-14, atol=0)
+
+
+def test_gate_reflection_sums_to_the_bound():
+    """sigmoid(z) + sigmoid(-z) = 1, so reflecting x + dt_bias about zero maps g to
+    lower_bound - g."""
+    rng = np.random.default_rng(13)
+    x, A, dt = _gate_case(rng)
+    xr = -x - 2.0 * dt[None]  # (xr + dt) = -(x + dt)
+    g1 = oracle.lowerbound_gate(x, A, dt, -5.0)
+    g2 = oracle.lowerbound_gate(xr, A, dt, -5.0)
+    np.testing.assert_allclose(g1 + g2, -5.0, rtol=0, atol=1e-14)
+
+
+def test_gate_range_limits_and_page_floor():
+    """[P1]: g lies between the bound and 0, so exp(g) stays above exp(-5) ~ 0.0067
+    (printed); large positive logits reach the bound, large negative ones 0, and
+    g falls as the logit rises."""
+    c = json.load(open(GOLDEN))["decay_floor"]
+    lb = c["gate_lower_bound"]
+    x = np.linspace(-8.0, 8.0, 161).reshape(161, 1, 1) * np.ones((1, 2, 3))
+    A = np.array([0.0, 0.5])
+    g = oracle.lowerbound_gate(x, A, None, lb)
+    assert np.all(g > lb) and np.all(g < 0.0)
+    assert np.all(np.diff(g, axis=0) < 0.0)
+    assert float(np.exp(g).min()) >= c["alpha_floor_printed"] - c["printed_digits_tol"]
+    far = oracle.lowerbound_gate(np.array([[[60.0, -60.0]]]), np.array([0.0]), None, lb)
+    assert far[0, 0, 0] == lb and -1e-25 < far[0, 0, 1] < 0.0
+    # A_log -> -inf: exp(A_log) = 0 and every g is the bound's half
+    flat = oracle.lowerbound_gate(x, np.array([-np.inf, -np.inf]), None, lb)
+    assert np.array_equal(flat, np.full_like(flat, lb / 2))
+
+
+def test_gate_without_bias_equals_zero_bias():
+    rng = np.random.default_rng(14)
+    x, A, dt = _gate_case(rng)
+    np.testing.assert_array_equal(oracle.lowerbound_gate(x, A, None, -5.0),
+                                  oracle.lowerbound_gate(x, A, np.zeros_like(dt), -5.0))
+
+
+def test_beta_sigmoid_values():
+    """sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4 and 1/4; the library's logistic
+    function agrees to rounding."""
+    from scipy.special import expit
+    y = oracle.sigmoid(np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0]))
+    np.testing.assert_allclose(y[:3], [0.5, 0.75, 0.25], rtol=1e-15, atol=0)
+    assert y[3] == 1.0 or abs(y[3] - 1.0) < 1e-17
+    assert 0.0 < y[4] < 1e-17
+    z = np.random.default_rng(15).standard_normal((7, 3)) * 4.0
+    np.testing.assert_allclose(oracle.sigmoid(z), expit(z), rtol=1e-15, atol=0)
+
+
 # ------------------------------------------- planted mistakes must be caught
 def _pins_pass():
     """Run a compact set of the pins above; True if all hold."""
@@ -357,6 +449,53 @@ MUTANTS = {
     "erase_with_query": lambda s: s.replace(
         "const double bk = beta * k[i];", "const double bk = beta * q[i];"),
 }
+
+
+def _gate_pins_pass():
+    checks = [test_gate_zero_argument_gives_half_the_bound, test_gate_closed_form_per_head,
+              test_gate_range_limits_and_page_floor, test_beta_sigmoid_values]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+GATE_MUTANTS = {
+    # A_log used without its exponential
+    "gate_no_exp": lambda s: s.replace("const double a = exp(A_log[h]);",
+                                       "const double a = A_log[h];"),
+    # sign inside the sigmoid flipped
+    "sigmoid_sign": lambda s: s.replace("return 1.0 / (1.0 + exp(-z));",
+                                        "return 1.0 / (1.0 + exp(z));"),
+    # bias read as [c, h] instead of [h, c]
+    "gate_bias_transposed": lambda s: s.replace("dt_bias[(size_t)h * K + c]",
+                                                "dt_bias[(size_t)c * H + h]"),
+    # bias added outside the scale
+    "gate_bias_unscaled": lambda s: s.replace("lower_bound * sigmoid(a * z);",
+                                              "lower_bound * sigmoid(a * x[i] + (z - x[i]));"),
+    # every head given head 0's A_log
+    "gate_head0": lambda s: s.replace("const double a = exp(A_log[h]);",
+                                      "const double a = exp(A_log[0]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
+def test_gate_pins_catch_planted_mistake(name, tmp_path):
+    """Plausible mistakes in the gate and beta front end, planted in a copy of the
+    oracle on the CPU, each fail one of the gate pins."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(SOURCE).read()
+    mutated = GATE_MUTANTS[name](src)
+    assert mutated != src, "mutation did not apply"
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(mutated)
+    lib_path = build_oracle(str(path), str(tmp_path / f"libmut_{name}.so"))
+    assert _gate_pins_pass(), "unmodified oracle must pass the gate pins"
+    with oracle.using(oracle.open_library(lib_path)):
+        assert not _gate_pins_pass(), f"planted mistake '{name}' was not caught"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
