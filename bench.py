@@ -6,6 +6,11 @@ before the timed region.  The recurrent decode workload (512 sequences x 96
 heads, fp32 states in HBM, 1000 in-place steps) is timed after it and reported
 in the same JSON line.
 
+With --front gate the prefill reads raw gate logits (fp32, in place of g), per-head
+A_log and per-channel dt_bias, and beta logits, and applies K3's lower-bounded gate
+and the beta sigmoid in the kernel ("How Kimi K3 Engineered Its Way to the
+Frontier", section "How KDA updates its state"); the byte count is the same.
+
 Algorithmic accounting (fixed; it does not depend on the implementation):
   prefill FLOP per token-head = 6 d^2 + C (3 d + 2 d) = 139,264   (d = 128, C = 64)
   prefill bytes per token-head = q, k, v, o in bf16 (4 x 256) + g fp32 (512) + beta (4)
@@ -55,6 +60,12 @@ def parse():
     ap.add_argument("--workload", default=PREFILL_WORKLOAD)
     ap.add_argument("--segments", type=int, default=0,
                     help="segments per sequence (0 = the library's automatic choice)")
+    ap.add_argument("--gate-params", choices=("matched", "heavy"), default="matched",
+                    help="gate parameter set for --front gate (see kda_inputs.GATE_PARAM_SETS)")
+    ap.add_argument("--front", choices=("logdecay", "gate"), default="logdecay",
+                    help="prefill inputs: log-decay g and beta (default), or gate logits "
+                         "with A_log, dt_bias and beta logits (the lower-bounded gate and "
+                         "the beta sigmoid computed in the kernel)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from rocprofv3 --pmc FETCH_SIZE and "
                          "WRITE_SIZE counter_collection.csv files (taken with "
@@ -62,10 +73,16 @@ def parse():
     return ap.parse_args()
 
 
-def time_prefill(kda, ki, workload, steps, warmup, segments=0):
+def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
+                 gate_params="matched"):
     import torch
     cfg = ki.CONFIGS[workload]
-    x = ki.make_prefill(cfg, device="cuda", seed=1002)
+    gate = front == "gate"
+    x = ki.make_prefill(cfg, device="cuda", seed=1002, gate_logits=gate, beta_logits=gate)
+    gp = (ki.make_gate_params(x["heads"], device="cuda", seed=1009,
+                              **ki.GATE_PARAM_SETS[gate_params]) if gate else {})
+    fkw = dict(A_log=gp.get("A_log"), dt_bias=gp.get("dt_bias"), lower_bound=-5.0,
+               beta_logits=gate)
     N, H = len(x["lengths"]), x["heads"]
     varlen = cfg.varlen
     o = torch.empty_like(x["q"])
@@ -80,7 +97,7 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0):
                       cu_seqlens=x["cu_seqlens"] if varlen else None,
                       cu_seqlens_host=x["cu_seqlens_host"] if varlen else None,
                       initial_state=x["initial_state"], num_seqs=N, out=o, final_state=sf,
-                      workspace=ws, segments=segments)
+                      workspace=ws, segments=segments, **fkw)
 
     for _ in range(warmup):
         step()
@@ -96,7 +113,8 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0):
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
     tokens = x["q"].shape[0]
-    res = dict(ms=ms, wall_s=wall, tokens=tokens, heads=H, seqs=N, x=x, cfg=cfg)
+    res = dict(ms=ms, wall_s=wall, tokens=tokens, heads=H, seqs=N, x=x, cfg=cfg,
+               gate_params=gp if gate else None)
     return res
 
 
@@ -131,11 +149,13 @@ def time_decode(kda, ki, steps, warmup=10):
                 bytes_per_step=heads * DECODE_BYTES_PER_HEAD, batch=cfg.batch, heads=cfg.heads)
 
 
-def cpu_baseline(x, chains_per_core, seconds):
+def cpu_baseline(x, chains_per_core, seconds, gp=None):
     """Time the fp64 oracle on a bounded sample of the same workload's chains.
 
     The sample (cores x chains_per_core whole (sequence, head) chains) is run
-    repeatedly until `seconds` of wall time have passed; the rate is the mean."""
+    repeatedly until `seconds` of wall time have passed; the rate is the mean.
+    With gate parameters `gp` the oracle's gate and beta sigmoid run inside the
+    timed loop too."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
@@ -152,11 +172,21 @@ def cpu_baseline(x, chains_per_core, seconds):
     cu2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     cat = lambda xs: np.concatenate(xs, axis=0)[:, None]
     args = (cat(qs), cat(ks), cat(vs), cat(gs), np.concatenate(bs)[:, None])
+    if gp is not None:
+        A_np, dt_np = to(gp["A_log"]), to(gp["dt_bias"])
     oracle.load()
     threads = min(cores, oracle.max_threads(), nchains)
     passes, t0 = 0, time.perf_counter()
     while True:
-        oracle.recurrent(*args, cu_seqlens=cu2, nthreads=threads)
+        if gp is not None:  # per token: the gate of its chain's head, then the loop
+            g = np.empty_like(args[3])
+            for i, (n, h) in enumerate(chains):
+                g[cu2[i]:cu2[i + 1]] = oracle.lowerbound_gate(
+                    args[3][cu2[i]:cu2[i + 1]], A_np[h:h + 1], dt_np[h:h + 1], -5.0)
+            run = (*args[:3], g, oracle.sigmoid(args[4]))
+        else:
+            run = args
+        oracle.recurrent(*run, cu_seqlens=cu2, nthreads=threads)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
@@ -173,7 +203,10 @@ PREFILL_KERNEL = "chunk_fwd_pipe_kernel"
 PREFILL_SOURCES = ["gated_delta_rule_10_amd/csrc/kda_chunk_pipe.hip",
                    "gated_delta_rule_10_amd/csrc/kda_chunk_common.h",
                    "gated_delta_rule_10_amd/csrc/kda_device.h"]
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_b4_t8192_h96_traffic.json")
+TRAFFIC_RECORDS = {
+    "logdecay": os.path.join(ROOT, "profiles", "chunk_fwd_bf16_b4_t8192_h96_traffic.json"),
+    "gate": os.path.join(ROOT, "profiles", "chunk_fwd_gate_bf16_b4_t8192_h96_traffic.json"),
+}
 
 
 def sources_digest(files):
@@ -184,12 +217,13 @@ def sources_digest(files):
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, front="logdecay"):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE readings,
     or None when they were taken on other kernel sources or another workload."""
-    if not os.path.exists(TRAFFIC_RECORD):
+    path = TRAFFIC_RECORDS[front]
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_RECORD))
+    rec = json.load(open(path))
     if sources_digest(rec["sources"]) != rec["source_sha256"] or rec["workload"] != workload:
         return None
     return rec["traffic_bytes"]
@@ -200,7 +234,7 @@ def copy_bytes_for(mib, heads=96):
     return max(1, (mib << 20) // (heads * D * D * 4)) * heads * D * D * 4
 
 
-def record_traffic(fetch_csv, write_csv, workload, mib):
+def record_traffic(fetch_csv, write_csv, workload, mib, front="logdecay"):
     """Scale the prefill kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
     what the same counters read for the state-pool copy of known size, and store
     the result with a digest of the kernel's sources."""
@@ -224,7 +258,8 @@ def record_traffic(fetch_csv, write_csv, workload, mib):
     wscale = copy_bytes / 1024 / (sum(w["copy"]) / len(w["copy"]))
     fk = sum(f["prefill"]) / len(f["prefill"])
     wk = sum(w["prefill"]) / len(w["prefill"])
-    rec = {"kernel": PREFILL_KERNEL, "workload": workload, "sources": PREFILL_SOURCES,
+    rec = {"kernel": PREFILL_KERNEL, "workload": workload, "front": front,
+           "sources": PREFILL_SOURCES,
            "source_sha256": sources_digest(PREFILL_SOURCES),
            "fetch_size_kib": fk, "write_size_kib": wk, "dispatches": len(f["prefill"]),
            "copy_calibration": {"bytes_each_way": copy_bytes,
@@ -233,7 +268,7 @@ def record_traffic(fetch_csv, write_csv, workload, mib):
                                 "fetch_scale": fscale, "write_scale": wscale},
            "read_bytes": round(fk * 1024 * fscale), "write_bytes": round(wk * 1024 * wscale)}
     rec["traffic_bytes"] = rec["read_bytes"] + rec["write_bytes"]
-    with open(TRAFFIC_RECORD, "w") as fh:
+    with open(TRAFFIC_RECORDS[front], "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
@@ -266,7 +301,8 @@ def copy_calibration(kda, mib):
 def main():
     args = parse()
     if args.record_traffic:
-        record_traffic(*args.record_traffic, args.workload, args.copy_calibration_mib or 1536)
+        record_traffic(*args.record_traffic, args.workload, args.copy_calibration_mib or 1536,
+                       args.front)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -279,7 +315,8 @@ def main():
     kda.library()
     torch.cuda.set_device(0)
 
-    pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup, args.segments)
+    pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup, args.segments,
+                       args.front, args.gate_params)
     H, tokens, N = pre["heads"], pre["tokens"], pre["seqs"]
     ms = pre["ms"]
     tok_s = tokens / (ms * 1e-3)
@@ -302,12 +339,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": N, "seq_len": tokens // N,
                    "heads": H, "head_dim": D, "chunk": C, "state": "fp32",
-                   "segments": args.segments},
+                   "segments": args.segments, "front": args.front,
+                   **({"gate_params": args.gate_params} if args.front == "gate" else {})},
         "tflops": tflops,
         "mfma_peak_frac": tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": measured_traffic(args.workload, args.front),
                      "kernel": PREFILL_KERNEL,
                      "bytes_per_launch": alg_bytes},
     }
@@ -315,7 +353,8 @@ def main():
         line["decode"] = time_decode(kda, ki, args.decode_steps)
         line["decode"]["workload"] = DECODE_WORKLOAD
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds,
+                                            pre["gate_params"])
     if args.copy_calibration_mib > 0:
         line["copy_calibration"] = copy_calibration(kda, args.copy_calibration_mib)
     print(json.dumps(line), flush=True)

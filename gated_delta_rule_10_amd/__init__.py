@@ -27,6 +27,8 @@ __all__ = [
     "STATE_COPY",
     "STATE_GATHER",
     "STATE_SCATTER",
+    "GATE_LOG_DECAY",
+    "GATE_LOWER_BOUND",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -41,6 +43,21 @@ class KDAError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {_STATUS.get(status, status)}")
         self.status = status
+
+
+GATE_LOG_DECAY = 0
+GATE_LOWER_BOUND = 1
+
+
+class Gate(ctypes.Structure):
+    """kda_gate: how g and beta are read (zero = log-decay g, beta as given)."""
+    _fields_ = [
+        ("mode", ctypes.c_int),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("lower_bound", ctypes.c_float),
+        ("beta_logits", ctypes.c_int32),
+    ]
 
 
 class ChunkFwdArgs(ctypes.Structure):
@@ -65,6 +82,7 @@ class ChunkFwdArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("segments", ctypes.c_int32),
+        ("gate", Gate),
     ]
 
 
@@ -84,6 +102,7 @@ class RecurrentStepArgs(ctypes.Structure):
         ("state_indices", ctypes.c_void_p),
         ("num_slots", ctypes.c_int32),
         ("o", ctypes.c_void_p),
+        ("gate", Gate),
     ]
 
 
@@ -155,6 +174,29 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims")
 
 
+def _gate(H, A_log, dt_bias, lower_bound, beta_logits):
+    """Fill a kda_gate: the lower-bounded gate when A_log is given, else log-decay g."""
+    gt = Gate()
+    gt.beta_logits = 1 if beta_logits else 0
+    if A_log is None:
+        if dt_bias is not None:
+            raise ValueError("dt_bias needs A_log (the lower-bounded gate)")
+        gt.mode = GATE_LOG_DECAY
+        return gt
+    _need(A_log, "A_log", dtype=torch.float32)
+    if A_log.numel() != H:
+        raise ValueError(f"A_log must hold {H} values")
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", dtype=torch.float32)
+        if dt_bias.numel() != H * 128:
+            raise ValueError(f"dt_bias must hold {H} x 128 values")
+    gt.mode = GATE_LOWER_BOUND
+    gt.A_log = A_log.data_ptr()
+    gt.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
+    gt.lower_bound = float(lower_bound)
+    return gt
+
+
 def _chunk_args(q, N, cu_seqlens, cu_seqlens_host, scale, segments):
     """Fill the size fields of kda_chunk_fwd_args; returns (args, host_array)."""
     T, H, D = q.shape
@@ -192,13 +234,18 @@ def chunk_fwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None, segments=0)
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
               output_final_state=True, scale=1.0, segments=0, num_seqs=None, out=None,
-              final_state=None, workspace=None):
+              final_state=None, workspace=None, A_log=None, dt_bias=None, lower_bound=-5.0,
+              beta_logits=False):
     """Chunkwise KDA prefill forward.
 
     q, k, v: [T, H, 128] bf16 or fp32 (same dtype); g: [T, H, 128] fp32 log-decay;
     beta: [T, H] fp32; cu_seqlens: int32 [N+1] on the device (packed batch) or None
     for ``num_seqs`` (default 1, or initial_state.shape[0]) sequences of equal
     length; initial_state: [N, H, 128, 128] fp32 or None.
+    With ``A_log`` ([H] fp32) g holds raw gate logits and the kernels apply the
+    lower-bounded gate lower_bound * sigmoid(exp(A_log) (g + dt_bias)) (dt_bias
+    [H, 128] fp32 or None); with ``beta_logits`` beta holds logits (sigmoid
+    applied in the kernels).
     Returns (o [T, H, 128], final_state [N, H, 128, 128] fp32 or None).
     """
     lib = library()
@@ -227,6 +274,7 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     if cu_seqlens is not None and cu_seqlens_host is None:
         cu_seqlens_host = cu_seqlens.tolist()  # one device-to-host copy
     a, host = _chunk_args(q, N, cu_seqlens, cu_seqlens_host, scale, segments)
+    a.gate = _gate(H, A_log, dt_bias, lower_bound, beta_logits)
     a.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.g, a.beta = g.data_ptr(), beta.data_ptr()
@@ -246,11 +294,13 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     return o, final_state
 
 
-def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=None):
+def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=None,
+                   A_log=None, dt_bias=None, lower_bound=-5.0, beta_logits=False):
     """One decode token per row, applied in place to ``state`` ([slots, H, 128, 128] fp32).
 
     q, k, v: [B, H, 128]; g: [B, H, 128] fp32; beta: [B, H] fp32;
     state_indices: int32 [B] (slot per row; negative = skip) or None (identity).
+    A_log, dt_bias, lower_bound, beta_logits: the gate front end, as in chunk_fwd.
     Returns o [B, H, 128].
     """
     lib = library()
@@ -273,6 +323,7 @@ def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=N
     a.state_indices = None if state_indices is None else state_indices.data_ptr()
     a.num_slots = state.shape[0]
     a.o = o.data_ptr()
+    a.gate = _gate(H, A_log, dt_bias, lower_bound, beta_logits)
     _check(lib.kda_recurrent_step(ctypes.byref(a), _stream(q)), "kda_recurrent_step")
     return o
 

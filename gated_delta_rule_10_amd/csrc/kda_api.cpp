@@ -15,6 +15,22 @@ bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH; }
 
+// The gate and beta front end: a known mode, A_log present in the gate mode,
+// the bound inside the range the prefill's exponent bounds are derived for.
+kda_status check_gate(const kda_gate &g, bool check_pointers) {
+  if (g.mode != KDA_GATE_LOG_DECAY && g.mode != KDA_GATE_LOWER_BOUND)
+    return KDA_ERROR_INVALID_VALUE;
+  if (g.beta_logits != 0 && g.beta_logits != 1) return KDA_ERROR_INVALID_VALUE;
+  if (g.mode == KDA_GATE_LOWER_BOUND) {
+    if (!(g.lower_bound >= -5.f && g.lower_bound <= 0.f)) return KDA_ERROR_INVALID_VALUE;
+    if (check_pointers) {
+      if (!g.A_log || !aligned(g.A_log, 4)) return KDA_ERROR_INVALID_VALUE;
+      if (g.dt_bias && !aligned(g.dt_bias, 4)) return KDA_ERROR_INVALID_VALUE;
+    }
+  }
+  return KDA_SUCCESS;
+}
+
 // Shared checks of the prefill arguments; fills the token count on success.
 // The workspace query reads sizes only, so it skips the pointer checks.
 constexpr int32_t kMaxHeads = 65536;
@@ -44,6 +60,7 @@ kda_status check_chunk_args(const kda_chunk_fwd_args *a, int64_t *total_tokens,
   // 32-bit buffer offsets
   if ((int64_t)a->num_seqs * a->num_heads > INT32_MAX / 2) return KDA_ERROR_INVALID_VALUE;
   if (a->num_heads > kMaxHeads) return KDA_ERROR_INVALID_VALUE;
+  if (check_gate(a->gate, check_pointers && T > 0) != KDA_SUCCESS) return KDA_ERROR_INVALID_VALUE;
   if (T > 0 && check_pointers) {
     const void *req[] = {a->q, a->k, a->v, a->g, a->o};
     for (const void *p : req)
@@ -74,7 +91,7 @@ const char *kda_status_string(kda_status s) {
   return "KDA_ERROR_UNKNOWN";
 }
 
-const char *kda_version(void) { return "libkda 0.1 (gfx950)"; }
+const char *kda_version(void) { return "libkda 0.2 (gfx950)"; }
 
 size_t kda_state_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype) {
   if (num_heads < 1 || head_dim < 1 || !valid_dtype(dtype)) return 0;
@@ -113,6 +130,7 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *a, void *stream) {
   if (!valid_dtype(a->io_dtype) || !isfinite(a->scale)) return KDA_ERROR_INVALID_VALUE;
   if (a->head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
   if ((int64_t)a->batch * a->num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if (check_gate(a->gate, a->batch > 0) != KDA_SUCCESS) return KDA_ERROR_INVALID_VALUE;
   if (!a->state_indices && a->batch > a->num_slots) return KDA_ERROR_INVALID_VALUE;
   if (a->batch > 0) {
     // the step reads q, k, v, g, beta and writes o element by element; the state

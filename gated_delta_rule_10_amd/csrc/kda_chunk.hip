@@ -141,7 +141,9 @@ __device__ __forceinline__ void gram_job(int jw, int u, int &kind, int &i, int &
   j = c & 15;
 }
 
-template <class OpT, int DV>
+// GATE: g holds gate logits of the lower-bounded gate, applied as a chunk's
+// log-decay is summed (gate_log2).
+template <class OpT, int DV, bool GATE>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   typedef Layout<OpT, DV> L;
   constexpr int VS = kD / DV;  // value blocks per head
@@ -247,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     rv_s = make_rsrc(vg + t0 * rowstride, (has_v && !zero_v) ? nv * row_qk : 0u);
     rg_s = make_rsrc(gg + t0 * rowstride, nv * row_g);
     rb = (lane < 8 && (uint32_t)lane < nv) ? p.beta[(t0 + lane) * H + h] : 0.f;
+    if (p.beta_logits && lane < 8 && (uint32_t)lane < nv) rb = sigmoid_fast(rb);
   };
   auto prefetch_row = [&](int t) {
     if ((uint32_t)t < nv) {
@@ -268,6 +271,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     for (int t = 0; t < 8; ++t) prefetch_row(t);
   };
   if (nchunks > 0) prefetch(0);
+  // gate constants: the head's factor and the bias of this lane's two channels
+  float gate_a = 0.f, gate_dt0 = 0.f, gate_dt1 = 0.f;
+  if constexpr (GATE) {
+    gate_a = gate_head_factor(p.A_log[h]);
+    if (p.dt_bias) {
+      gate_dt0 = p.dt_bias[h * kD + c0];
+      gate_dt1 = p.dt_bias[h * kD + c0 + 1];
+    }
+  }
 
   for (int j = 0; j < nchunks; ++j) {
     const int Lc = (int)((len - (int64_t)j * kC) < kC ? (len - (int64_t)j * kC) : kC);
@@ -278,8 +290,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        a0 += rg[t][0] * kLog2e;
-        a1 += rg[t][1] * kLog2e;
+        if constexpr (GATE) {  // rows past the sequence end keep log-decay 0
+          if (16 * st + 8 * th + t < Lc) {
+            a0 += gate_log2(rg[t][0], gate_a, gate_dt0, p.gate_scale);
+            a1 += gate_log2(rg[t][1], gate_a, gate_dt1, p.gate_scale);
+          }
+        } else {
+          a0 += rg[t][0] * kLog2e;
+          a1 += rg[t][1] * kLog2e;
+        }
         Gl0[t] = a0;
         Gl1[t] = a1;
       }
@@ -746,8 +765,12 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkParams p) {
 
 template <class OpT, int DV>
 hipError_t launch_typed(const ChunkParams &p, int64_t items, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_fwd_kernel<OpT, DV>), dim3((unsigned)items), dim3(kThreads), 0,
-                     stream, p);
+  if (p.gate)
+    hipLaunchKernelGGL((chunk_fwd_kernel<OpT, DV, true>), dim3((unsigned)items), dim3(kThreads),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_fwd_kernel<OpT, DV, false>), dim3((unsigned)items),
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -829,6 +852,12 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
   p.H = a.num_heads;
   p.seq_len = a.seq_len;
   p.scale = a.scale;
+  p.gate = a.gate.mode == KDA_GATE_LOWER_BOUND ? 1 : 0;
+  p.A_log = a.gate.A_log;
+  p.dt_bias = a.gate.dt_bias;
+  // lower_bound log2(e), folded once for the kernels' base-2 exponentials
+  p.gate_scale = (float)((double)a.gate.lower_bound * 1.4426950408889634);
+  p.beta_logits = a.gate.beta_logits;
   if (plan.order_bytes) {
     int32_t *order = reinterpret_cast<int32_t *>((char *)a.workspace + plan.order_off);
     hipLaunchKernelGGL(order_longest_first_kernel, dim3(1), dim3(1024), 0, stream,

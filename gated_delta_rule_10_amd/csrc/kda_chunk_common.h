@@ -35,6 +35,12 @@ struct ChunkParams {
   // two rounds of its transition items)
   int32_t chain0, nchains;
   int32_t seg_front;
+  // gate front end: with gate != 0, g holds gate logits of the lower-bounded
+  // gate (A_log [H], dt_bias [H][128] or null, gate_scale = lower_bound log2 e);
+  // with beta_logits != 0, beta holds logits
+  const float *A_log, *dt_bias;
+  float gate_scale;
+  int32_t gate, beta_logits;
 };
 
 // Segment items ("Kimi K3 -- Training and Infrastructure Notes", section 4.1):

@@ -69,6 +69,14 @@ struct Smem {
 };
 static_assert(sizeof(Buf) % 16 == 0, "buffer alignment");
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget exceeded");
+static_assert(kLDK * 2 >= 128 * 2 + 16, "v rows need 16 spare bytes");
+
+// The 16 spare bytes at the end of each v row (never read as v) hold the
+// lower-bounded gate's dt_bias of the chain's head: channels 4 r .. 4 r + 3 in
+// row r < 32.
+__device__ __forceinline__ float *gate_dt_slot(Smem &sm, int r) {
+  return reinterpret_cast<float *>(sm.v + r * kLDK + 128);
+}
 
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef shortx4_t __attribute__((address_space(3))) lds_shortx4;
@@ -256,6 +264,11 @@ __device__ __forceinline__ void inverse(Buf &B, int d, int l16, int g4) {
 // log-decay is positive; then Gm = G_31 and every factor is within 2^{+-64}.
 // Otherwise the chunk runs as four 16-token windows, window w with the
 // reference at its token 8.
+//
+// GATE: g holds gate logits and the lower-bounded gate is applied as the chunk
+// is digested (gate_log2); beta logits (p.beta_logits) pass through a sigmoid
+// as a window's beta is first used.
+template <bool GATE>
 __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkItem &itm,
                                               Smem &sm, const int pw, const int lane,
                                               const int nblk) {
@@ -275,8 +288,10 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   f32x4 Rg[4][2];              // 8 fp32 channels per token
   float Rb[4];                 // beta per token
   float Gl[4][8];              // log2-decay summed from the quarter's start (inclusive)
-  float qp[8];                 // of the earlier quarters of the chunk
-  float gref[8], gend[8];      // reference and end of a 64-token window (chunk-relative)
+  // without the gate: per channel the chunk-relative prefix of this quarter and
+  // the one-reference window's reference and end, held from decide() to phase 1
+  // (the gate variant re-reads them from sm.qtot to keep its registers free)
+  float qp[8], gref[8], gend[8];
   int blk = 0, win = 0;
   bool slow = false;
 
@@ -284,6 +299,21 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   const bf16 *kg = reinterpret_cast<const bf16 *>(p.k) + (int64_t)h * kD;
   const bf16 *vg = reinterpret_cast<const bf16 *>(p.v) + (int64_t)h * kD;
   const float *gg = p.g + (int64_t)h * kD;
+  // gate constants: the head's factor, and the bias of this lane's channels in
+  // registers for the first chunk (later chunks read it from the v rows' spare
+  // bytes, so it holds no registers through the loop)
+  float gate_a = 0.f, dt0[8];
+  if constexpr (GATE) {
+    gate_a = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                           __builtin_bit_cast(int, gate_head_factor(p.A_log[h]))));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dt0[i] = p.dt_bias ? p.dt_bias[h * kD + 8 * co + i] : 0.f;
+    if (pw == 0 && ts == 0) {
+      *reinterpret_cast<f32x4 *>(gate_dt_slot(sm, 2 * co)) = f32x4{dt0[0], dt0[1], dt0[2], dt0[3]};
+      *reinterpret_cast<f32x4 *>(gate_dt_slot(sm, 2 * co + 1)) =
+          f32x4{dt0[4], dt0[5], dt0[6], dt0[7]};
+    }
+  }
   const uint32_t voff_b16 = (uint32_t)r0 * row_b16 + 16u * co;
   const uint32_t voff_f32 = (uint32_t)r0 * row_f32 + 32u * co;
   auto rows_of = [&](int b) -> uint32_t {
@@ -324,17 +354,30 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   // Log2-decay of a chunk from Rg: Gl (from the quarter's start), the quarter's
   // totals to sm.qtot[pw], and whether no log-decay of the quarter is positive
   // to sm.flag[pw].
-  auto digest_g = [&]() {
+  // nvalid: rows of the chunk in the sequence; dt_of(i): the gate's bias of
+  // channel 8 co + i
+  auto digest_g = [&](int nvalid, auto dt_of) {
     bool ok = true;
     float a[8], y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       a[i] = 0.f;
+      float dt = 0.f;
+      if constexpr (GATE) dt = dt_of(i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float gv = Rg[j][i >> 2][i & 3];
-        ok = ok && gv <= 0.f;  // false on NaN
-        a[i] = fmaf(gv, kLog2e, a[i]);
+        if constexpr (GATE) {
+          // rows past the sequence end read gate logit 0, whose gate is not 0:
+          // they get log-decay 0 (a 0 / 1 factor)
+          const float live = __builtin_amdgcn_fmed3f((float)(nvalid - r0 - j), 0.f, 1.f);
+          const float gl = live * gate_log2(gv, gate_a, dt, p.gate_scale);
+          ok = ok && gl <= 0.f;  // false on NaN
+          a[i] += gl;
+        } else {
+          ok = ok && gv <= 0.f;  // false on NaN
+          a[i] = fmaf(gv, kLog2e, a[i]);
+        }
         Gl[j][i] = a[i];
       }
     }
@@ -357,8 +400,30 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     const bool wave_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
     if (lane == 0) sm.flag[pw] = wave_ok ? 1 : 0;
   };
-  // After the barrier that follows digest_g: chunk-relative prefix of this
-  // quarter, the one-reference window, and whether it fits (same on all waves).
+  // From the quarter totals of the current chunk (sm.qtot, written by
+  // digest_g and read after the barrier that follows it, until the chunk's last
+  // window digests the next one): per channel of the lane, the chunk-relative
+  // prefix of this quarter qp, the one-reference window's reference gref
+  // (token 31) and end gend -- what decide() leaves in registers, re-read by the
+  // gate variant.
+  auto chunk_refs = [&](float (&qp)[8], float (&gref)[8], float (&gend)[8]) {
+    f32x4 t[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      t[q][0] = *reinterpret_cast<const f32x4 *>(&sm.qtot[q][8 * co]);
+      t[q][1] = *reinterpret_cast<const f32x4 *>(&sm.qtot[q][8 * co + 4]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = t[0][i >> 2][i & 3], q1 = t[1][i >> 2][i & 3];
+      const float q2 = t[2][i >> 2][i & 3], q3 = t[3][i >> 2][i & 3];
+      qp[i] = (pw > 0 ? q0 : 0.f) + (pw > 1 ? q1 : 0.f) + (pw > 2 ? q2 : 0.f);
+      gref[i] = q0 + q1;
+      gend[i] = q0 + q1 + q2 + q3;
+    }
+  };
+  // After the barrier that follows digest_g: whether one reference fits the
+  // chunk (same on all waves).
   auto decide = [&]() -> bool {
     f32x4 t[4][2];
 #pragma unroll
@@ -385,7 +450,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   // the sequence read nothing (empty buffer range); a group that is not due yet
   // (the next window is in the same chunk) reloads the chunk it already holds.
   issue_g(0);
-  digest_g();  // waits for g of chunk 0
+  digest_g((int)rows_of(0), [&](int i) { return dt0[i]; });  // waits for g of chunk 0
   issue_qk(0);
   issue_v(0);
   issue_g(1);
@@ -400,6 +465,10 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     const bool last = win == nwin - 1;  // last window of the chunk
     // ====================== phase 1: operands of window it
     if (blk < nblk) {
+      if (p.beta_logits) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Rb[j] = sigmoid_fast(Rb[j]);
+      }
       const int row_lo = slow ? 16 * win : 0;
       const int row_hi = slow ? (16 * win + 16 < Lc ? 16 * win + 16 : Lc) : Lc;
       // this window's reference and end per channel, relative to its start; the
@@ -408,11 +477,18 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       const bool mine = !slow || pw == win;
       float off[8], wref[8], wend[8];
       if (!slow) {
+        if constexpr (GATE) {
+          float qp2[8];
+          chunk_refs(qp2, wref, wend);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          wref[i] = gref[i];
-          wend[i] = gend[i];
-          off[i] = qp[i] - gref[i];
+          for (int i = 0; i < 8; ++i) off[i] = qp2[i] - wref[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            wref[i] = gref[i];
+            wend[i] = gend[i];
+            off[i] = qp[i] - gref[i];
+          }
         }
       } else {
 #pragma unroll
@@ -501,7 +577,9 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       }
     }
     issue_v(blk + 1);  // v of the next chunk (written at its first window)
-    if (blk < nblk && last && blk + 1 < nblk) digest_g();  // read after the barrier
+    if (blk < nblk && last && blk + 1 < nblk)  // read after the barrier
+      digest_g((int)rows_of(blk + 1),
+               [&](int i) { return gate_dt_slot(sm, 2 * co + (i >> 2))[i & 3]; });
     issue_g(blk < nblk && last ? blk + 2 : blk + 1);
     bool fresh = false;  // a new chunk starts at the next window
     if (blk < nblk) {
@@ -701,6 +779,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   }
 }
 
+template <bool GATE>
 __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   const ChunkItem itm = decode_item(p, 1);
@@ -723,7 +802,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
   // producers build window it into buf[it & 1] while the consumers run window
   // it - 1 from buf[(it - 1) & 1].
   if (w >= 4)
-    producer_loop(p, itm, sm, w - 4, lane, nblk);
+    producer_loop<GATE>(p, itm, sm, w - 4, lane, nblk);
   else
     consumer_loop(p, itm, sm, w, lane);
 }
@@ -731,7 +810,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
 }  // namespace
 
 hipError_t launch_chunk_fwd_pipe(const ChunkParams &p, int64_t items, hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_fwd_pipe_kernel, dim3((unsigned)items), dim3(512), 0, stream, p);
+  if (p.gate)
+    hipLaunchKernelGGL(chunk_fwd_pipe_kernel<true>, dim3((unsigned)items), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL(chunk_fwd_pipe_kernel<false>, dim3((unsigned)items), dim3(512), 0, stream,
+                       p);
   return hipGetLastError();
 }
 

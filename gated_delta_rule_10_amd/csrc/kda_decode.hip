@@ -20,6 +20,10 @@
 // accesses.  Column sums over the key rows are reduced first in registers, then
 // across the row groups through LDS.  All state loads are issued before anything
 // waits on them.
+//
+// GATE: g holds gate logits of K3's lower-bounded gate ("How Kimi K3 Engineered
+// Its Way to the Frontier", "How KDA updates its state"), turned into the decay
+// as it is staged; beta logits (beta_logits) pass through a sigmoid.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -30,12 +34,18 @@ constexpr int kD = KDA_HEAD_DIM;  // 128
 constexpr int kCols = 64;     // value columns per workgroup: two workgroups per state
 constexpr int kThreads = 256;
 
-template <class IO, int NC, int NT>
+struct GateArgs {
+  const float *A_log, *dt_bias;  // [H], [H][128] or null
+  float scale;                   // lower_bound log2(e)
+  int32_t beta_logits;
+};
+
+template <class IO, int NC, int NT, bool GATE>
 __global__ __launch_bounds__(NT) void recurrent_step_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
     const int32_t *__restrict__ slot_of_row, int32_t num_slots, int32_t H, float scale,
-    IO *__restrict__ o) {
+    IO *__restrict__ o, GateArgs ga) {
   constexpr int NP = kD / NC;        // workgroups per state
   constexpr int CG = NC / 4;         // column groups (4 columns each)
   constexpr int RG = NT / CG;        // row groups
@@ -61,13 +71,21 @@ __global__ __launch_bounds__(NT) void recurrent_step_kernel(
   __shared__ f32x4 red[2][RG][CG];
   __shared__ float sqk;
   const int64_t tok = (int64_t)bh * kD;
+  auto decay = [&](int c) -> float {  // alpha of key channel c
+    const float x = g[tok + c];
+    if constexpr (GATE)
+      return fast_exp2(gate_log2(x, gate_head_factor(ga.A_log[h]),
+                                 ga.dt_bias ? ga.dt_bias[h * kD + c] : 0.f, ga.scale));
+    else
+      return fast_exp2(x * kLog2e);
+  };
   if (t < kD) {
     sq[t] = to_f32(q[tok + t]);
     sk[t] = to_f32(k[tok + t]);
   } else if (t < 2 * kD) {
-    sa[t - kD] = fast_exp2(g[tok + t - kD] * kLog2e);
+    sa[t - kD] = decay(t - kD);
   }
-  if (NT < 2 * kD && t < kD) sa[t] = fast_exp2(g[tok + t] * kLog2e);
+  if (NT < 2 * kD && t < kD) sa[t] = decay(t);
   block_sync();
 
   if (t < 64) {  // q . k, one wave
@@ -98,7 +116,8 @@ __global__ __launch_bounds__(NT) void recurrent_step_kernel(
       y += yy[j * NC + t];
     }
     const int col = NC * part + t;
-    const float u = beta[bh] * (to_f32(v[tok + col]) - r);
+    const float bt = ga.beta_logits ? sigmoid_fast(beta[bh]) : beta[bh];
+    const float u = bt * (to_f32(v[tok + col]) - r);
     su[t] = u;
     o[tok + col] = from_f32<IO>(scale * (y + sqk * u));
   }
@@ -113,24 +132,29 @@ __global__ __launch_bounds__(NT) void recurrent_step_kernel(
   }
 }
 
+template <class IO, bool GATE>
+hipError_t launch_typed(const kda_recurrent_step_args &a, const GateArgs &ga, hipStream_t stream) {
+  constexpr int NC = kCols, NT = kThreads;
+  const dim3 grid((unsigned)a.batch * (unsigned)a.num_heads * (unsigned)(kD / NC));
+  hipLaunchKernelGGL((recurrent_step_kernel<IO, NC, NT, GATE>), grid, dim3(NT), 0, stream,
+                     (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, a.g, a.beta, a.state,
+                     a.state_indices, a.num_slots, a.num_heads, a.scale, (IO *)a.o, ga);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_recurrent_step(const kda_recurrent_step_args &a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  constexpr int NC = kCols, NT = kThreads;
-  const dim3 grid((unsigned)a.batch * (unsigned)a.num_heads * (unsigned)(kD / NC));
-  if (a.io_dtype == KDA_BF16) {
-    hipLaunchKernelGGL((recurrent_step_kernel<bf16, NC, NT>), grid, dim3(NT), 0, stream,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.g, a.beta,
-                       a.state, a.state_indices, a.num_slots, a.num_heads, a.scale,
-                       (bf16 *)a.o);
-  } else {
-    hipLaunchKernelGGL((recurrent_step_kernel<float, NC, NT>), grid, dim3(NT), 0, stream,
-                       (const float *)a.q, (const float *)a.k, (const float *)a.v, a.g,
-                       a.beta, a.state, a.state_indices, a.num_slots, a.num_heads, a.scale,
-                       (float *)a.o);
-  }
-  return hipGetLastError();
+  GateArgs ga;
+  ga.A_log = a.gate.A_log;
+  ga.dt_bias = a.gate.dt_bias;
+  ga.scale = (float)((double)a.gate.lower_bound * 1.4426950408889634);  // lower_bound log2(e)
+  ga.beta_logits = a.gate.beta_logits;
+  const bool gate = a.gate.mode == KDA_GATE_LOWER_BOUND;
+  if (a.io_dtype == KDA_BF16)
+    return gate ? launch_typed<bf16, true>(a, ga, stream) : launch_typed<bf16, false>(a, ga, stream);
+  return gate ? launch_typed<float, true>(a, ga, stream) : launch_typed<float, false>(a, ga, stream);
 }
 
 }  // namespace kda

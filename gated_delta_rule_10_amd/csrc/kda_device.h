@@ -44,6 +44,22 @@ __device__ __forceinline__ void block_sync() { __syncthreads(); }
 // exp2 on the hardware transcendental unit (inputs are pre-scaled by log2 e).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// K3's lower-bounded gate in log2 units ("How Kimi K3 Engineered Its Way to the
+// Frontier", "How KDA updates its state"): for gate logit x of a channel with
+// bias dt, log2(alpha) = s sigmoid(exp(A_log) (x + dt)) = s / (1 + 2^{-a (x + dt)}),
+// where s = lower_bound log2(e) is folded on the host and a = exp(A_log) log2(e)
+// (gate_head_factor).  Very large logits give s, very negative ones 0 (1 / inf).
+__device__ __forceinline__ float gate_log2(float x, float a, float dt, float s) {
+  return s * __builtin_amdgcn_rcpf(1.f + fast_exp2(-(a * (x + dt))));
+}
+__device__ __forceinline__ float gate_head_factor(float A_log) {
+  return fast_exp2(A_log * kLog2e) * kLog2e;
+}
+// beta from a beta logit: 1 / (1 + e^{-x}).
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * kLog2e));
+}
+
 // ---------------------------------------------------------------- fragments
 template <class OpT> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };

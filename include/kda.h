@@ -33,7 +33,8 @@
  *    128 x 128 block contiguous.  A fixed-length batch [B, T, ...] is the same
  *    memory with N = B and T_total = B * T.
  *  - g is the natural-log decay (alpha = exp(g), g <= 0 expected); beta is the
- *    post-sigmoid write strength in [0, 1].  o = scale * S_t^T q_t; the pages'
+ *    post-sigmoid write strength in [0, 1] -- unless kda_gate says they hold
+ *    gate logits or beta logits (below).  o = scale * S_t^T q_t; the pages'
  *    formula has scale = 1.
  *  - Ownership: the caller allocates and owns every buffer (device memory unless
  *    a field says host).  The library allocates no device memory, keeps no
@@ -75,6 +76,36 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Head dimension (d_k = d_v) and chunk length this build implements. */
 #define KDA_HEAD_DIM 128
 #define KDA_CHUNK 64
+
+/* ------------------------------------------------------------------------
+ * Gate and beta front end, shared by the prefill and the decode step.
+ *
+ * KDA_GATE_LOG_DECAY: g holds the natural-log decay itself (alpha = exp(g)).
+ * KDA_GATE_LOWER_BOUND: g holds raw per-channel gate logits x, and the kernels
+ * compute K3's lower-bounded gate ([P1] "How KDA updates its state", the gate
+ * that replaces Kimi Linear's softplus gate) on the fly:
+ *     g[t, h, c] = lower_bound * sigmoid(exp(A_log[h]) * (x[t, h, c] + dt_bias[h, c]))
+ * so every g lies in [lower_bound, 0].  lower_bound * log2(e) is folded into one
+ * constant on the host, as [P1] "FlashKDA steps the state once per 16 tokens"
+ * describes.
+ * beta_logits = 1: beta holds logits and the kernels use sigmoid(beta) ([P4]
+ * "FlashKDA: the equation, shipped as a kernel": beta logits pass through a
+ * sigmoid); 0: beta is used as given.
+ * A zero-initialised kda_gate is the plain mode (log-decay g, beta as given).
+ * ---------------------------------------------------------------------- */
+typedef enum kda_gate_mode {
+  KDA_GATE_LOG_DECAY = 0,
+  KDA_GATE_LOWER_BOUND = 1
+} kda_gate_mode;
+
+typedef struct kda_gate {
+  kda_gate_mode mode;
+  const float *A_log;    /* device [H] fp32; required with KDA_GATE_LOWER_BOUND     */
+  const float *dt_bias;  /* device [H, 128] fp32, or NULL = no bias                   */
+  float lower_bound;     /* KDA_GATE_LOWER_BOUND: in [-5, 0] (the pages use -5; the  */
+                         /* prefill's exponent bounds are derived for that floor)     */
+  int32_t beta_logits;   /* 0 or 1, see above                                         */
+} kda_gate;
 
 /* ------------------------------------------------------------------------
  * Chunkwise prefill forward ([P1] "FlashKDA steps the state once per 16
@@ -119,8 +150,8 @@ typedef struct kda_chunk_fwd_args {
   const void *q;                  /* [T_total, H, 128] io_dtype                          */
   const void *k;                  /* [T_total, H, 128] io_dtype                          */
   const void *v;                  /* [T_total, H, 128] io_dtype                          */
-  const float *g;                 /* [T_total, H, 128] log-decay                         */
-  const float *beta;              /* [T_total, H]                                        */
+  const float *g;                 /* [T_total, H, 128] log-decay, or gate logits         */
+  const float *beta;              /* [T_total, H] beta, or beta logits                   */
   const float *initial_state;     /* [N, H, 128, 128] or NULL = zeros                    */
   float *final_state;             /* [N, H, 128, 128] or NULL = not written.  May equal  */
                                   /* initial_state (in-place update).                    */
@@ -130,6 +161,7 @@ typedef struct kda_chunk_fwd_args {
   int32_t segments;               /* 0 = automatic, 1 = never split, > 1 = split each    */
                                   /* sequence into this many segments (capped so every   */
                                   /* segment holds at least one chunk)                   */
+  kda_gate gate;                  /* how g and beta are read (zero = log-decay, beta)    */
 } kda_chunk_fwd_args;
 
 /* Bytes of workspace kda_chunk_fwd needs for these arguments (pointers are not
@@ -140,7 +172,9 @@ kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *args, size_t *
 /* Enqueue the prefill forward on `stream`.  Errors: KDA_ERROR_INVALID_VALUE for
  * null required pointers, negative sizes, misaligned pointers, cu_seqlens_host
  * that is not 0-based and non-decreasing, T_total beyond 2^31 - 1 tokens,
- * num_seqs * num_heads beyond 2^30 - 1, or num_heads beyond 65,536;
+ * num_seqs * num_heads beyond 2^30 - 1, num_heads beyond 65,536, an unknown
+ * gate mode, a missing or misaligned A_log, a misaligned dt_bias, lower_bound
+ * outside [-5, 0] or beta_logits other than 0 or 1;
  * KDA_ERROR_UNSUPPORTED for head_dim != 128 or chunk_size != 64;
  * KDA_ERROR_WORKSPACE when the workspace is smaller than queried. */
 kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args, void *stream);
@@ -166,14 +200,19 @@ typedef struct kda_recurrent_step_args {
   const void *q;                  /* [B, H, 128] io_dtype                                */
   const void *k;                  /* [B, H, 128] io_dtype                                */
   const void *v;                  /* [B, H, 128] io_dtype                                */
-  const float *g;                 /* [B, H, 128]                                         */
-  const float *beta;              /* [B, H]                                              */
+  const float *g;                 /* [B, H, 128] log-decay, or gate logits               */
+  const float *beta;              /* [B, H] beta, or beta logits                         */
   float *state;                   /* pool [num_slots, H, 128, 128] fp32, in place        */
   const int32_t *state_indices;   /* device [B] or NULL (identity, needs B <= num_slots) */
   int32_t num_slots;
   void *o;                        /* [B, H, 128] io_dtype                                */
+  kda_gate gate;                  /* how g and beta are read (zero = log-decay, beta)    */
 } kda_recurrent_step_args;
 
+/* Enqueue one decode step on `stream`.  Errors: KDA_ERROR_INVALID_VALUE for
+ * null or misaligned pointers, negative sizes, batch * num_heads beyond
+ * 2^31 - 1, batch > num_slots without state_indices, and the gate checks of
+ * kda_chunk_fwd; KDA_ERROR_UNSUPPORTED for head_dim != 128. */
 kda_status kda_recurrent_step(const kda_recurrent_step_args *args, void *stream);
 
 /* ------------------------------------------------------------------------

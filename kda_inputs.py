@@ -16,6 +16,13 @@ Recipe (the workload statements of the prefill/decode configurations):
   S0    = zeros, or N(0, 0.02^2) fp32 when ``init_std`` is given.
 Variable-length packs draw lengths log-uniformly (see ``varlen_lengths``).
 
+Gate front end (``gate_logits`` / ``beta_logits``): the same generators give the
+raw N(0, 1) draws instead -- gate logits in place of g and beta logits in place
+of beta (whose sigmoid is the recipe's beta) -- and ``make_gate_params`` draws
+per-head A_log ~ N(a_log_mean, a_log_std^2) and per-channel
+dt_bias ~ N(dt_mean, dt_std^2) (the pages give no initialisation; these are
+synthetic parameters of the right shapes).
+
 Every tensor has its own generator seeded from (seed, tensor id), and large
 tensors are filled slice by slice (fixed slice size) so that no fp32 staging
 copy of a whole bf16 tensor is ever made.
@@ -32,7 +39,7 @@ import torch
 D = 128
 _SLICE_ROWS = 1 << 15  # rows of [rows, H, D] generated per step
 
-_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "s0": 6}
+_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "s0": 6, "A_log": 7, "dt_bias": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -145,9 +152,32 @@ def _fill(out: torch.Tensor, gen: torch.Generator, kind: str, bound=None) -> Non
         del x
 
 
+# Gate parameter sets.  "matched": with N(0, 1) gate logits the log-decay has
+# about the statistics of the recipe's -softplus(N(0, 1)) (mean ~ -0.8, the same on
+# every channel); "heavy": a spread of per-channel biases and per-head scales,
+# so that some channels of every head decay fast (near the bound) on many tokens.
+GATE_PARAM_SETS = {
+    "matched": dict(a_log_mean=0.0, a_log_std=0.1, dt_mean=-2.0, dt_std=0.1),
+    "heavy": dict(a_log_mean=0.0, a_log_std=0.5, dt_mean=-2.0, dt_std=0.5),
+}
+
+
+def make_gate_params(heads: int, device="cpu", seed: int = 1009, a_log_mean: float = 0.0,
+                     a_log_std: float = 0.1, dt_mean: float = -2.0, dt_std: float = 0.1) -> dict:
+    """Per-head A_log [H] and per-channel dt_bias [H, 128], fp32 (defaults: "matched")."""
+    A = torch.empty((heads,), dtype=torch.float32, device=device)
+    _fill(A.view(heads, 1), _gen(device, seed, _TENSOR_IDS["A_log"]), "normal")
+    A.mul_(float(a_log_std)).add_(float(a_log_mean))
+    dt = torch.empty((heads, D), dtype=torch.float32, device=device)
+    _fill(dt, _gen(device, seed, _TENSOR_IDS["dt_bias"]), "normal")
+    dt.mul_(float(dt_std)).add_(float(dt_mean))
+    return {"A_log": A, "dt_bias": dt}
+
+
 def make_prefill(cfg: PrefillConfig, device="cpu", seed: int = 1001, dtype=None,
                  heads: Optional[int] = None, lengths: Optional[Sequence[int]] = None,
-                 init_std="cfg", g_lower_bound="cfg") -> dict:
+                 init_std="cfg", g_lower_bound="cfg", gate_logits: bool = False,
+                 beta_logits: bool = False) -> dict:
     """Generate one batch of prefill inputs for ``cfg`` (overrides allowed).
 
     Returns a dict with q, k, v ([T, H, 128], I/O dtype), g ([T, H, 128] fp32),
@@ -167,9 +197,9 @@ def make_prefill(cfg: PrefillConfig, device="cpu", seed: int = 1001, dtype=None,
         _fill(t, _gen(device, seed, _TENSOR_IDS[name]), kind)
         out[name] = t
     g = torch.empty((T, H, D), dtype=torch.float32, device=device)
-    _fill(g, _gen(device, seed, _TENSOR_IDS["g"]), "logdecay", lb)
+    _fill(g, _gen(device, seed, _TENSOR_IDS["g"]), "normal" if gate_logits else "logdecay", lb)
     beta = torch.empty((T, H), dtype=torch.float32, device=device)
-    _fill(beta, _gen(device, seed, _TENSOR_IDS["beta"]), "sigmoid")
+    _fill(beta, _gen(device, seed, _TENSOR_IDS["beta"]), "normal" if beta_logits else "sigmoid")
     out["g"], out["beta"] = g, beta
     if std is None:
         out["initial_state"] = None
@@ -191,7 +221,8 @@ def make_prefill(cfg: PrefillConfig, device="cpu", seed: int = 1001, dtype=None,
 
 def make_decode_ring(cfg: DecodeConfig, device="cpu", seed: int = 1005,
                      batch: Optional[int] = None, heads: Optional[int] = None,
-                     ring: Optional[int] = None) -> dict:
+                     ring: Optional[int] = None, gate_logits: bool = False,
+                     beta_logits: bool = False) -> dict:
     """Per-step decode inputs for ``ring`` distinct steps plus the initial state pool.
 
     q, k, g: [ring, B, H, 128]; v: [ring, B, H, 128]; beta: [ring, B, H];
@@ -207,9 +238,9 @@ def make_decode_ring(cfg: DecodeConfig, device="cpu", seed: int = 1005,
         _fill(t, _gen(device, seed, _TENSOR_IDS[name]), kind)
         out[name] = t.view(R, B, H, D)
     g = torch.empty((R * B, H, D), dtype=torch.float32, device=device)
-    _fill(g, _gen(device, seed, _TENSOR_IDS["g"]), "logdecay")
+    _fill(g, _gen(device, seed, _TENSOR_IDS["g"]), "normal" if gate_logits else "logdecay")
     beta = torch.empty((R * B, H), dtype=torch.float32, device=device)
-    _fill(beta, _gen(device, seed, _TENSOR_IDS["beta"]), "sigmoid")
+    _fill(beta, _gen(device, seed, _TENSOR_IDS["beta"]), "normal" if beta_logits else "sigmoid")
     out["g"], out["beta"] = g.view(R, B, H, D), beta.view(R, B, H)
     s = torch.empty((B, H, D, D), dtype=torch.float32, device=device)
     _fill(s, _gen(device, seed, _TENSOR_IDS["s0"]), "normal")

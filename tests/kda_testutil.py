@@ -29,11 +29,14 @@ def to64(t) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
 
-def oracle_chains(inp: dict, chains, scale=1.0, nthreads=0):
+def oracle_chains(inp: dict, chains, scale=1.0, nthreads=0, front=None):
     """Run the oracle on selected (sequence n, head h) chains of a prefill batch.
 
     Returns {(n, h): (o [L, 128], S_final [128, 128])} computed from exactly the
-    tensors in ``inp`` (the values the GPU received)."""
+    tensors in ``inp`` (the values the GPU received).  ``front`` (optional dict:
+    A_log, dt_bias, lower_bound for the lower-bounded gate when A_log is not None;
+    beta_logits) says that g and beta hold logits: the oracle's gate and sigmoid
+    turn each chain's logits into g and beta first."""
     cu = inp["cu_seqlens_host"]
     # gather every chain into one packed single-head batch for one oracle call
     qs, ks, vs, gs, bs, s0s, lens = [], [], [], [], [], [], []
@@ -42,8 +45,17 @@ def oracle_chains(inp: dict, chains, scale=1.0, nthreads=0):
         qs.append(to64(inp["q"][a:b, h]))
         ks.append(to64(inp["k"][a:b, h]))
         vs.append(to64(inp["v"][a:b, h]))
-        gs.append(to64(inp["g"][a:b, h]))
-        bs.append(to64(inp["beta"][a:b, h]))
+        g = to64(inp["g"][a:b, h])
+        beta = to64(inp["beta"][a:b, h])
+        if front is not None and front.get("A_log") is not None:
+            dt = front.get("dt_bias")
+            g = oracle.lowerbound_gate(g[:, None], to64(front["A_log"][h:h + 1]),
+                                       None if dt is None else to64(dt[h:h + 1]),
+                                       front["lower_bound"])[:, 0]
+        if front is not None and front.get("beta_logits"):
+            beta = oracle.sigmoid(beta)
+        gs.append(g)
+        bs.append(beta)
         s0 = inp.get("initial_state")
         s0s.append(to64(s0[n, h]) if s0 is not None else np.zeros((128, 128)))
         lens.append(b - a)

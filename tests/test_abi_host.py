@@ -150,3 +150,77 @@ def test_state_io_rejects_invalid_arguments(lib):
     assert f(kda.STATE_COPY, base, 0, 2, base * 4, 0, 2, None, 1, 4, 64, None) == 2
     assert f(kda.STATE_COPY, base, 0, 1, base * 4, 0, 2, None, 2, 4, 128, None) == 1  # count > src
     assert f(kda.STATE_ZERO, None, 0, 0, base, 0, 2, None, 0, 4, 128, None) == 0  # empty
+
+
+def _gate_args(**gate):
+    a = _args()
+    a.gate.mode = kda.GATE_LOWER_BOUND
+    a.gate.A_log = 1 << 21
+    a.gate.lower_bound = -5.0
+    for k_, v_ in gate.items():
+        setattr(a.gate, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,pointer_only", [
+    ("mode", 5, False),
+    ("A_log", 0, True),
+    ("A_log", (1 << 21) + 2, True),    # needs 4 bytes
+    ("dt_bias", (1 << 21) + 1, True),
+    ("lower_bound", -5.5, False),      # below the floor the exponent bounds assume
+    ("lower_bound", 0.25, False),
+    ("lower_bound", float("nan"), False),
+    ("beta_logits", 2, False),
+])
+def test_gate_front_end_rejects_invalid_arguments(lib, field, value, pointer_only):
+    """The lower-bounded gate's arguments are checked on the host, by both the
+    prefill (the size query skips pointers) and the decode step."""
+    a = _gate_args(**{field: value})
+    assert lib.kda_chunk_fwd(ctypes.byref(a), None) == 1
+    size = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(size)) == (
+        0 if pointer_only else 1)
+    d = kda.RecurrentStepArgs()
+    d.batch, d.num_heads, d.head_dim, d.io_dtype, d.scale = 4, 2, 128, kda.KDA_BF16, 1.0
+    d.q = d.k = d.v = d.g = d.beta = d.state = d.o = 1 << 20
+    d.num_slots = 4
+    d.gate = a.gate
+    assert lib.kda_recurrent_step(ctypes.byref(d), None) == 1
+
+
+def test_gate_bounds_accepted_by_the_size_query(lib):
+    """lower_bound -5 (the pages' value) and 0 are inside the accepted range."""
+    for lb in (-5.0, -1.0, 0.0):
+        a = _gate_args(lower_bound=lb, beta_logits=1)
+        size = ctypes.c_size_t(0)
+        assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(size)) == 0
+
+
+def test_ctypes_structs_match_the_header(tmp_path):
+    """The binding's structure mirrors have the header's field offsets and sizes
+    (a C program built against include/kda.h prints them)."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    structs = {"kda_chunk_fwd_args": kda.ChunkFwdArgs,
+               "kda_recurrent_step_args": kda.RecurrentStepArgs, "kda_gate": kda.Gate}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kda.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                               check=True).stdout.splitlines():
+        s, f, n = line.split()
+        got[(s, f)] = int(n)
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
