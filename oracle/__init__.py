@@ -29,6 +29,11 @@ __all__ = [
     "transition",
     "lowerbound_gate",
     "sigmoid",
+    "short_conv",
+    "swish",
+    "l2norm",
+    "rmsnorm",
+    "fused_decode_step",
     "max_threads",
     "load",
     "open_library",
@@ -88,10 +93,17 @@ def open_library(path):
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, ctypes.c_double, _DP,
     ]
     lib.kda_oracle_sigmoid.argtypes = [ctypes.c_int64, _DP, _DP]
+    lib.kda_oracle_short_conv.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP,
+                                          _DP, _DP]
+    lib.kda_oracle_swish.argtypes = [ctypes.c_int64, _DP, _DP]
+    lib.kda_oracle_l2norm.argtypes = [ctypes.c_int64, ctypes.c_int, _DP, ctypes.c_double, _DP]
+    lib.kda_oracle_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int, _DP, _DP, ctypes.c_double,
+                                       _DP]
     lib.kda_oracle_max_threads.argtypes = []
     for fn in ("kda_oracle_recurrent", "kda_oracle_chunked", "kda_oracle_decode_step",
                "kda_oracle_transition", "kda_oracle_lowerbound_gate", "kda_oracle_sigmoid",
-               "kda_oracle_max_threads"):
+               "kda_oracle_short_conv", "kda_oracle_swish", "kda_oracle_l2norm",
+               "kda_oracle_rmsnorm", "kda_oracle_max_threads"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -253,6 +265,123 @@ def sigmoid(x):
     rc = lib.kda_oracle_sigmoid(x.size, _ptr(x), _ptr(y))
     _check(rc, "kda_oracle_sigmoid")
     return y
+
+
+def short_conv(x, w, cache):
+    """Causal depthwise convolution continuing from ``cache``.
+
+    x: [T, C] inputs; w: [C, W] taps (oldest first); cache: [W - 1, C] previous
+    inputs (oldest first).  Returns (y [T, C], new cache [W - 1, C]).
+    """
+    lib = load()
+    x = _f64(x, "x")
+    w = _f64(w, "w")
+    T, C = x.shape
+    if w.ndim != 2 or w.shape[0] != C:
+        raise ValueError("w must be [C, W]")
+    W = w.shape[1]
+    cache = np.array(_f64(cache, "cache"), copy=True)
+    if cache.shape != (W - 1, C):
+        raise ValueError(f"cache must be [{W - 1}, {C}]")
+    y = np.empty_like(x)
+    rc = lib.kda_oracle_short_conv(T, C, W, _ptr(x), _ptr(w), _ptr(cache), _ptr(y))
+    _check(rc, "kda_oracle_short_conv")
+    return y, cache
+
+
+def swish(x):
+    """x * sigmoid(x), elementwise."""
+    lib = load()
+    x = _f64(x, "x")
+    y = np.empty_like(x)
+    _check(lib.kda_oracle_swish(x.size, _ptr(x), _ptr(y)), "kda_oracle_swish")
+    return y
+
+
+def l2norm(x, eps=1e-6):
+    """x / sqrt(sum x^2 + eps) over the last axis."""
+    lib = load()
+    x = _f64(x, "x")
+    y = np.empty_like(x)
+    n = x.shape[-1]
+    _check(lib.kda_oracle_l2norm(x.size // n, n, _ptr(x), float(eps), _ptr(y)),
+           "kda_oracle_l2norm")
+    return y
+
+
+def rmsnorm(x, weight=None, eps=1e-6):
+    """x / sqrt(mean x^2 + eps) * weight over the last axis (weight [n] or None)."""
+    lib = load()
+    x = _f64(x, "x")
+    y = np.empty_like(x)
+    n = x.shape[-1]
+    w = _f64(weight, "weight")
+    if w is not None:
+        w = np.ascontiguousarray(w.reshape(-1))
+        if w.shape != (n,):
+            raise ValueError(f"weight must hold {n} values")
+    _check(lib.kda_oracle_rmsnorm(x.size // n, n, _ptr(x), _ptr(w), float(eps), _ptr(y)),
+           "kda_oracle_rmsnorm")
+    return y
+
+
+def fused_decode_step(q_in, k_in, v_in, g, beta, conv_w, conv_cache, state_pool,
+                      slot_idx=None, scale=1.0, l2_eps=1e-6, norm_weight=None,
+                      norm_eps=1e-6, out_norm=True, gate=None):
+    """One decode token per row with the layer's front and back end, composed from
+    the functions above ("Kimi K3 -- Training and Infrastructure Notes", section 4.5:
+    one kernel covers short convolution, input normalisation, gating, the
+    recurrence and output normalisation; "Kimi K3: a 2.8T open model ...",
+    "Kimi Delta Attention": q, k from a short convolution, Swish and L2
+    normalisation, v from a short convolution and Swish).
+
+    Per row b with slot s = slot_idx[b] (b when None; negative = skipped):
+      for each of q, k, v (index i = 0, 1, 2): the short convolution of the row's
+      raw input continuing from conv_cache[s, i] with taps conv_w[i] (width 4),
+      then Swish; q and k L2-normalised per head; with ``gate`` (dict A_log,
+      dt_bias, lower_bound, beta_logits) g and beta are logits turned by the
+      lower-bounded gate and the sigmoid; the KDA step on state_pool[s]; o
+      RMSNorm-ed per head with ``norm_weight`` [V] (or weight 1) if out_norm.
+
+    q_in, k_in, v_in, g: [B, H, K]; beta: [B, H]; conv_w: [3, H, K, W];
+    conv_cache: [slots, 3, W - 1, H, K]; state_pool: [slots, H, K, V].
+    Returns (o [B, H, V] (NaN for skipped rows), new state_pool, new conv_cache).
+    """
+    ins = [_f64(t, "x") for t in (q_in, k_in, v_in)]
+    B, H, K = ins[0].shape
+    w = _f64(conv_w, "conv_w")
+    W = w.shape[-1]
+    cache = np.array(_f64(conv_cache, "conv_cache"), copy=True)
+    if w.shape != (3, H, K, W) or cache.shape[1:] != (3, W - 1, H, K):
+        raise ValueError("conv_w must be [3, H, K, W] and conv_cache [slots, 3, W-1, H, K]")
+    slots = (np.arange(B) if slot_idx is None
+             else np.asarray(_f64(slot_idx, "slot_idx")).astype(np.int64))
+    conv = [np.zeros((B, H, K)) for _ in range(3)]
+    for b in range(B):
+        s = int(slots[b])
+        if s < 0:
+            continue
+        for i in range(3):
+            y, c_new = short_conv(ins[i][b].reshape(1, H * K), w[i].reshape(H * K, W),
+                                  cache[s, i].reshape(W - 1, H * K))
+            conv[i][b] = swish(y).reshape(H, K)
+            cache[s, i] = c_new.reshape(W - 1, H, K)
+    q = l2norm(conv[0], l2_eps)
+    k = l2norm(conv[1], l2_eps)
+    v = conv[2]
+    g = _f64(g, "g")
+    beta = _f64(beta, "beta")
+    if gate is not None:
+        if gate.get("A_log") is not None:
+            g = lowerbound_gate(g, gate["A_log"], gate.get("dt_bias"), gate["lower_bound"])
+        if gate.get("beta_logits"):
+            beta = sigmoid(beta)
+    o, pool = decode_step(q, k, v, g, beta, state_pool,
+                          None if slot_idx is None else slots, scale=scale)
+    if out_norm:
+        live = slots >= 0
+        o[live] = rmsnorm(o[live], norm_weight, norm_eps)
+    return o, pool, cache
 
 
 def max_threads() -> int:

@@ -25,6 +25,13 @@
  *       subsection "FlashKDA: the equation, shipped as a kernel" (optional state
  *       in and out, variable-length batches through cumulative sequence lengths;
  *       beta arrives as logits that pass through a sigmoid).
+ *  [P1] section "How KDA updates its state" (the layer carries three ShortConv
+ *       caches, for the query, key and value projections) and "What the
+ *       hybrid saves" (kernel size 4); [P4] "Kimi Delta Attention" (queries and
+ *       keys come from a short convolution followed by Swish and L2
+ *       normalisation, values from a short convolution and Swish); [P3]
+ *       section 4.5 (the fused decode kernel covers short convolution, input
+ *       normalisation, gating, the recurrence and output normalisation).
  *  [P1] section "How KDA updates its state", the part on how the decay logit
  *       becomes a decay: K3's lower-bounded gate (flash-linear-attention's
  *       gate.py) turns a raw per-channel gate logit into a log-decay in
@@ -36,6 +43,11 @@
  *  - g is the natural-log decay (alpha = exp(g)), beta is already post-sigmoid.
  *  - Variable-length batches reset the state to the sequence's own initial state
  *    at every cu_seqlens boundary.
+ *  - ShortConv is a causal depthwise convolution without bias whose cache holds
+ *    the W - 1 previous raw inputs, oldest first; taps w[c, 0..W-1] run oldest
+ *    to newest, so w[c, W-1] multiplies the current input.
+ *  - L2 normalisation is x / sqrt(sum x^2 + eps); "output normalisation" is an
+ *    RMSNorm over each head's V outputs, x / sqrt(mean x^2 + eps) * w.
  *
  * Layouts (row-major, innermost last), the same as the product ABI:
  *   q, k, g : [T_total, H, K]      v, o : [T_total, H, V]      beta : [T_total, H]
@@ -357,6 +369,67 @@ int kda_oracle_lowerbound_gate(int64_t T, int H, int K, const double *x, const d
 int kda_oracle_sigmoid(int64_t n, const double *x, double *y) {
   if (n < 0 || (n > 0 && (!x || !y))) return KDA_ORACLE_EINVAL;
   for (int64_t i = 0; i < n; ++i) y[i] = sigmoid(x[i]);
+  return KDA_ORACLE_OK;
+}
+
+/*
+ * ShortConv: causal depthwise convolution of width W over T tokens of C channels,
+ * continuing from the cache of the W - 1 previous inputs (cache[j, c] is the input
+ * at time j - (W - 1), j = 0 oldest):
+ *   y[t, c] = sum_{i=0}^{W-1} w[c, i] * x[t - (W - 1) + i, c]
+ * The cache is replaced by the last W - 1 inputs.  x, y: [T, C]; w: [C, W];
+ * cache: [W - 1, C].  y may not alias x.
+ */
+int kda_oracle_short_conv(int64_t T, int C, int W, const double *x, const double *w,
+                          double *cache, double *y) {
+  if (T < 0 || C <= 0 || W < 1 || !w || !cache || (T > 0 && (!x || !y)))
+    return KDA_ORACLE_EINVAL;
+  const int64_t n = T + W - 1;  /* the cache rows, then the new inputs */
+  double *ext = (double *)malloc(sizeof(double) * (size_t)n * C);
+  if (!ext) return KDA_ORACLE_ENOMEM;
+  memcpy(ext, cache, sizeof(double) * (size_t)(W - 1) * C);
+  if (T > 0) memcpy(ext + (size_t)(W - 1) * C, x, sizeof(double) * (size_t)T * C);
+  for (int64_t t = 0; t < T; ++t)
+    for (int c = 0; c < C; ++c) {
+      double acc = 0.0;
+      for (int i = 0; i < W; ++i) acc += w[(size_t)c * W + i] * ext[(size_t)(t + i) * C + c];
+      y[(size_t)t * C + c] = acc;
+    }
+  memcpy(cache, ext + (size_t)T * C, sizeof(double) * (size_t)(W - 1) * C);
+  free(ext);
+  return KDA_ORACLE_OK;
+}
+
+/* Swish (SiLU) elementwise: x * sigmoid(x). */
+int kda_oracle_swish(int64_t n, const double *x, double *y) {
+  if (n < 0 || (n > 0 && (!x || !y))) return KDA_ORACLE_EINVAL;
+  for (int64_t i = 0; i < n; ++i) y[i] = x[i] * sigmoid(x[i]);
+  return KDA_ORACLE_OK;
+}
+
+/* L2 normalisation of each of `rows` vectors of length n: x / sqrt(sum x^2 + eps). */
+int kda_oracle_l2norm(int64_t rows, int n, const double *x, double eps, double *y) {
+  if (rows < 0 || n <= 0 || (rows > 0 && (!x || !y))) return KDA_ORACLE_EINVAL;
+  for (int64_t r = 0; r < rows; ++r) {
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) ss += x[(size_t)r * n + i] * x[(size_t)r * n + i];
+    const double inv = 1.0 / sqrt(ss + eps);
+    for (int i = 0; i < n; ++i) y[(size_t)r * n + i] = x[(size_t)r * n + i] * inv;
+  }
+  return KDA_ORACLE_OK;
+}
+
+/* RMSNorm of each of `rows` vectors of length n: x / sqrt(mean x^2 + eps) * w
+ * (w: [n], or NULL for 1). */
+int kda_oracle_rmsnorm(int64_t rows, int n, const double *x, const double *w, double eps,
+                       double *y) {
+  if (rows < 0 || n <= 0 || (rows > 0 && (!x || !y))) return KDA_ORACLE_EINVAL;
+  for (int64_t r = 0; r < rows; ++r) {
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) ss += x[(size_t)r * n + i] * x[(size_t)r * n + i];
+    const double inv = 1.0 / sqrt(ss / n + eps);
+    for (int i = 0; i < n; ++i) y[(size_t)r * n + i] = x[(size_t)r * n + i] * inv * (w ? w[i] : 1.0);
+  }
   return KDA_ORACLE_OK;
 }
 

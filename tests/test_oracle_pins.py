@@ -17,6 +17,9 @@ Pages (cited by title and section):
   The lower-bounded gate: [P1] "How KDA updates its state" (K3's gate from
   flash-linear-attention's gate.py: g = lower_bound * sigmoid(exp(A_log) *
   (x + dt_bias)), so g stays in (lower_bound, 0) and exp(g) above exp(-5)).
+  The decode front end: [P1] "How KDA updates its state" and "What the hybrid
+  saves" (three ShortConv caches of kernel size 4, 216 KiB per layer in bf16);
+  [P4] "Kimi Delta Attention" (short convolution, Swish, L2 normalisation).
 """
 import json
 import math
@@ -404,6 +407,137 @@ def test_beta_sigmoid_values():
     np.testing.assert_allclose(oracle.sigmoid(z), expit(z), rtol=1e-15, atol=0)
 
 
+# ------------------------------------------------------- decode front end
+def test_short_conv_matches_library_correlation():
+    """The causal depthwise convolution equals numpy's 'valid' correlation of the
+    cache followed by the inputs with each channel's taps (oldest tap first)."""
+    rng = np.random.default_rng(21)
+    T, C, W = 7, 5, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    cache = rng.standard_normal((W - 1, C))
+    y, new_cache = oracle.short_conv(x, w, cache)
+    ext = np.concatenate([cache, x])
+    for c in range(C):
+        np.testing.assert_allclose(y[:, c], np.correlate(ext[:, c], w[c], mode="valid"),
+                                   rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(new_cache, x[-(W - 1):])
+
+
+def test_short_conv_identity_and_delay_taps():
+    """Tap on the newest input reproduces x; tap on the oldest delays it by
+    W - 1 tokens, reading the cache first."""
+    rng = np.random.default_rng(22)
+    T, C, W = 6, 3, 4
+    x = rng.standard_normal((T, C))
+    cache = rng.standard_normal((W - 1, C))
+    ident = np.zeros((C, W)); ident[:, -1] = 1.0
+    delay = np.zeros((C, W)); delay[:, 0] = 1.0
+    np.testing.assert_array_equal(oracle.short_conv(x, ident, cache)[0], x)
+    np.testing.assert_array_equal(oracle.short_conv(x, delay, cache)[0],
+                                  np.concatenate([cache, x])[:T])
+
+
+def test_short_conv_streams_token_by_token():
+    """One call over T tokens equals T one-token calls chained through the cache
+    (the decode step's use)."""
+    rng = np.random.default_rng(23)
+    T, C, W = 9, 4, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    cache0 = rng.standard_normal((W - 1, C))
+    y_all, c_all = oracle.short_conv(x, w, cache0)
+    cache = cache0
+    for t in range(T):
+        y_t, cache = oracle.short_conv(x[t:t + 1], w, cache)
+        np.testing.assert_allclose(y_t[0], y_all[t], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(cache, c_all)
+
+
+def test_conv_cache_bytes_match_page_accounting():
+    """[P1] "What the hybrid saves": three caches of kernel size 4 (W - 1 = 3
+    previous inputs) over 96 heads x 128 channels in bf16 are 216 KiB."""
+    c = json.load(open(GOLDEN))["state_memory"]
+    W = c["conv_kernel_size"]
+    assert 3 * (W - 1) * c["heads"] * c["head_dim"] * 2 == c["conv_cache_bytes_per_layer"]
+
+
+def test_swish_identities():
+    """swish(0) = 0, swish(x) - swish(-x) = x, swish(ln 3) = 0.75 ln 3, and the
+    library logistic function times x."""
+    from scipy.special import expit
+    assert oracle.swish(np.array([0.0]))[0] == 0.0
+    x = np.random.default_rng(24).standard_normal(50) * 5
+    np.testing.assert_allclose(oracle.swish(x) - oracle.swish(-x), x, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.swish(np.array([math.log(3.0)])), [0.75 * math.log(3.0)],
+                               rtol=1e-15)
+    np.testing.assert_allclose(oracle.swish(x), x * expit(x), rtol=1e-14, atol=1e-15)
+
+
+def test_l2norm_closed_forms():
+    """(3, 4) -> (0.6, 0.8) with eps = 0; with eps the norm is |x| / sqrt(|x|^2 + eps);
+    zero stays zero."""
+    np.testing.assert_allclose(oracle.l2norm(np.array([[3.0, 4.0]]), eps=0.0), [[0.6, 0.8]],
+                               rtol=1e-15)
+    x = np.random.default_rng(25).standard_normal((4, 128))
+    y = oracle.l2norm(x, eps=1e-6)
+    nx = np.linalg.norm(x, axis=-1)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), nx / np.sqrt(nx ** 2 + 1e-6),
+                               rtol=1e-13)
+    np.testing.assert_allclose(y / np.linalg.norm(y, axis=-1, keepdims=True),
+                               x / nx[:, None], rtol=1e-12)
+    assert np.array_equal(oracle.l2norm(np.zeros((1, 8))), np.zeros((1, 8)))
+
+
+def test_rmsnorm_closed_forms():
+    """An alternating +-c vector has mean square c^2: it maps to +-w / sqrt(1 + eps/c^2);
+    the weight multiplies per element; scaling x by 7 leaves the eps = 0 result."""
+    c, eps = 3.0, 1e-6
+    x = np.array([[c, -c, c, -c]])
+    w = np.array([1.0, 2.0, 0.5, -1.0])
+    np.testing.assert_allclose(oracle.rmsnorm(x, w, eps),
+                               np.array([[1, -2, 0.5, 1.0]]) / math.sqrt(1 + eps / c ** 2),
+                               rtol=1e-15)
+    z = np.random.default_rng(26).standard_normal((3, 128))
+    np.testing.assert_allclose(oracle.rmsnorm(7 * z, None, 0.0), oracle.rmsnorm(z, None, 0.0),
+                               rtol=1e-13)
+    np.testing.assert_allclose(np.mean(oracle.rmsnorm(z, None, 0.0) ** 2, axis=-1), 1.0,
+                               rtol=1e-13)
+
+
+def test_fused_decode_steps_equal_whole_sequence_front_end():
+    """T fused decode steps from an empty (zero) cache equal the whole sequence
+    pushed through the short convolution at once, Swish, L2 normalisation, the
+    token loop and the output RMSNorm (streaming = batch)."""
+    rng = np.random.default_rng(27)
+    T, H, K, W = 6, 2, 4, 4
+    raw = [rng.standard_normal((T, H, K)) for _ in range(3)]
+    w = rng.standard_normal((3, H, K, W))
+    g = -np.logaddexp(0.0, rng.standard_normal((T, H, K)))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, H))))
+    nw = rng.standard_normal(K)
+    pool = rng.standard_normal((1, H, K, K)) * 0.1
+    cache = np.zeros((1, 3, W - 1, H, K))
+    outs = []
+    st = pool
+    for t in range(T):
+        o, st, cache = oracle.fused_decode_step(raw[0][t:t + 1], raw[1][t:t + 1],
+                                                raw[2][t:t + 1], g[t:t + 1], beta[t:t + 1],
+                                                w, cache, st, norm_weight=nw, scale=0.5)
+        outs.append(o[0])
+    conv = []
+    for i in range(3):
+        y, _ = oracle.short_conv(raw[i].reshape(T, H * K), w[i].reshape(H * K, W),
+                                 np.zeros((W - 1, H * K)))
+        conv.append(oracle.swish(y).reshape(T, H, K))
+    q, k = oracle.l2norm(conv[0]), oracle.l2norm(conv[1])
+    o_ref, s_ref = oracle.recurrent(q, k, conv[2], g, beta, initial_state=pool, scale=0.5)
+    np.testing.assert_allclose(np.array(outs), oracle.rmsnorm(o_ref, nw), rtol=1e-11,
+                               atol=1e-12)
+    np.testing.assert_allclose(st, s_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(cache[0, 0], raw[0][-(W - 1):])
+
+
 # ------------------------------------------- planted mistakes must be caught
 def _pins_pass():
     """Run a compact set of the pins above; True if all hold."""
@@ -479,6 +613,53 @@ GATE_MUTANTS = {
     "gate_head0": lambda s: s.replace("const double a = exp(A_log[h]);",
                                       "const double a = exp(A_log[0]);"),
 }
+
+
+def _front_pins_pass():
+    checks = [test_short_conv_matches_library_correlation, test_short_conv_streams_token_by_token,
+              test_swish_identities, test_l2norm_closed_forms, test_rmsnorm_closed_forms]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+FRONT_MUTANTS = {
+    # taps applied newest first
+    "conv_taps_reversed": lambda s: s.replace("acc += w[(size_t)c * W + i] * ext",
+                                              "acc += w[(size_t)c * W + (W - 1 - i)] * ext"),
+    # cache left as it was
+    "conv_cache_not_updated": lambda s: s.replace(
+        "memcpy(cache, ext + (size_t)T * C, sizeof(double) * (size_t)(W - 1) * C);", ""),
+    # Swish with the reflected sigmoid
+    "swish_sign": lambda s: s.replace("y[i] = x[i] * sigmoid(x[i]);",
+                                      "y[i] = x[i] * sigmoid(-x[i]);"),
+    # L2 normalisation without the square root
+    "l2_no_sqrt": lambda s: s.replace("const double inv = 1.0 / sqrt(ss + eps);",
+                                      "const double inv = 1.0 / (ss + eps);"),
+    # RMSNorm over the sum instead of the mean
+    "rms_sum": lambda s: s.replace("const double inv = 1.0 / sqrt(ss / n + eps);",
+                                   "const double inv = 1.0 / sqrt(ss + eps);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FRONT_MUTANTS))
+def test_front_pins_catch_planted_mistake(name, tmp_path):
+    """Plausible mistakes in the decode front end's pieces, planted in a copy of
+    the oracle on the CPU, each fail one of their pins."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(SOURCE).read()
+    mutated = FRONT_MUTANTS[name](src)
+    assert mutated != src, "mutation did not apply"
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(mutated)
+    lib_path = build_oracle(str(path), str(tmp_path / f"libmut_{name}.so"))
+    assert _front_pins_pass(), "unmodified oracle must pass the front-end pins"
+    with oracle.using(oracle.open_library(lib_path)):
+        assert not _front_pins_pass(), f"planted mistake '{name}' was not caught"
 
 
 @pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
