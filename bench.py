@@ -17,6 +17,8 @@ Algorithmic accounting (fixed; it does not depend on the implementation):
                                  = 1,540, plus 64 KiB per (sequence, head) final state
   decode bytes per (row, head) per step = 2 x 65,536 (state read + write)
                                  + 3 x 256 (q, k, v) + 512 (g) + 4 (beta) + 256 (o) = 132,612
+                                 (+ 4,608 for the fused step's three bf16 conv caches,
+                                 read and rewritten; per-head weights are not counted)
 Roofline peaks: HBM 8.0 TB/s; bf16 dense matrix 2.5 PFLOP/s (2,516.6 TFLOP/s).
 """
 from __future__ import annotations
@@ -39,6 +41,7 @@ FLOP_PER_TOKEN_HEAD = 6 * D * D + C * (3 * D + 2 * D)          # 139,264
 BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 4 * D + 4                   # 1,540
 STATE_BYTES = D * D * 4                                        # 65,536
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 3 * 2 * D + 4 * D + 4 + 2 * D   # 132,612
+CONV_CACHE_BYTES_PER_HEAD = 2 * 3 * 3 * D * 2                              # 4,608 (read + write)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 
@@ -50,6 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-kernel", choices=("step", "fused"), default="step",
+                    help="decode leg: the plain step (default) or the fused step with the "
+                         "short-convolution front end and the output RMSNorm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains-per-core", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -118,17 +124,24 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
     return res
 
 
-def time_decode(kda, ki, steps, warmup=10):
+def time_decode(kda, ki, steps, warmup=10, kernel="step"):
     import torch
     cfg = ki.DECODE_CONFIGS[DECODE_WORKLOAD]
-    x = ki.make_decode_ring(cfg, device="cuda")
+    fused = kernel == "fused"
+    x = ki.make_decode_ring(cfg, device="cuda", raw_qk=fused)
     state = x["state"]
     o = torch.empty_like(x["q"][0])
+    front = ki.make_conv_front(cfg.batch, cfg.heads, cfg.dtype, device="cuda") if fused else None
 
     def step(t):
         r = t % cfg.ring
-        kda.recurrent_step(x["q"][r], x["k"][r], x["v"][r], x["g"][r], x["beta"][r], state,
-                           out=o)
+        if fused:
+            kda.fused_decode_step(x["q"][r], x["k"][r], x["v"][r], x["g"][r], x["beta"][r], state,
+                                  front["conv_cache"], front["conv_weight"],
+                                  norm_weight=front["norm_weight"], out=o)
+        else:
+            kda.recurrent_step(x["q"][r], x["k"][r], x["v"][r], x["g"][r], x["beta"][r], state,
+                               out=o)
 
     for t in range(warmup):
         step(t)
@@ -142,11 +155,13 @@ def time_decode(kda, ki, steps, warmup=10):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     heads = cfg.batch * cfg.heads
-    gbs = heads * DECODE_BYTES_PER_HEAD / (ms * 1e-3) / 1e9
-    del x, state
+    per_head = DECODE_BYTES_PER_HEAD + (CONV_CACHE_BYTES_PER_HEAD if fused else 0)
+    gbs = heads * per_head / (ms * 1e-3) / 1e9
+    del x, state, front
     torch.cuda.empty_cache()
     return dict(ms_per_step=ms, steps=steps, gb_per_s=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
-                bytes_per_step=heads * DECODE_BYTES_PER_HEAD, batch=cfg.batch, heads=cfg.heads)
+                bytes_per_step=heads * per_head, batch=cfg.batch, heads=cfg.heads,
+                kernel="fused_step_kernel" if fused else "recurrent_step_kernel")
 
 
 def cpu_baseline(x, chains_per_core, seconds, gp=None):
@@ -350,7 +365,7 @@ def main():
                      "bytes_per_launch": alg_bytes},
     }
     if not args.no_decode:
-        line["decode"] = time_decode(kda, ki, args.decode_steps)
+        line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel)
         line["decode"]["workload"] = DECODE_WORKLOAD
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds,

@@ -17,6 +17,8 @@ __all__ = [
     "chunk_fwd",
     "chunk_fwd_workspace_size",
     "recurrent_step",
+    "fused_decode_step",
+    "conv_cache_bytes",
     "state_io",
     "state_bytes",
     "library",
@@ -106,6 +108,34 @@ class RecurrentStepArgs(ctypes.Structure):
     ]
 
 
+class FusedStepArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("conv_weight", ctypes.c_void_p),
+        ("conv_cache", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32),
+        ("l2_eps", ctypes.c_float),
+        ("out_norm", ctypes.c_int32),
+        ("norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+        ("o", ctypes.c_void_p),
+        ("gate", Gate),
+    ]
+
+
+CONV_WIDTH = 4
+
 _LIB = None
 
 
@@ -122,6 +152,9 @@ def library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkFwdArgs),
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs), ctypes.c_void_p]
+    lib.kda_fused_decode_step.argtypes = [ctypes.POINTER(FusedStepArgs), ctypes.c_void_p]
+    lib.kda_conv_cache_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+    lib.kda_conv_cache_bytes.restype = ctypes.c_size_t
     lib.kda_state_io.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -326,6 +359,63 @@ def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=N
     a.gate = _gate(H, A_log, dt_bias, lower_bound, beta_logits)
     _check(lib.kda_recurrent_step(ctypes.byref(a), _stream(q)), "kda_recurrent_step")
     return o
+
+
+def fused_decode_step(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices=None,
+                      scale=1.0, l2_eps=1e-6, out_norm=True, norm_weight=None, norm_eps=1e-6,
+                      out=None, A_log=None, dt_bias=None, lower_bound=-5.0, beta_logits=False):
+    """One decode token per row with the front end (short convolution of q, k, v
+    continuing from ``conv_cache``, Swish, L2 norm of q and k), the recurrence and
+    the output RMSNorm, in one kernel; ``state`` and ``conv_cache`` are updated in
+    place.
+
+    q, k, v: [B, H, 128] raw projections (bf16 or fp32); g: [B, H, 128] fp32;
+    beta: [B, H] fp32; state: [slots, H, 128, 128] fp32; conv_cache:
+    [slots, 3, 3, H, 128] in q's dtype; conv_weight: [3, H, 128, 4] fp32;
+    norm_weight: [128] fp32 or None.  The gate arguments are those of chunk_fwd.
+    Returns o [B, H, 128].
+    """
+    lib = library()
+    _need(q, "q", ndim=3)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, dtype=q.dtype, ndim=3)
+    _need(g, "g", dtype=torch.float32, ndim=3)
+    _need(beta, "beta", dtype=torch.float32, ndim=2)
+    _need(state, "state", dtype=torch.float32, ndim=4)
+    _need(conv_cache, "conv_cache", dtype=q.dtype, ndim=5)
+    _need(conv_weight, "conv_weight", dtype=torch.float32, ndim=4)
+    B, H, D = q.shape
+    if conv_cache.shape[1:] != (3, CONV_WIDTH - 1, H, D) or conv_cache.shape[0] != state.shape[0]:
+        raise ValueError(f"conv_cache must be [{state.shape[0]}, 3, {CONV_WIDTH - 1}, {H}, {D}]")
+    if conv_weight.shape != (3, H, D, CONV_WIDTH):
+        raise ValueError(f"conv_weight must be [3, {H}, {D}, {CONV_WIDTH}]")
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", dtype=torch.float32)
+        if norm_weight.numel() != D:
+            raise ValueError(f"norm_weight must hold {D} values")
+    if state_indices is not None:
+        _need(state_indices, "state_indices", dtype=torch.int32, ndim=1)
+    o = out if out is not None else torch.empty_like(q)
+    a = FusedStepArgs()
+    a.batch, a.num_heads, a.head_dim = B, H, D
+    a.io_dtype = _dtype_code(q.dtype)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
+    a.conv_weight, a.conv_cache = conv_weight.data_ptr(), conv_cache.data_ptr()
+    a.state = state.data_ptr()
+    a.state_indices = None if state_indices is None else state_indices.data_ptr()
+    a.num_slots = state.shape[0]
+    a.l2_eps, a.out_norm, a.norm_eps = float(l2_eps), 1 if out_norm else 0, float(norm_eps)
+    a.norm_weight = None if norm_weight is None else norm_weight.data_ptr()
+    a.o = o.data_ptr()
+    a.gate = _gate(H, A_log, dt_bias, lower_bound, beta_logits)
+    _check(lib.kda_fused_decode_step(ctypes.byref(a), _stream(q)), "kda_fused_decode_step")
+    return o
+
+
+def conv_cache_bytes(num_heads: int, head_dim: int = 128,
+                     dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(library().kda_conv_cache_bytes(num_heads, head_dim, _dtype_code(dtype)))
 
 
 def state_io(op: int, dst, src=None, indices=None, count=None):

@@ -147,6 +147,38 @@ kda_status kda_recurrent_step(const kda_recurrent_step_args *a, void *stream) {
   return launch_status(kda::launch_recurrent_step(*a, (hipStream_t)stream));
 }
 
+size_t kda_conv_cache_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype) {
+  if (num_heads < 1 || head_dim < 1 || !valid_dtype(dtype)) return 0;
+  return (size_t)3 * (KDA_CONV_WIDTH - 1) * num_heads * head_dim * (dtype == KDA_F32 ? 4u : 2u);
+}
+
+kda_status kda_fused_decode_step(const kda_fused_step_args *a, void *stream) {
+  if (!a) return KDA_ERROR_INVALID_VALUE;
+  if (a->batch < 0 || a->num_heads < 1 || a->num_slots < 0) return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(a->io_dtype) || !isfinite(a->scale)) return KDA_ERROR_INVALID_VALUE;
+  if (a->head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
+  if ((int64_t)a->batch * a->num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if (!(a->l2_eps >= 0.f) || !isfinite(a->l2_eps) || !(a->norm_eps >= 0.f) ||
+      !isfinite(a->norm_eps))
+    return KDA_ERROR_INVALID_VALUE;
+  if (a->out_norm != 0 && a->out_norm != 1) return KDA_ERROR_INVALID_VALUE;
+  if (check_gate(a->gate, a->batch > 0) != KDA_SUCCESS) return KDA_ERROR_INVALID_VALUE;
+  if (!a->state_indices && a->batch > a->num_slots) return KDA_ERROR_INVALID_VALUE;
+  if (a->batch > 0) {
+    const uintptr_t es = a->io_dtype == KDA_F32 ? 4u : 2u;
+    const void *io[] = {a->q, a->k, a->v, a->o, a->conv_cache};
+    for (const void *p : io)
+      if (!p || !aligned(p, es)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->g || !aligned(a->g, 4) || !a->beta || !aligned(a->beta, 4))
+      return KDA_ERROR_INVALID_VALUE;
+    if (!a->conv_weight || !aligned16(a->conv_weight)) return KDA_ERROR_INVALID_VALUE;
+    if (a->norm_weight && !aligned(a->norm_weight, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->state || !aligned16(a->state)) return KDA_ERROR_INVALID_VALUE;
+    if (a->state_indices && ((uintptr_t)a->state_indices & 3u)) return KDA_ERROR_INVALID_VALUE;
+  }
+  return launch_status(kda::launch_fused_decode_step(*a, (hipStream_t)stream));
+}
+
 kda_status kda_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
                         int32_t src_slots, void *dst, kda_dtype dst_dtype, int32_t dst_slots,
                         const int32_t *indices, int32_t count, int32_t num_heads,

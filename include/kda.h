@@ -216,6 +216,70 @@ typedef struct kda_recurrent_step_args {
 kda_status kda_recurrent_step(const kda_recurrent_step_args *args, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Fused decode step: the layer's front end, the recurrence and the output
+ * normalisation in one kernel ([P3] section 4.5: one fused kernel covers short
+ * convolution, input normalisation, gating, the KDA recurrence and output
+ * normalisation; [P4] "Kimi Delta Attention": queries and keys come from a short
+ * convolution followed by Swish and L2 normalisation, values from a short
+ * convolution and Swish; [P1] "How KDA updates its state" and "What the hybrid
+ * saves": one ShortConv cache each for the query, key and value projections,
+ * kernel size 4).
+ *
+ * For each row b with slot s = state_indices[b] (s = b when NULL; rows whose
+ * slot is negative or >= num_slots are skipped) and head h:
+ *   for X = q, k, v (i = 0, 1, 2) and channel c, with the cache holding the three
+ *   previous raw inputs, oldest first:
+ *     y = sum_{j<4} conv_weight[i, h, c, j] * (cache[s, i, 0..2, h, c], X[b, h, c])_j
+ *     cache[s, i, ., h, c] <- (cache[s, i, 1, h, c], cache[s, i, 2, h, c], X[b, h, c])
+ *     X' = y * sigmoid(y)                                    (Swish)
+ *   q' <- q' / sqrt(|q'|^2 + l2_eps), k' likewise            (per head)
+ *   the step of kda_recurrent_step with q', k', v' (g and beta read per `gate`)
+ *   o <- o / sqrt(mean_c o_c^2 + norm_eps) * norm_weight[c]  (when out_norm)
+ * The cache holds raw inputs, so it round-trips exactly in io_dtype; the
+ * convolution, norms and recurrence run in fp32.  Two rows naming the same slot
+ * race (caller error; no out-of-bounds access results).
+ * ---------------------------------------------------------------------- */
+#define KDA_CONV_WIDTH 4
+
+typedef struct kda_fused_step_args {
+  int32_t batch;                  /* B >= 0 rows, one token each                         */
+  int32_t num_heads;              /* H >= 1                                              */
+  int32_t head_dim;               /* must be KDA_HEAD_DIM                                */
+  kda_dtype io_dtype;             /* dtype of q, k, v, o and the conv cache              */
+  float scale;
+  const void *q;                  /* [B, H, 128] io_dtype, projected, before the conv    */
+  const void *k;                  /* [B, H, 128] io_dtype                                */
+  const void *v;                  /* [B, H, 128] io_dtype                                */
+  const float *g;                 /* [B, H, 128] log-decay, or gate logits               */
+  const float *beta;              /* [B, H] beta, or beta logits                         */
+  const float *conv_weight;       /* [3, H, 128, 4] fp32 taps (q, k, v), oldest first    */
+  void *conv_cache;               /* [num_slots, 3, 3, H, 128] io_dtype, in place        */
+  float *state;                   /* [num_slots, H, 128, 128] fp32, in place             */
+  const int32_t *state_indices;   /* device [B] or NULL (identity, needs B <= num_slots) */
+                                  /* one slot indexes both the state and the conv cache  */
+  int32_t num_slots;
+  float l2_eps;                   /* >= 0, finite (1e-6 is the usual value)              */
+  int32_t out_norm;               /* 1 = RMSNorm the output, 0 = raw o                   */
+  const float *norm_weight;       /* [128] fp32 output-norm weight, or NULL = 1          */
+  float norm_eps;                 /* >= 0, finite                                        */
+  void *o;                        /* [B, H, 128] io_dtype                                */
+  kda_gate gate;                  /* how g and beta are read (zero = log-decay, beta)    */
+} kda_fused_step_args;
+
+/* Bytes of one slot's conv cache (3 caches x 3 inputs x H x head_dim elements of
+ * dtype): 216 KiB for 96 heads in bf16 ([P1] "What the hybrid saves").  0 for
+ * invalid input. */
+size_t kda_conv_cache_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype);
+
+/* Enqueue one fused decode step on `stream`.  Errors: KDA_ERROR_INVALID_VALUE for
+ * null or misaligned pointers (conv_weight and the state need 16 bytes, the
+ * others their element size), negative sizes, batch * num_heads beyond
+ * 2^31 - 1, batch > num_slots without state_indices, negative or non-finite
+ * epsilons, out_norm other than 0 or 1, and the gate checks of kda_chunk_fwd;
+ * KDA_ERROR_UNSUPPORTED for head_dim != 128. */
+kda_status kda_fused_decode_step(const kda_fused_step_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
  * State-pool copies ([P3] section 4.5: states are stored head by head
  * contiguously; a cache hit copies a read-only snapshot into the request's
  * private running state; new checkpoints are written to fresh slots).

@@ -23,6 +23,13 @@ per-head A_log ~ N(a_log_mean, a_log_std^2) and per-channel
 dt_bias ~ N(dt_mean, dt_std^2) (the pages give no initialisation; these are
 synthetic parameters of the right shapes).
 
+Decode front end (``raw_qk`` and ``make_conv_front``): q and k are the raw
+N(0, 1) projections (the kernel's short convolution, Swish and L2 norm make
+the unit vectors); conv taps ~ N(0, 0.5^2) per (input, head, channel, tap),
+caches ~ N(0, 1) (as if earlier tokens had been seen), cast to the I/O dtype;
+output-norm weight 1 + N(0, 0.1^2).  The pages give none of these
+distributions.
+
 Every tensor has its own generator seeded from (seed, tensor id), and large
 tensors are filled slice by slice (fixed slice size) so that no fp32 staging
 copy of a whole bf16 tensor is ever made.
@@ -39,7 +46,8 @@ import torch
 D = 128
 _SLICE_ROWS = 1 << 15  # rows of [rows, H, D] generated per step
 
-_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "s0": 6, "A_log": 7, "dt_bias": 8}
+_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "s0": 6, "A_log": 7, "dt_bias": 8,
+               "conv_w": 9, "conv_cache": 10, "norm_w": 11}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -219,10 +227,26 @@ def make_prefill(cfg: PrefillConfig, device="cpu", seed: int = 1001, dtype=None,
     return out
 
 
+def make_conv_front(slots: int, heads: int, dtype: str = "bf16", device="cpu",
+                    seed: int = 1011) -> dict:
+    """conv_cache [slots, 3, 3, H, 128] (I/O dtype), conv_weight [3, H, 128, 4] and
+    norm_weight [128] (fp32) for the fused decode step."""
+    w = torch.empty((3 * heads * D, 4), dtype=torch.float32, device=device)
+    _fill(w, _gen(device, seed, _TENSOR_IDS["conv_w"]), "normal")
+    w.mul_(0.5)
+    cache = torch.empty((slots * 3 * 3 * heads, D), dtype=torch_dtype(dtype), device=device)
+    _fill(cache, _gen(device, seed, _TENSOR_IDS["conv_cache"]), "normal")
+    nw = torch.empty((D, 1), dtype=torch.float32, device=device)
+    _fill(nw, _gen(device, seed, _TENSOR_IDS["norm_w"]), "normal")
+    nw.mul_(0.1).add_(1.0)
+    return {"conv_weight": w.view(3, heads, D, 4), "conv_cache": cache.view(slots, 3, 3, heads, D),
+            "norm_weight": nw.view(D)}
+
+
 def make_decode_ring(cfg: DecodeConfig, device="cpu", seed: int = 1005,
                      batch: Optional[int] = None, heads: Optional[int] = None,
                      ring: Optional[int] = None, gate_logits: bool = False,
-                     beta_logits: bool = False) -> dict:
+                     beta_logits: bool = False, raw_qk: bool = False) -> dict:
     """Per-step decode inputs for ``ring`` distinct steps plus the initial state pool.
 
     q, k, g: [ring, B, H, 128]; v: [ring, B, H, 128]; beta: [ring, B, H];
@@ -233,7 +257,8 @@ def make_decode_ring(cfg: DecodeConfig, device="cpu", seed: int = 1005,
     R = cfg.ring if ring is None else ring
     dt = torch_dtype(cfg.dtype)
     out = {}
-    for name, kind in (("q", "unit"), ("k", "unit"), ("v", "normal")):
+    for name, kind in (("q", "normal" if raw_qk else "unit"), ("k", "normal" if raw_qk else "unit"),
+                       ("v", "normal")):
         t = torch.empty((R * B, H, D), dtype=dt, device=device)
         _fill(t, _gen(device, seed, _TENSOR_IDS[name]), kind)
         out[name] = t.view(R, B, H, D)

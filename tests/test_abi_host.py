@@ -203,7 +203,8 @@ def test_ctypes_structs_match_the_header(tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
     structs = {"kda_chunk_fwd_args": kda.ChunkFwdArgs,
-               "kda_recurrent_step_args": kda.RecurrentStepArgs, "kda_gate": kda.Gate}
+               "kda_recurrent_step_args": kda.RecurrentStepArgs, "kda_gate": kda.Gate,
+               "kda_fused_step_args": kda.FusedStepArgs}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kda.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -224,3 +225,41 @@ def test_ctypes_structs_match_the_header(tmp_path):
         assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def test_conv_cache_bytes_match_page_accounting(lib):
+    """[P1] "What the hybrid saves": the three ShortConv caches of a 96-head layer
+    are 216 KiB in bf16."""
+    c = json.load(open(GOLDEN))["state_memory"]
+    assert lib.kda_conv_cache_bytes(c["heads"], c["head_dim"], kda.KDA_BF16) == \
+        c["conv_cache_bytes_per_layer"]
+    assert lib.kda_conv_cache_bytes(c["heads"], c["head_dim"], kda.KDA_F32) == \
+        2 * c["conv_cache_bytes_per_layer"]
+    assert lib.kda_conv_cache_bytes(0, 128, kda.KDA_BF16) == 0
+
+
+def test_fused_decode_step_rejects_invalid_arguments(lib):
+    def args(**kw):
+        a = kda.FusedStepArgs()
+        a.batch, a.num_heads, a.head_dim, a.io_dtype, a.scale = 4, 2, 128, kda.KDA_BF16, 1.0
+        fake = 1 << 20
+        a.q = a.k = a.v = a.g = a.beta = a.state = a.o = a.conv_cache = a.conv_weight = fake
+        a.num_slots, a.l2_eps, a.norm_eps, a.out_norm = 4, 1e-6, 1e-6, 1
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return a
+    f = lambda a: lib.kda_fused_decode_step(ctypes.byref(a), None)
+    assert f(args(head_dim=64)) == 2
+    assert f(args(batch=-1)) == 1
+    assert f(args(num_slots=3)) == 1
+    assert f(args(conv_cache=0)) == 1
+    assert f(args(conv_weight=(1 << 20) + 4)) == 1  # needs 16 bytes
+    assert f(args(conv_cache=(1 << 20) + 1)) == 1
+    assert f(args(l2_eps=-1.0)) == 1
+    assert f(args(norm_eps=float("inf"))) == 1
+    assert f(args(out_norm=2)) == 1
+    assert f(args(norm_weight=(1 << 20) + 2)) == 1
+    assert f(args(batch=0, q=0, conv_cache=0)) == 0  # nothing to do
+    a = args()
+    a.gate.mode = 1  # lower-bounded gate without A_log
+    assert f(a) == 1
