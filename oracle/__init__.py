@@ -34,6 +34,7 @@ __all__ = [
     "l2norm",
     "rmsnorm",
     "fused_decode_step",
+    "spec_verify_step",
     "max_threads",
     "load",
     "open_library",
@@ -381,6 +382,51 @@ def fused_decode_step(q_in, k_in, v_in, g, beta, conv_w, conv_cache, state_pool,
     if out_norm:
         live = slots >= 0
         o[live] = rmsnorm(o[live], norm_weight, norm_eps)
+    return o, pool, cache
+
+
+def spec_verify_step(new, replay, num_replay, conv_w, conv_cache, state_pool, slot_idx=None,
+                     **kw):
+    """Speculative-decode verification with replay ("Kimi K3 -- Training and
+    Infrastructure Notes", section 4.5, KDA decoding: the state after an accepted
+    draft prefix is determined by the drafts' projected inputs, so only those are
+    kept; the accepted tokens are replayed to rebuild the state, the state of the
+    verified tokens is written back, and the replayed tokens and the next window
+    run in one recurrent loop).
+
+    Per row b with slot s (skipped when negative): first the first num_replay[b]
+    tokens of ``replay`` (the previous window's projected inputs) go through
+    ``fused_decode_step`` in order; the state and conv cache reached are the ones
+    written back.  Then the T tokens of ``new`` go through the same steps from
+    there, and their outputs are returned; the state they reach is dropped.
+
+    new, replay: dicts of q, k, v, g [B, T, H, K] and beta [B, T, H] (replay may
+    have a different T, or be None with num_replay all zero); num_replay: [B];
+    the other arguments as in ``fused_decode_step``.
+    Returns (o [B, T, H, V], new state_pool, new conv_cache).
+    """
+    nq = _f64(new["q"], "q")
+    B, T, H, K = nq.shape
+    slots = np.arange(B) if slot_idx is None else np.asarray(slot_idx).astype(np.int64)
+    num_replay = np.asarray(num_replay).astype(np.int64)
+    pool = np.array(_f64(state_pool, "state_pool"), copy=True)
+    cache = np.array(_f64(conv_cache, "conv_cache"), copy=True)
+    V = pool.shape[-1]
+    o = np.full((B, T, H, V), np.nan)
+    names = ("q", "k", "v", "g", "beta")
+    for b in range(B):
+        s = int(slots[b])
+        if s < 0:
+            continue
+        st, cc = pool[s:s + 1], cache[s:s + 1]
+        for t in range(int(num_replay[b])):
+            args = [_f64(replay[n], n)[b, t][None] for n in names]
+            _, st, cc = fused_decode_step(*args, conv_w, cc, st, **kw)
+        pool[s:s + 1], cache[s:s + 1] = st, cc  # written back
+        for t in range(T):
+            args = [_f64(new[n], n)[b, t][None] for n in names]
+            o_t, st, cc = fused_decode_step(*args, conv_w, cc, st, **kw)
+            o[b, t] = o_t[0]
     return o, pool, cache
 
 

@@ -538,6 +538,70 @@ def test_fused_decode_steps_equal_whole_sequence_front_end():
     np.testing.assert_array_equal(cache[0, 0], raw[0][-(W - 1):])
 
 
+def _spec_inputs(rng, B, T, H, K):
+    return {"q": rng.standard_normal((B, T, H, K)), "k": rng.standard_normal((B, T, H, K)),
+            "v": rng.standard_normal((B, T, H, K)),
+            "g": -np.logaddexp(0.0, rng.standard_normal((B, T, H, K))),
+            "beta": 1 / (1 + np.exp(-rng.standard_normal((B, T, H))))}
+
+
+def test_spec_verify_replay_equals_accepted_token_stream():
+    """Two verification rounds with replay: the committed state and cache equal
+    plain fused steps over exactly the accepted tokens, and each window's outputs
+    equal plain fused steps from the committed point (the draft tokens that are
+    rejected leave no trace)."""
+    rng = np.random.default_rng(31)
+    B, T, H, K = 3, 3, 2, 4
+    w = rng.standard_normal((3, H, K, 4))
+    pool0 = rng.standard_normal((B, H, K, K)) * 0.1
+    cache0 = rng.standard_normal((B, 3, 3, H, K))
+    win1, win2 = _spec_inputs(rng, B, T, H, K), _spec_inputs(rng, B, T, H, K)
+    acc = np.array([0, 2, 3])  # tokens of window 1 accepted per row
+    o1, pool1, cache1 = oracle.spec_verify_step(win1, None, np.zeros(B), w, cache0, pool0)
+    assert np.array_equal(pool1, pool0) and np.array_equal(cache1, cache0)
+    o2, pool2, cache2 = oracle.spec_verify_step(win2, win1, acc, w, cache1, pool1)
+    for b in range(B):
+        st, cc = pool0[b:b + 1], cache0[b:b + 1]
+        for t in range(T):  # window 1's outputs: plain steps from the committed point
+            args = [win1[n][b, t][None] for n in ("q", "k", "v", "g", "beta")]
+            o_t, st, cc = oracle.fused_decode_step(*args, w, cc, st)
+            np.testing.assert_allclose(o1[b, t], o_t[0], rtol=1e-13, atol=1e-14)
+        st, cc = pool0[b:b + 1], cache0[b:b + 1]
+        for t in range(int(acc[b])):
+            args = [win1[n][b, t][None] for n in ("q", "k", "v", "g", "beta")]
+            _, st, cc = oracle.fused_decode_step(*args, w, cc, st)
+        np.testing.assert_allclose(pool2[b], st[0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_array_equal(cache2[b], cc[0])
+        for t in range(T):
+            args = [win2[n][b, t][None] for n in ("q", "k", "v", "g", "beta")]
+            o_t, st, cc = oracle.fused_decode_step(*args, w, cc, st)
+            np.testing.assert_allclose(o2[b, t], o_t[0], rtol=1e-13, atol=1e-14)
+
+
+def test_spec_verify_one_token_window_is_the_decode_step():
+    """A window of one new token with nothing to replay is one fused step, except
+    that the state and cache are not advanced; replaying that token next time
+    advances them exactly as the step does."""
+    rng = np.random.default_rng(32)
+    B, H, K = 2, 2, 4
+    w = rng.standard_normal((3, H, K, 4))
+    pool0 = rng.standard_normal((B, H, K, K)) * 0.1
+    cache0 = rng.standard_normal((B, 3, 3, H, K))
+    win = _spec_inputs(rng, B, 1, H, K)
+    o, pool1, cache1 = oracle.spec_verify_step(win, None, np.zeros(B), w, cache0, pool0,
+                                               norm_weight=np.ones(K) * 2)
+    args = [win[n][:, 0] for n in ("q", "k", "v", "g", "beta")]
+    o_ref, pool_ref, cache_ref = oracle.fused_decode_step(*args, w, cache0, pool0,
+                                                          norm_weight=np.ones(K) * 2)
+    np.testing.assert_array_equal(o[:, 0], o_ref)
+    assert np.array_equal(pool1, pool0)
+    _, pool2, cache2 = oracle.spec_verify_step(_spec_inputs(rng, B, 1, H, K), win,
+                                               np.ones(B), w, cache1, pool1,
+                                               norm_weight=np.ones(K) * 2)
+    np.testing.assert_array_equal(pool2, pool_ref)
+    np.testing.assert_array_equal(cache2, cache_ref)
+
+
 # ------------------------------------------- planted mistakes must be caught
 def _pins_pass():
     """Run a compact set of the pins above; True if all hold."""
