@@ -53,9 +53,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--decode-kernel", choices=("step", "fused"), default="step",
-                    help="decode leg: the plain step (default) or the fused step with the "
-                         "short-convolution front end and the output RMSNorm")
+    ap.add_argument("--decode-kernel", choices=("step", "fused", "spec"), default="step",
+                    help="decode leg: the plain step (default), the fused step with the "
+                         "short-convolution front end and the output RMSNorm, or the "
+                         "speculative-decode verification (replay of a --spec-window-token "
+                         "window, all accepted, plus a new window of as many tokens)")
+    ap.add_argument("--spec-window", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains-per-core", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -124,18 +127,31 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
     return res
 
 
-def time_decode(kda, ki, steps, warmup=10, kernel="step"):
+def time_decode(kda, ki, steps, warmup=10, kernel="step", window=4):
     import torch
     cfg = ki.DECODE_CONFIGS[DECODE_WORKLOAD]
-    fused = kernel == "fused"
+    fused = kernel != "step"
     x = ki.make_decode_ring(cfg, device="cuda", raw_qk=fused)
     state = x["state"]
     o = torch.empty_like(x["q"][0])
     front = ki.make_conv_front(cfg.batch, cfg.heads, cfg.dtype, device="cuda") if fused else None
+    if kernel == "spec":  # windows of `window` tokens: [B, T, H, ...], two alternating
+        wins = []
+        for w in range(2):
+            xw = ki.make_decode_ring(cfg, device="cuda", ring=window, seed=2000 + w, raw_qk=True)
+            wins.append({n: xw[n].transpose(0, 1).contiguous()
+                         for n in ("q", "k", "v", "g", "beta")})
+            del xw
+        o = torch.empty_like(wins[0]["q"])
 
     def step(t):
         r = t % cfg.ring
-        if fused:
+        if kernel == "spec":
+            new, prev = wins[t % 2], wins[(t + 1) % 2]
+            kda.spec_verify_step(new["q"], new["k"], new["v"], new["g"], new["beta"], state,
+                                 front["conv_cache"], front["conv_weight"], replay=prev,
+                                 norm_weight=front["norm_weight"], out=o)
+        elif fused:
             kda.fused_decode_step(x["q"][r], x["k"][r], x["v"][r], x["g"][r], x["beta"][r], state,
                                   front["conv_cache"], front["conv_weight"],
                                   norm_weight=front["norm_weight"], out=o)
@@ -156,12 +172,21 @@ def time_decode(kda, ki, steps, warmup=10, kernel="step"):
     ms = start.elapsed_time(end) / steps
     heads = cfg.batch * cfg.heads
     per_head = DECODE_BYTES_PER_HEAD + (CONV_CACHE_BYTES_PER_HEAD if fused else 0)
+    extra = {}
+    if kernel == "spec":  # replayed and new tokens' inputs, new tokens' outputs
+        tok_in = 3 * 2 * D + 4 * D + 4
+        per_head = 2 * STATE_BYTES + CONV_CACHE_BYTES_PER_HEAD + 2 * window * tok_in + \
+            window * 2 * D
+        extra = {"window": window, "replayed": window,
+                 "tokens_verified_per_s": cfg.batch * window / (ms * 1e-3)}
     gbs = heads * per_head / (ms * 1e-3) / 1e9
     del x, state, front
     torch.cuda.empty_cache()
     return dict(ms_per_step=ms, steps=steps, gb_per_s=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
                 bytes_per_step=heads * per_head, batch=cfg.batch, heads=cfg.heads,
-                kernel="fused_step_kernel" if fused else "recurrent_step_kernel")
+                kernel="decode_loop_kernel", entry={"step": "kda_recurrent_step",
+                "fused": "kda_fused_decode_step", "spec": "kda_spec_verify_step"}[kernel],
+                **extra)
 
 
 def cpu_baseline(x, chains_per_core, seconds, gp=None):
@@ -365,7 +390,8 @@ def main():
                      "bytes_per_launch": alg_bytes},
     }
     if not args.no_decode:
-        line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel)
+        line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel,
+                                     window=args.spec_window)
         line["decode"]["workload"] = DECODE_WORKLOAD
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds,

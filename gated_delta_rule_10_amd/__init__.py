@@ -18,6 +18,7 @@ __all__ = [
     "chunk_fwd_workspace_size",
     "recurrent_step",
     "fused_decode_step",
+    "spec_verify_step",
     "conv_cache_bytes",
     "state_io",
     "state_bytes",
@@ -134,6 +135,20 @@ class FusedStepArgs(ctypes.Structure):
     ]
 
 
+class SpecVerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("step", FusedStepArgs),
+        ("window", ctypes.c_int32),
+        ("replay_q", ctypes.c_void_p),
+        ("replay_k", ctypes.c_void_p),
+        ("replay_v", ctypes.c_void_p),
+        ("replay_g", ctypes.c_void_p),
+        ("replay_beta", ctypes.c_void_p),
+        ("replay_window", ctypes.c_int32),
+        ("num_replay", ctypes.c_void_p),
+    ]
+
+
 CONV_WIDTH = 4
 
 _LIB = None
@@ -153,6 +168,7 @@ def library(path: str = LIB_PATH):
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs), ctypes.c_void_p]
     lib.kda_fused_decode_step.argtypes = [ctypes.POINTER(FusedStepArgs), ctypes.c_void_p]
+    lib.kda_spec_verify_step.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     lib.kda_conv_cache_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
     lib.kda_conv_cache_bytes.restype = ctypes.c_size_t
     lib.kda_state_io.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
@@ -361,6 +377,48 @@ def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=N
     return o
 
 
+def _fused_args(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices, scale,
+                l2_eps, out_norm, norm_weight, norm_eps, o, A_log, dt_bias, lower_bound,
+                beta_logits, token_dims):
+    """Check and fill kda_fused_step_args; q, k, v, g are [B, (T,) H, 128]."""
+    _need(q, "q", ndim=token_dims + 1)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, dtype=q.dtype, ndim=token_dims + 1)
+    _need(g, "g", dtype=torch.float32, ndim=token_dims + 1)
+    _need(beta, "beta", dtype=torch.float32, ndim=token_dims)
+    _need(state, "state", dtype=torch.float32, ndim=4)
+    _need(conv_cache, "conv_cache", dtype=q.dtype, ndim=5)
+    _need(conv_weight, "conv_weight", dtype=torch.float32, ndim=4)
+    B, H, D = q.shape[0], q.shape[-2], q.shape[-1]
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape or \
+            beta.shape != q.shape[:-1]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    if conv_cache.shape[1:] != (3, CONV_WIDTH - 1, H, D) or conv_cache.shape[0] != state.shape[0]:
+        raise ValueError(f"conv_cache must be [{state.shape[0]}, 3, {CONV_WIDTH - 1}, {H}, {D}]")
+    if conv_weight.shape != (3, H, D, CONV_WIDTH):
+        raise ValueError(f"conv_weight must be [3, {H}, {D}, {CONV_WIDTH}]")
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", dtype=torch.float32)
+        if norm_weight.numel() != D:
+            raise ValueError(f"norm_weight must hold {D} values")
+    if state_indices is not None:
+        _need(state_indices, "state_indices", dtype=torch.int32, ndim=1)
+    a = FusedStepArgs()
+    a.batch, a.num_heads, a.head_dim = B, H, D
+    a.io_dtype = _dtype_code(q.dtype)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
+    a.conv_weight, a.conv_cache = conv_weight.data_ptr(), conv_cache.data_ptr()
+    a.state = state.data_ptr()
+    a.state_indices = None if state_indices is None else state_indices.data_ptr()
+    a.num_slots = state.shape[0]
+    a.l2_eps, a.out_norm, a.norm_eps = float(l2_eps), 1 if out_norm else 0, float(norm_eps)
+    a.norm_weight = None if norm_weight is None else norm_weight.data_ptr()
+    a.o = o.data_ptr()
+    a.gate = _gate(H, A_log, dt_bias, lower_bound, beta_logits)
+    return a
+
+
 def fused_decode_step(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices=None,
                       scale=1.0, l2_eps=1e-6, out_norm=True, norm_weight=None, norm_eps=1e-6,
                       out=None, A_log=None, dt_bias=None, lower_bound=-5.0, beta_logits=False):
@@ -376,40 +434,56 @@ def fused_decode_step(q, k, v, g, beta, state, conv_cache, conv_weight, state_in
     Returns o [B, H, 128].
     """
     lib = library()
-    _need(q, "q", ndim=3)
-    for name, t in (("k", k), ("v", v)):
-        _need(t, name, dtype=q.dtype, ndim=3)
-    _need(g, "g", dtype=torch.float32, ndim=3)
-    _need(beta, "beta", dtype=torch.float32, ndim=2)
-    _need(state, "state", dtype=torch.float32, ndim=4)
-    _need(conv_cache, "conv_cache", dtype=q.dtype, ndim=5)
-    _need(conv_weight, "conv_weight", dtype=torch.float32, ndim=4)
-    B, H, D = q.shape
-    if conv_cache.shape[1:] != (3, CONV_WIDTH - 1, H, D) or conv_cache.shape[0] != state.shape[0]:
-        raise ValueError(f"conv_cache must be [{state.shape[0]}, 3, {CONV_WIDTH - 1}, {H}, {D}]")
-    if conv_weight.shape != (3, H, D, CONV_WIDTH):
-        raise ValueError(f"conv_weight must be [3, {H}, {D}, {CONV_WIDTH}]")
-    if norm_weight is not None:
-        _need(norm_weight, "norm_weight", dtype=torch.float32)
-        if norm_weight.numel() != D:
-            raise ValueError(f"norm_weight must hold {D} values")
-    if state_indices is not None:
-        _need(state_indices, "state_indices", dtype=torch.int32, ndim=1)
     o = out if out is not None else torch.empty_like(q)
-    a = FusedStepArgs()
-    a.batch, a.num_heads, a.head_dim = B, H, D
-    a.io_dtype = _dtype_code(q.dtype)
-    a.scale = float(scale)
-    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
-    a.conv_weight, a.conv_cache = conv_weight.data_ptr(), conv_cache.data_ptr()
-    a.state = state.data_ptr()
-    a.state_indices = None if state_indices is None else state_indices.data_ptr()
-    a.num_slots = state.shape[0]
-    a.l2_eps, a.out_norm, a.norm_eps = float(l2_eps), 1 if out_norm else 0, float(norm_eps)
-    a.norm_weight = None if norm_weight is None else norm_weight.data_ptr()
-    a.o = o.data_ptr()
-    a.gate = _gate(H, A_log, dt_bias, lower_bound, beta_logits)
+    a = _fused_args(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices, scale,
+                    l2_eps, out_norm, norm_weight, norm_eps, o, A_log, dt_bias, lower_bound,
+                    beta_logits, token_dims=2)
     _check(lib.kda_fused_decode_step(ctypes.byref(a), _stream(q)), "kda_fused_decode_step")
+    return o
+
+
+def spec_verify_step(q, k, v, g, beta, state, conv_cache, conv_weight, replay=None,
+                     num_replay=None, state_indices=None, scale=1.0, l2_eps=1e-6,
+                     out_norm=True, norm_weight=None, norm_eps=1e-6, out=None, A_log=None,
+                     dt_bias=None, lower_bound=-5.0, beta_logits=False):
+    """Speculative-decode verification with replay, one kernel.
+
+    q, k, v, g: [B, T, H, 128] the new window (raw projections, log-decay or gate
+    logits); beta: [B, T, H].  ``replay``: dict of the previous window's q, k, v,
+    g [B, Tr, H, 128] and beta [B, Tr, H], or None; ``num_replay``: int32 [B] on
+    the device (accepted tokens of the replay window, clamped to [0, Tr]) or None
+    for all.  The accepted replay tokens advance ``state`` and ``conv_cache`` in
+    place; the new window's outputs are returned ([B, T, H, 128]) and its state
+    is dropped.  Other arguments as in fused_decode_step.
+    """
+    lib = library()
+    o = out if out is not None else torch.empty_like(q)
+    a = _fused_args(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices, scale,
+                    l2_eps, out_norm, norm_weight, norm_eps, o, A_log, dt_bias, lower_bound,
+                    beta_logits, token_dims=3)
+    va = SpecVerifyArgs()
+    va.step = a
+    va.window = q.shape[1]
+    if replay is not None:
+        rq = replay["q"]
+        _need(rq, "replay q", dtype=q.dtype, ndim=4)
+        if rq.shape[0] != q.shape[0] or rq.shape[2:] != q.shape[2:]:
+            raise ValueError("replay window must be [B, Tr, H, 128]")
+        for name in ("k", "v"):
+            _need(replay[name], f"replay {name}", dtype=q.dtype, ndim=4)
+            if replay[name].shape != rq.shape:
+                raise ValueError("replay shape mismatch")
+        _need(replay["g"], "replay g", dtype=torch.float32, ndim=4)
+        _need(replay["beta"], "replay beta", dtype=torch.float32, ndim=3)
+        if replay["g"].shape != rq.shape or replay["beta"].shape != rq.shape[:-1]:
+            raise ValueError("replay shape mismatch")
+        va.replay_q, va.replay_k, va.replay_v = (replay[n].data_ptr() for n in ("q", "k", "v"))
+        va.replay_g, va.replay_beta = replay["g"].data_ptr(), replay["beta"].data_ptr()
+        va.replay_window = rq.shape[1]
+    if num_replay is not None:
+        _need(num_replay, "num_replay", dtype=torch.int32, ndim=1)
+        va.num_replay = num_replay.data_ptr()
+    _check(lib.kda_spec_verify_step(ctypes.byref(va), _stream(q)), "kda_spec_verify_step")
     return o
 
 

@@ -76,6 +76,38 @@ kda_status check_chunk_args(const kda_chunk_fwd_args *a, int64_t *total_tokens,
   return KDA_SUCCESS;
 }
 
+// Checks of the fused-step arguments; the token pointers (q, k, v, g, beta, o)
+// are checked only when `tokens` is set.
+kda_status check_fused_args(const kda_fused_step_args *a, bool tokens) {
+  if (!a) return KDA_ERROR_INVALID_VALUE;
+  if (a->batch < 0 || a->num_heads < 1 || a->num_slots < 0) return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(a->io_dtype) || !isfinite(a->scale)) return KDA_ERROR_INVALID_VALUE;
+  if (a->head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
+  if ((int64_t)a->batch * a->num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if (!(a->l2_eps >= 0.f) || !isfinite(a->l2_eps) || !(a->norm_eps >= 0.f) ||
+      !isfinite(a->norm_eps))
+    return KDA_ERROR_INVALID_VALUE;
+  if (a->out_norm != 0 && a->out_norm != 1) return KDA_ERROR_INVALID_VALUE;
+  if (check_gate(a->gate, a->batch > 0) != KDA_SUCCESS) return KDA_ERROR_INVALID_VALUE;
+  if (!a->state_indices && a->batch > a->num_slots) return KDA_ERROR_INVALID_VALUE;
+  if (a->batch > 0) {
+    const uintptr_t es = a->io_dtype == KDA_F32 ? 4u : 2u;
+    if (tokens) {
+      const void *io[] = {a->q, a->k, a->v, a->o};
+      for (const void *p : io)
+        if (!p || !aligned(p, es)) return KDA_ERROR_INVALID_VALUE;
+      if (!a->g || !aligned(a->g, 4) || !a->beta || !aligned(a->beta, 4))
+        return KDA_ERROR_INVALID_VALUE;
+    }
+    if (!a->conv_cache || !aligned(a->conv_cache, es)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->conv_weight || !aligned16(a->conv_weight)) return KDA_ERROR_INVALID_VALUE;
+    if (a->norm_weight && !aligned(a->norm_weight, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->state || !aligned16(a->state)) return KDA_ERROR_INVALID_VALUE;
+    if (a->state_indices && ((uintptr_t)a->state_indices & 3u)) return KDA_ERROR_INVALID_VALUE;
+  }
+  return KDA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,30 +185,30 @@ size_t kda_conv_cache_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype
 }
 
 kda_status kda_fused_decode_step(const kda_fused_step_args *a, void *stream) {
-  if (!a) return KDA_ERROR_INVALID_VALUE;
-  if (a->batch < 0 || a->num_heads < 1 || a->num_slots < 0) return KDA_ERROR_INVALID_VALUE;
-  if (!valid_dtype(a->io_dtype) || !isfinite(a->scale)) return KDA_ERROR_INVALID_VALUE;
-  if (a->head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
-  if ((int64_t)a->batch * a->num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
-  if (!(a->l2_eps >= 0.f) || !isfinite(a->l2_eps) || !(a->norm_eps >= 0.f) ||
-      !isfinite(a->norm_eps))
-    return KDA_ERROR_INVALID_VALUE;
-  if (a->out_norm != 0 && a->out_norm != 1) return KDA_ERROR_INVALID_VALUE;
-  if (check_gate(a->gate, a->batch > 0) != KDA_SUCCESS) return KDA_ERROR_INVALID_VALUE;
-  if (!a->state_indices && a->batch > a->num_slots) return KDA_ERROR_INVALID_VALUE;
-  if (a->batch > 0) {
-    const uintptr_t es = a->io_dtype == KDA_F32 ? 4u : 2u;
-    const void *io[] = {a->q, a->k, a->v, a->o, a->conv_cache};
+  const kda_status st = check_fused_args(a, true);
+  if (st != KDA_SUCCESS) return st;
+  return launch_status(kda::launch_fused_decode_step(*a, (hipStream_t)stream));
+}
+
+kda_status kda_spec_verify_step(const kda_spec_verify_args *v, void *stream) {
+  if (!v) return KDA_ERROR_INVALID_VALUE;
+  if (v->window < 0 || v->replay_window < 0) return KDA_ERROR_INVALID_VALUE;
+  const kda_status st = check_fused_args(&v->step, v->window > 0);
+  if (st != KDA_SUCCESS) return st;
+  const kda_fused_step_args &a = v->step;
+  const int64_t tmax = v->window > v->replay_window ? v->window : v->replay_window;
+  if ((int64_t)a.batch * tmax * a.num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if (a.batch > 0 && v->replay_window > 0) {
+    const uintptr_t es = a.io_dtype == KDA_F32 ? 4u : 2u;
+    const void *io[] = {v->replay_q, v->replay_k, v->replay_v};
     for (const void *p : io)
       if (!p || !aligned(p, es)) return KDA_ERROR_INVALID_VALUE;
-    if (!a->g || !aligned(a->g, 4) || !a->beta || !aligned(a->beta, 4))
+    if (!v->replay_g || !aligned(v->replay_g, 4) || !v->replay_beta ||
+        !aligned(v->replay_beta, 4))
       return KDA_ERROR_INVALID_VALUE;
-    if (!a->conv_weight || !aligned16(a->conv_weight)) return KDA_ERROR_INVALID_VALUE;
-    if (a->norm_weight && !aligned(a->norm_weight, 4)) return KDA_ERROR_INVALID_VALUE;
-    if (!a->state || !aligned16(a->state)) return KDA_ERROR_INVALID_VALUE;
-    if (a->state_indices && ((uintptr_t)a->state_indices & 3u)) return KDA_ERROR_INVALID_VALUE;
   }
-  return launch_status(kda::launch_fused_decode_step(*a, (hipStream_t)stream));
+  if (v->num_replay && ((uintptr_t)v->num_replay & 3u)) return KDA_ERROR_INVALID_VALUE;
+  return launch_status(kda::launch_spec_verify(*v, (hipStream_t)stream));
 }
 
 kda_status kda_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,

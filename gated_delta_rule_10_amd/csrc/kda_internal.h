@@ -10,11 +10,12 @@
 
 namespace kda {
 
-// Decode step: two workgroups per (row, head).
+// Decode (one loop kernel, one workgroup per (row, head)): the plain step, the
+// fused step (front end + step + output norm) and the speculative-decode
+// verification with replay.
 hipError_t launch_recurrent_step(const kda_recurrent_step_args &a, hipStream_t stream);
-
-// Fused decode step (front end + step + output norm): one workgroup per (row, head).
 hipError_t launch_fused_decode_step(const kda_fused_step_args &a, hipStream_t stream);
+hipError_t launch_spec_verify(const kda_spec_verify_args &v, hipStream_t stream);
 
 // State pool copy/convert/zero.
 hipError_t launch_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,

@@ -280,6 +280,49 @@ size_t kda_conv_cache_bytes(int32_t num_heads, int32_t head_dim, kda_dtype dtype
 kda_status kda_fused_decode_step(const kda_fused_step_args *args, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Speculative-decode verification with replay ([P3] section 4.5, KDA decoding:
+ * after verification rejects some drafted tokens the in-place state has run past
+ * the last accepted one; instead of a state snapshot per draft position, only the
+ * drafts' projected inputs are kept, the accepted tokens are replayed to rebuild
+ * the state on chip, the state of the verified tokens is written back, and the
+ * replayed tokens and the next draft window share one recurrent loop in one
+ * kernel with the front end and the output normalisation).
+ *
+ * The caller keeps the previous call's window inputs (q, k, v, g, beta of
+ * `replay_window` tokens per row) and passes them back with the number of those
+ * tokens that were accepted.  For each row b with slot s (as kda_fused_decode_step)
+ * and head h, in one loop:
+ *   1. the first n_b = clamp(num_replay[b], 0, replay_window) replay tokens
+ *      (all replay_window when num_replay is NULL) run through the fused step in
+ *      order, without outputs; if n_b > 0 the state and the conv cache reached
+ *      are written back to slot s (n_b = 0 leaves both untouched);
+ *   2. the `window` new tokens run through the fused step from there, their
+ *      outputs are written to o, and the state and conv window they reach are
+ *      dropped.
+ * The state is read once and written at most once per call, however many tokens
+ * run.  The fields of `step` keep their meaning except that q, k, v, g, o are
+ * [B, window, H, 128] and beta [B, window, H].
+ * ---------------------------------------------------------------------- */
+typedef struct kda_spec_verify_args {
+  kda_fused_step_args step;       /* the new window and everything shared            */
+  int32_t window;                 /* new tokens per row (>= 0)                           */
+  const void *replay_q;           /* [B, replay_window, H, 128] io_dtype                 */
+  const void *replay_k;
+  const void *replay_v;
+  const float *replay_g;          /* [B, replay_window, H, 128] (read per step.gate)     */
+  const float *replay_beta;       /* [B, replay_window, H]                               */
+  int32_t replay_window;          /* >= 0; replay pointers may be NULL when 0            */
+  const int32_t *num_replay;      /* device [B] accepted tokens to replay, or NULL = all */
+} kda_spec_verify_args;
+
+/* Enqueue one verification on `stream`.  Errors: those of kda_fused_decode_step
+ * (for step, whose token pointers are checked when window > 0), negative
+ * window or replay_window, missing or misaligned replay pointers when
+ * replay_window > 0, a misaligned num_replay, and B * max(window,
+ * replay_window) * H beyond 2^31 - 1. */
+kda_status kda_spec_verify_step(const kda_spec_verify_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
  * State-pool copies ([P3] section 4.5: states are stored head by head
  * contiguously; a cache hit copies a read-only snapshot into the request's
  * private running state; new checkpoints are written to fresh slots).

@@ -395,7 +395,7 @@ def spec_verify_step(new, replay, num_replay, conv_w, conv_cache, state_pool, sl
     run in one recurrent loop).
 
     Per row b with slot s (skipped when negative): first the first num_replay[b]
-    tokens of ``replay`` (the previous window's projected inputs) go through
+    (clamped to [0, Tr]) tokens of ``replay`` (the previous window's projected inputs) go through
     ``fused_decode_step`` in order; the state and conv cache reached are the ones
     written back.  Then the T tokens of ``new`` go through the same steps from
     there, and their outputs are returned; the state they reach is dropped.
@@ -419,7 +419,8 @@ def spec_verify_step(new, replay, num_replay, conv_w, conv_cache, state_pool, sl
         if s < 0:
             continue
         st, cc = pool[s:s + 1], cache[s:s + 1]
-        for t in range(int(num_replay[b])):
+        n_rep = 0 if replay is None else min(max(int(num_replay[b]), 0), replay["q"].shape[1])
+        for t in range(n_rep):
             args = [_f64(replay[n], n)[b, t][None] for n in names]
             _, st, cc = fused_decode_step(*args, conv_w, cc, st, **kw)
         pool[s:s + 1], cache[s:s + 1] = st, cc  # written back

@@ -204,7 +204,8 @@ def test_ctypes_structs_match_the_header(tmp_path):
         pytest.skip("gcc not available")
     structs = {"kda_chunk_fwd_args": kda.ChunkFwdArgs,
                "kda_recurrent_step_args": kda.RecurrentStepArgs, "kda_gate": kda.Gate,
-               "kda_fused_step_args": kda.FusedStepArgs}
+               "kda_fused_step_args": kda.FusedStepArgs,
+               "kda_spec_verify_args": kda.SpecVerifyArgs}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kda.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -263,3 +264,31 @@ def test_fused_decode_step_rejects_invalid_arguments(lib):
     a = args()
     a.gate.mode = 1  # lower-bounded gate without A_log
     assert f(a) == 1
+
+
+def test_spec_verify_rejects_invalid_arguments(lib):
+    def args(**kw):
+        va = kda.SpecVerifyArgs()
+        a = va.step
+        a.batch, a.num_heads, a.head_dim, a.io_dtype, a.scale = 4, 2, 128, kda.KDA_BF16, 1.0
+        fake = 1 << 20
+        a.q = a.k = a.v = a.g = a.beta = a.state = a.o = a.conv_cache = a.conv_weight = fake
+        a.num_slots, a.l2_eps, a.norm_eps, a.out_norm = 4, 1e-6, 1e-6, 1
+        va.window, va.replay_window = 3, 3
+        va.replay_q = va.replay_k = va.replay_v = va.replay_g = va.replay_beta = fake
+        for k_, v_ in kw.items():
+            setattr(va, k_, v_)
+        return va
+    f = lambda va: lib.kda_spec_verify_step(ctypes.byref(va), None)
+    assert f(args(window=-1)) == 1
+    assert f(args(replay_window=-2)) == 1
+    assert f(args(replay_g=0)) == 1
+    assert f(args(replay_q=(1 << 20) + 1)) == 1
+    assert f(args(num_replay=(1 << 20) + 2)) == 1
+    va = args()
+    va.step.head_dim = 96
+    assert f(va) == 2
+    va = args(window=0)  # replay only: the new-window pointers are not read
+    va.step.q = 0
+    va.step.batch = 0
+    assert f(va) == 0
