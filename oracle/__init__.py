@@ -24,6 +24,7 @@ from .build import build_oracle, library_path
 
 __all__ = [
     "recurrent",
+    "recurrent_bwd",
     "chunked",
     "decode_step",
     "transition",
@@ -90,6 +91,11 @@ def open_library(path):
     lib.kda_oracle_transition.argtypes = [
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, _DP, _DP, _DP,
     ]
+    lib.kda_oracle_recurrent_bwd.argtypes = [
+        ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _DP, _DP, _DP, _DP, _DP, ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP,
+    ]
+    lib.kda_oracle_recurrent_bwd.restype = ctypes.c_int
     lib.kda_oracle_lowerbound_gate.argtypes = [
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP, ctypes.c_double, _DP,
     ]
@@ -170,6 +176,33 @@ def recurrent(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0,
                                   _ptr(o), _ptr(sf), int(nthreads))
     _check(rc, "kda_oracle_recurrent")
     return o, sf
+
+
+def recurrent_bwd(q, k, v, g, beta, dO, cu_seqlens=None, initial_state=None, dS_final=None,
+                  scale=1.0):
+    """Gradients of L = sum <dO, o> + <dS_final, S_T> through the token loop.
+
+    Shapes as in ``recurrent``; dO: [T, H, V]; dS_final: [N, H, K, V] or None.
+    Returns a dict of dq, dk, dg [T, H, K], dv [T, H, V], dbeta [T, H] and
+    dS0 [N, H, K, V] (fp64).
+    """
+    lib = load()
+    q, k, v, g, beta, cu, s0, T, H, K, V, N = _common(q, k, v, g, beta, cu_seqlens,
+                                                        initial_state)
+    dO = _f64(dO, "dO")
+    if dO.shape != (T, H, V):
+        raise ValueError("dO must be [T, H, V]")
+    dsf = _f64(dS_final, "dS_final")
+    if dsf is not None and dsf.shape != (N, H, K, V):
+        raise ValueError(f"dS_final must be [{N}, {H}, {K}, {V}]")
+    out = {"dq": np.zeros((T, H, K)), "dk": np.zeros((T, H, K)), "dv": np.zeros((T, H, V)),
+           "dg": np.zeros((T, H, K)), "dbeta": np.zeros((T, H)), "dS0": np.zeros((N, H, K, V))}
+    rc = lib.kda_oracle_recurrent_bwd(N, cu.ctypes.data_as(_I64P), H, K, V, _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(s0),
+                                      _ptr(dO), _ptr(dsf), *(_ptr(out[n]) for n in
+                                      ("dq", "dk", "dv", "dg", "dbeta", "dS0")))
+    _check(rc, "kda_oracle_recurrent_bwd")
+    return out
 
 
 def chunked(q, k, v, g, beta, chunk_size, cu_seqlens=None, initial_state=None, scale=1.0,

@@ -339,6 +339,114 @@ int kda_oracle_transition(int64_t T, int K, int V, const double *k, const double
 }
 
 /*
+ * Gradients of the token loop (the backward pass a training step needs; [P1]
+ * "FlashKDA steps the state once per 16 tokens" notes FlashKDA is forward-only,
+ * [P3] section 4.1 that KDA kernels serve training).  For the loss
+ *   L = sum_t <dO_t, o_t> + sum_{n,h} <dS_final[n,h], S_T[n,h]>
+ * reverse-mode through each token of kda_oracle_recurrent, in the order the
+ * token was computed:
+ *   S' = Diag(a) S,  a = exp(g);  r = S'^T k;  u = beta (v - r);  S+ = S' + k u^T;
+ *   o = scale S+^T q
+ * backwards (dS is dL/dS+ on entry):
+ *   dS += scale q dO^T;     dq = scale S+ dO
+ *   dk = dS u;  du = dS^T k;  dv = beta du;  dbeta = (v - r) . du;  dr = -beta du
+ *   dS' = dS + k dr^T;      dk += S' dr
+ *   dg_i = sum_j dS'_ij S'_ij  (= a_i sum_j dS'_ij S_ij);   dS <- Diag(a) dS'
+ * The states before each token are kept (T x K x V per chain), so this is for
+ * small cases.  s0 and dS_final may be NULL (zero); dS0 may be NULL.
+ */
+int kda_oracle_recurrent_bwd(int N, const int64_t *cu_seqlens, int H, int K, int V,
+                             const double *q, const double *k, const double *v,
+                             const double *g, const double *beta, double scale,
+                             const double *S0, const double *dO, const double *dS_final,
+                             double *dq, double *dk, double *dv, double *dg, double *dbeta,
+                             double *dS0) {
+  if (H <= 0 || K <= 0 || V <= 0 || !cu_seqlens || !dO) return KDA_ORACLE_EINVAL;
+  if (!check_cu(N, cu_seqlens, cu_seqlens[N])) return KDA_ORACLE_EINVAL;
+  const size_t KV = (size_t)K * V;
+  for (int n = 0; n < N; ++n)
+    for (int h = 0; h < H; ++h) {
+      const int64_t t0 = cu_seqlens[n], t1 = cu_seqlens[n + 1], T = t1 - t0;
+      /* states before each token (T + 1 of them), then work vectors */
+      double *St = (double *)malloc(sizeof(double) * ((size_t)(T + 1) * KV + 2 * KV + 4 * V));
+      if (!St) return KDA_ORACLE_ENOMEM;
+      double *dS = St + (size_t)(T + 1) * KV, *Sp = dS + KV;
+      double *r = Sp + KV, *u = r + V, *du = u + V, *dr = du + V;
+      if (S0) memcpy(St, S0 + ((size_t)n * H + h) * KV, sizeof(double) * KV);
+      else memset(St, 0, sizeof(double) * KV);
+      /* forward, keeping every state */
+      for (int64_t t = 0; t < T; ++t) {
+        const size_t th = (size_t)(t0 + t) * H + h;
+        const double *kt = k + th * K, *gt = g + th * K, *vt = v + th * V;
+        double *S = St + (size_t)(t + 1) * KV;
+        for (int i = 0; i < K; ++i)
+          for (int j = 0; j < V; ++j) S[i * V + j] = exp(gt[i]) * St[(size_t)t * KV + i * V + j];
+        for (int j = 0; j < V; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < K; ++i) acc += kt[i] * S[i * V + j];
+          r[j] = acc;
+        }
+        for (int i = 0; i < K; ++i)
+          for (int j = 0; j < V; ++j) S[i * V + j] += beta[th] * kt[i] * (vt[j] - r[j]);
+      }
+      if (dS_final) memcpy(dS, dS_final + ((size_t)n * H + h) * KV, sizeof(double) * KV);
+      else memset(dS, 0, sizeof(double) * KV);
+      /* backward */
+      for (int64_t t = T - 1; t >= 0; --t) {
+        const size_t th = (size_t)(t0 + t) * H + h;
+        const double *qt = q + th * K, *kt = k + th * K, *gt = g + th * K, *vt = v + th * V;
+        const double *dOt = dO + th * V;
+        const double *Sprev = St + (size_t)t * KV, *Snew = St + (size_t)(t + 1) * KV;
+        const double b = beta[th];
+        for (int i = 0; i < K; ++i)
+          for (int j = 0; j < V; ++j) Sp[i * V + j] = exp(gt[i]) * Sprev[i * V + j];
+        for (int j = 0; j < V; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < K; ++i) acc += kt[i] * Sp[i * V + j];
+          r[j] = acc;
+          u[j] = b * (vt[j] - acc);
+        }
+        /* o = scale S+^T q */
+        for (int i = 0; i < K; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < V; ++j) {
+            dS[i * V + j] += scale * qt[i] * dOt[j];
+            acc += Snew[i * V + j] * dOt[j];
+          }
+          if (dq) dq[th * K + i] = scale * acc;
+        }
+        /* S+ = S' + k u^T */
+        for (int j = 0; j < V; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < K; ++i) acc += dS[i * V + j] * kt[i];
+          du[j] = acc;
+        }
+        double db = 0.0;
+        for (int j = 0; j < V; ++j) {
+          if (dv) dv[th * V + j] = b * du[j];
+          db += (vt[j] - r[j]) * du[j];
+          dr[j] = -b * du[j];
+        }
+        if (dbeta) dbeta[th] = db;
+        for (int i = 0; i < K; ++i) {
+          double dki = 0.0, dgi = 0.0;
+          for (int j = 0; j < V; ++j) {
+            dki += dS[i * V + j] * u[j] + Sp[i * V + j] * dr[j];
+            const double dSp = dS[i * V + j] + kt[i] * dr[j];  /* dL/dS' */
+            dgi += dSp * Sp[i * V + j];
+            dS[i * V + j] = exp(gt[i]) * dSp;                  /* dL/dS before the token */
+          }
+          if (dk) dk[th * K + i] = dki;
+          if (dg) dg[th * K + i] = dgi;
+        }
+      }
+      if (dS0) memcpy(dS0 + ((size_t)n * H + h) * KV, dS, sizeof(double) * KV);
+      free(St);
+    }
+  return KDA_ORACLE_OK;
+}
+
+/*
  * K3's lower-bounded gate ([P1] section "How KDA updates its state"), elementwise over tokens t,
  * heads h and key channels c of x [T, H, K]:
  *   g[t,h,c] = lower_bound * sigmoid(exp(A_log[h]) * (x[t,h,c] + dt_bias[h,c]))

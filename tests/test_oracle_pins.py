@@ -602,6 +602,73 @@ def test_spec_verify_one_token_window_is_the_decode_step():
     np.testing.assert_array_equal(cache2, cache_ref)
 
 
+# ------------------------------------------------------------ backward pass
+def _bwd_case(seed=41):
+    rng = np.random.default_rng(seed)
+    H, K, V = 2, 3, 2
+    lens = [3, 2]
+    T = sum(lens)
+    x = {"q": rng.standard_normal((T, H, K)), "k": rng.standard_normal((T, H, K)) * 0.7,
+         "v": rng.standard_normal((T, H, V)),
+         "g": -np.logaddexp(0.0, rng.standard_normal((T, H, K))),
+         "beta": 1 / (1 + np.exp(-rng.standard_normal((T, H)))),
+         "S0": rng.standard_normal((2, H, K, V)) * 0.5}
+    dO = rng.standard_normal((T, H, V))
+    dSf = rng.standard_normal((2, H, K, V))
+    return x, dO, dSf, [0, 3, 5]
+
+
+def _loss(x, dO, dSf, cu, scale):
+    o, sf = oracle.recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=cu,
+                             initial_state=x["S0"], scale=scale)
+    return float(np.sum(o * dO) + np.sum(sf * dSf))
+
+
+def test_backward_matches_central_differences():
+    """Every gradient of L = <dO, o> + <dS_final, S_T>, entry by entry, against the
+    central difference (L(x + h) - L(x - h)) / 2h of the forward token loop, over
+    a two-sequence pack with nonzero initial states and a non-unit scale."""
+    x, dO, dSf, cu = _bwd_case()
+    scale = 0.8
+    got = oracle.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, cu_seqlens=cu,
+                               initial_state=x["S0"], dS_final=dSf, scale=scale)
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "S0": "dS0"}
+    h = 1e-6
+    for name, gname in names.items():
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {kk: vv.copy() for kk, vv in x.items()}
+            xm = {kk: vv.copy() for kk, vv in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            num[idx] = (_loss(xp, dO, dSf, cu, scale) - _loss(xm, dO, dSf, cu, scale)) / (2 * h)
+        np.testing.assert_allclose(got[gname], num, rtol=1e-6, atol=1e-8, err_msg=gname)
+
+
+def test_backward_special_cases():
+    """With beta = 0 and g = 0 the state never changes: dv = 0, dq = scale S0 dO,
+    dS0 = scale sum_t q_t dO_t^T + dS_final, dk = 0 (k only enters through the
+    erase and the write, both scaled by beta) and dg_t = <dS'_t, S0>."""
+    x, dO, dSf, cu = _bwd_case(42)
+    x["beta"][:] = 0.0
+    x["g"][:] = 0.0
+    got = oracle.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, cu_seqlens=cu,
+                               initial_state=x["S0"], dS_final=dSf, scale=0.5)
+    assert np.array_equal(got["dv"], np.zeros_like(got["dv"]))
+    assert np.allclose(got["dk"], 0.0, atol=1e-15)
+    for n, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        for h in range(x["q"].shape[1]):
+            S0 = x["S0"][n, h]
+            np.testing.assert_allclose(got["dq"][a:b, h], 0.5 * dO[a:b, h] @ S0.T, rtol=1e-13)
+            ds0 = dSf[n, h] + 0.5 * x["q"][a:b, h].T @ dO[a:b, h]
+            np.testing.assert_allclose(got["dS0"][n, h], ds0, rtol=1e-13, atol=1e-14)
+            # dL/dS' at token t: dS_final plus the reads of tokens t .. end
+            for t in range(a, b):
+                dsp = dSf[n, h] + 0.5 * x["q"][t:b, h].T @ dO[t:b, h]
+                np.testing.assert_allclose(got["dg"][t, h], np.sum(dsp * S0, axis=1),
+                                           rtol=1e-12, atol=1e-13)
+
+
 # ------------------------------------------- planted mistakes must be caught
 def _pins_pass():
     """Run a compact set of the pins above; True if all hold."""
@@ -724,6 +791,48 @@ def test_front_pins_catch_planted_mistake(name, tmp_path):
     assert _front_pins_pass(), "unmodified oracle must pass the front-end pins"
     with oracle.using(oracle.open_library(lib_path)):
         assert not _front_pins_pass(), f"planted mistake '{name}' was not caught"
+
+
+def _bwd_pins_pass():
+    for c in (test_backward_matches_central_differences, test_backward_special_cases):
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+BWD_MUTANTS = {
+    # decay gradient taken against the undecayed state
+    "dg_undecayed": lambda s: s.replace("dgi += dSp * Sp[i * V + j];",
+                                        "dgi += dSp * Sprev[i * V + j];"),
+    # state gradient carried back without the decay
+    "dS_no_decay": lambda s: s.replace("dS[i * V + j] = exp(gt[i]) * dSp;",
+                                       "dS[i * V + j] = dSp;"),
+    # beta gradient with the wrong sign of r
+    "dbeta_sign": lambda s: s.replace("db += (vt[j] - r[j]) * du[j];",
+                                      "db += (vt[j] + r[j]) * du[j];"),
+    # erase path of dk dropped
+    "dk_no_erase": lambda s: s.replace("dki += dS[i * V + j] * u[j] + Sp[i * V + j] * dr[j];",
+                                       "dki += dS[i * V + j] * u[j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_pins_catch_planted_mistake(name, tmp_path):
+    """Plausible mistakes in the backward pass, planted in a copy of the oracle on
+    the CPU, each fail the finite-difference or special-case pin."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(SOURCE).read()
+    mutated = BWD_MUTANTS[name](src)
+    assert mutated != src, "mutation did not apply"
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(mutated)
+    lib_path = build_oracle(str(path), str(tmp_path / f"libmut_{name}.so"))
+    assert _bwd_pins_pass(), "unmodified oracle must pass the backward pins"
+    with oracle.using(oracle.open_library(lib_path)):
+        assert not _bwd_pins_pass(), f"planted mistake '{name}' was not caught"
 
 
 @pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
