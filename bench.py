@@ -59,6 +59,8 @@ def parse():
                          "speculative-decode verification (replay of a --spec-window-token "
                          "window, all accepted, plus a new window of as many tokens)")
     ap.add_argument("--spec-window", type=int, default=4)
+    ap.add_argument("--bwd", action="store_true",
+                    help="also time the chunked backward on the prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains-per-core", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -125,6 +127,57 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
     res = dict(ms=ms, wall_s=wall, tokens=tokens, heads=H, seqs=N, x=x, cfg=cfg,
                gate_params=gp if gate else None)
     return res
+
+
+BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 4 * D + 4 + 4 * 4 * D + 4     # 3,592
+
+
+def time_backward(kda, ki, workload, steps, warmup):
+    """The chunked backward on the prefill workload: gradients of <dO, o> with
+    dO ~ N(0, 1) in the I/O dtype; grads and workspace allocated once."""
+    import torch
+    cfg = ki.CONFIGS[workload]
+    x = ki.make_prefill(cfg, device="cuda", seed=1002)
+    T, H = x["q"].shape[0], x["heads"]
+    N = len(x["lengths"])
+    gen = torch.Generator(device="cuda").manual_seed(1007)
+    dO = torch.randn((T, H, D), generator=gen, device="cuda").to(x["q"].dtype)
+    varlen = cfg.varlen
+    grads = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO,
+                          cu_seqlens=x["cu_seqlens"] if varlen else None,
+                          cu_seqlens_host=x["cu_seqlens_host"] if varlen else None,
+                          initial_state=x["initial_state"], num_seqs=N)
+    ws = [None]
+
+    def step():
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO,
+                      cu_seqlens=x["cu_seqlens"] if varlen else None,
+                      cu_seqlens_host=x["cu_seqlens_host"] if varlen else None,
+                      initial_state=x["initial_state"], num_seqs=N, grads=grads,
+                      workspace=ws[0])
+
+    # one workspace for every step
+    ws_bytes = kda.chunk_bwd_workspace_size(
+        x["q"], num_seqs=N, cu_seqlens_host=x["cu_seqlens_host"] if varlen else None)
+    ws[0] = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = T * H * BWD_BYTES_PER_TOKEN_HEAD
+    del x, grads, ws, dO
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "steps": steps, "tokens_per_s": T / (ms * 1e-3),
+            "algorithmic_bytes": alg, "gb_per_s": alg / (ms * 1e-3) / 1e9,
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "workload": workload,
+            "kernels": ["bwd_states_kernel", "bwd_serial_kernel", "bwd_finalize_kernel"]}
 
 
 def time_decode(kda, ki, steps, warmup=10, kernel="step", window=4):
@@ -393,6 +446,9 @@ def main():
         line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel,
                                      window=args.spec_window)
         line["decode"]["workload"] = DECODE_WORKLOAD
+    if args.bwd:
+        line["backward"] = time_backward(kda, ki, args.workload, max(2, args.steps // 4),
+                                         max(1, args.warmup // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds,
                                             pre["gate_params"])

@@ -16,6 +16,8 @@ __all__ = [
     "KDAError",
     "chunk_fwd",
     "chunk_fwd_workspace_size",
+    "chunk_bwd",
+    "chunk_bwd_workspace_size",
     "recurrent_step",
     "fused_decode_step",
     "spec_verify_step",
@@ -86,6 +88,35 @@ class ChunkFwdArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("segments", ctypes.c_int32),
         ("gate", Gate),
+    ]
+
+
+class ChunkBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p),
+        ("dO", ctypes.c_void_p),
+        ("dfinal_state", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("dg", ctypes.c_void_p),
+        ("dbeta", ctypes.c_void_p),
+        ("dinitial_state", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -167,6 +198,9 @@ def library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkFwdArgs),
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs), ctypes.c_void_p]
+    lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(ChunkBwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(ChunkBwdArgs),
+                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_fused_decode_step.argtypes = [ctypes.POINTER(FusedStepArgs), ctypes.c_void_p]
     lib.kda_spec_verify_step.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     lib.kda_conv_cache_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
@@ -341,6 +375,103 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     _check(lib.kda_chunk_fwd(ctypes.byref(a), _stream(q)), "kda_chunk_fwd")
     del host
     return o, final_state
+
+
+def chunk_bwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None) -> int:
+    """Workspace bytes for the backward of a prefill of ``q``'s shape (host only)."""
+    lib = library()
+    T, H, D = q.shape
+    a = ChunkBwdArgs()
+    host = None
+    if cu_seqlens_host is not None:
+        host = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+        a.num_seqs = len(cu_seqlens_host) - 1
+        a.cu_seqlens_host = host
+        a.cu_seqlens = 16  # non-null marker: only the host copy is read here
+    else:
+        a.num_seqs = num_seqs or 1
+        a.seq_len = T // a.num_seqs
+    a.num_heads, a.head_dim = H, D
+    a.io_dtype = _dtype_code(q.dtype)
+    a.scale = 1.0
+    out = ctypes.c_size_t(0)
+    _check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(out)),
+           "kda_chunk_bwd_workspace_size")
+    del host
+    return int(out.value)
+
+
+def chunk_bwd(q, k, v, g, beta, dO, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+              dfinal_state=None, scale=1.0, num_seqs=None, want_dinitial=True, workspace=None,
+              grads=None):
+    """Backward of chunk_fwd (log-decay g, beta as given): gradients of
+    L = <dO, o> + <dfinal_state, S_T>.
+
+    Shapes as in chunk_fwd; dO: [T, H, 128] in q's dtype; dfinal_state:
+    [N, H, 128, 128] fp32 or None.  Returns a dict of fp32 dq, dk, dv, dg
+    [T, H, 128], dbeta [T, H] and dinitial_state [N, H, 128, 128] (None unless
+    want_dinitial).  ``grads`` may pass preallocated outputs with those keys.
+    """
+    lib = library()
+    _need(q, "q", ndim=3)
+    for name, t in (("k", k), ("v", v), ("dO", dO)):
+        _need(t, name, dtype=q.dtype, ndim=3)
+    _need(g, "g", dtype=torch.float32, ndim=3)
+    _need(beta, "beta", dtype=torch.float32, ndim=2)
+    T, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or g.shape != q.shape or dO.shape != q.shape \
+            or beta.shape != (T, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta, dO")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
+        N = cu_seqlens.shape[0] - 1
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.tolist()
+    else:
+        N = num_seqs or (initial_state.shape[0] if initial_state is not None else 1)
+    for name, t in (("initial_state", initial_state), ("dfinal_state", dfinal_state)):
+        if t is not None:
+            _need(t, name, dtype=torch.float32, ndim=4)
+            if t.shape != (N, H, D, D):
+                raise ValueError(f"{name} must be [{N}, {H}, {D}, {D}]")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = dict(grads) if grads is not None else {}
+    for name in ("dq", "dk", "dv", "dg"):
+        out.setdefault(name, torch.empty((T, H, D), **f32))
+    out.setdefault("dbeta", torch.empty((T, H), **f32))
+    if want_dinitial:
+        out.setdefault("dinitial_state", torch.empty((N, H, D, D), **f32))
+    else:
+        out["dinitial_state"] = None
+    a = ChunkBwdArgs()
+    host = None
+    a.num_seqs = N
+    if cu_seqlens_host is not None:
+        host = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+        a.cu_seqlens_host = host
+        a.cu_seqlens = cu_seqlens.data_ptr()
+    else:
+        if T % N:
+            raise ValueError("T_total must be a multiple of the number of sequences")
+        a.seq_len = T // N
+    a.num_heads, a.head_dim = H, D
+    a.io_dtype = _dtype_code(q.dtype)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta, a.dO = (t.data_ptr() for t in (q, k, v, g, beta, dO))
+    a.initial_state = None if initial_state is None else initial_state.data_ptr()
+    a.dfinal_state = None if dfinal_state is None else dfinal_state.data_ptr()
+    a.dq, a.dk, a.dv, a.dg, a.dbeta = (out[n].data_ptr() for n in ("dq", "dk", "dv", "dg",
+                                                                     "dbeta"))
+    a.dinitial_state = None if out["dinitial_state"] is None else out["dinitial_state"].data_ptr()
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(ws_bytes)),
+           "kda_chunk_bwd_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _check(lib.kda_chunk_bwd(ctypes.byref(a), _stream(q)), "kda_chunk_bwd")
+    del host
+    return out
 
 
 def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=None,

@@ -108,6 +108,51 @@ kda_status check_fused_args(const kda_fused_step_args *a, bool tokens) {
   return KDA_SUCCESS;
 }
 
+// The backward's arguments: the forward's size and offset rules, then pointers.
+kda_status check_bwd_args(const kda_chunk_bwd_args *a, int64_t *total_tokens, int64_t *max_sub,
+                          bool check_pointers) {
+  if (!a) return KDA_ERROR_INVALID_VALUE;
+  kda_chunk_fwd_args f = {};
+  f.num_seqs = a->num_seqs;
+  f.seq_len = a->seq_len;
+  f.cu_seqlens = a->cu_seqlens;
+  f.cu_seqlens_host = a->cu_seqlens_host;
+  f.num_heads = a->num_heads;
+  f.head_dim = a->head_dim;
+  f.chunk_size = KDA_CHUNK;
+  f.io_dtype = a->io_dtype;
+  f.scale = a->scale;
+  const kda_status st = check_chunk_args(&f, total_tokens, false);
+  if (st != KDA_SUCCESS) return st;
+  const int64_t T = *total_tokens;
+  int64_t ms = 0;
+  for (int32_t n = 0; n < a->num_seqs; ++n) {
+    const int64_t len = a->cu_seqlens ? (int64_t)a->cu_seqlens_host[n + 1] - a->cu_seqlens_host[n]
+                                      : a->seq_len;
+    const int64_t sub = (len + 15) / 16;
+    if (sub > ms) ms = sub;
+  }
+  *max_sub = ms;
+  if (T > 0 && check_pointers) {
+    const void *in16[] = {a->q, a->k, a->v, a->dO, a->g, a->dq, a->dk, a->dv, a->dg};
+    for (const void *p : in16)
+      if (!p || !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (!a->beta || !aligned(a->beta, 4) || !a->dbeta || !aligned(a->dbeta, 4))
+      return KDA_ERROR_INVALID_VALUE;
+    const void *outs[] = {a->dq, a->dk, a->dv, a->dg, a->dbeta};
+    const void *ins[] = {a->q, a->k, a->v, a->dO, a->g, a->beta};
+    for (const void *o : outs)
+      for (const void *i : ins)
+        if (o == i) return KDA_ERROR_INVALID_VALUE;
+  }
+  if (check_pointers) {
+    if (a->initial_state && !aligned16(a->initial_state)) return KDA_ERROR_INVALID_VALUE;
+    if (a->dfinal_state && !aligned16(a->dfinal_state)) return KDA_ERROR_INVALID_VALUE;
+    if (a->dinitial_state && !aligned16(a->dinitial_state)) return KDA_ERROR_INVALID_VALUE;
+  }
+  return KDA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,6 +199,25 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a, void *stream) {
     if (((uintptr_t)a->workspace & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   }
   return launch_status(kda::launch_chunk_fwd(*a, plan, (hipStream_t)stream));
+}
+
+kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *a, size_t *bytes) {
+  if (!bytes) return KDA_ERROR_INVALID_VALUE;
+  int64_t T = 0, ms = 0;
+  const kda_status st = check_bwd_args(a, &T, &ms, false);
+  if (st != KDA_SUCCESS) return st;
+  *bytes = kda::chunk_bwd_workspace_bytes(T, a->num_seqs, a->num_heads);
+  return KDA_SUCCESS;
+}
+
+kda_status kda_chunk_bwd(const kda_chunk_bwd_args *a, void *stream) {
+  int64_t T = 0, ms = 0;
+  const kda_status st = check_bwd_args(a, &T, &ms, true);
+  if (st != KDA_SUCCESS) return st;
+  const size_t need = kda::chunk_bwd_workspace_bytes(T, a->num_seqs, a->num_heads);
+  if (!a->workspace || a->workspace_bytes < need) return KDA_ERROR_WORKSPACE;
+  if (((uintptr_t)a->workspace & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
+  return launch_status(kda::launch_chunk_bwd(*a, T, ms, (hipStream_t)stream));
 }
 
 kda_status kda_recurrent_step(const kda_recurrent_step_args *a, void *stream) {

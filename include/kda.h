@@ -180,6 +180,49 @@ kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *args, size_t *
 kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Chunked backward ([P1] "How KDA updates its state": the recurrence;
+ * "FlashKDA steps the state once per 16 tokens": the chunkwise form, forward
+ * only in FlashKDA; [P3] section 4.1: the KDA kernels serve training).
+ *
+ * For the forward of kda_chunk_fwd (log-decay g, beta as given) and the loss
+ *     L = sum_t <dO_t, o_t> + sum_{n,h} <dfinal_state[n,h], S_T[n,h]>
+ * it writes dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dinitial_state.  The
+ * state is recomputed from the inputs (states at every 16-token sub-chunk start
+ * kept in the workspace); all gradients are fp32.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_chunk_bwd_args {
+  int32_t num_seqs;               /* as kda_chunk_fwd_args                               */
+  int32_t seq_len;
+  const int32_t *cu_seqlens;
+  const int32_t *cu_seqlens_host;
+  int32_t num_heads;
+  int32_t head_dim;               /* must be KDA_HEAD_DIM                                */
+  kda_dtype io_dtype;             /* dtype of q, k, v and dO                             */
+  float scale;
+  const void *q, *k, *v;          /* [T_total, H, 128] io_dtype                          */
+  const float *g;                 /* [T_total, H, 128] log-decay                         */
+  const float *beta;              /* [T_total, H]                                        */
+  const float *initial_state;     /* [N, H, 128, 128] or NULL = zeros                    */
+  const void *dO;                 /* [T_total, H, 128] io_dtype: dL/do                   */
+  const float *dfinal_state;      /* [N, H, 128, 128] or NULL = zeros                    */
+  float *dq, *dk, *dv, *dg;       /* [T_total, H, 128] fp32 outputs                      */
+  float *dbeta;                   /* [T_total, H] fp32 output                            */
+  float *dinitial_state;          /* [N, H, 128, 128] fp32 output, or NULL               */
+  void *workspace;                /* device scratch of >= the queried size, 256-B aligned */
+  size_t workspace_bytes;
+} kda_chunk_bwd_args;
+
+/* Bytes of workspace kda_chunk_bwd needs: (T_total / 16 + N + 1) x H x (64 KiB
+ * of state + 27,200 B of partial sums).  Host only. */
+kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *args, size_t *bytes);
+
+/* Enqueue the backward on `stream`.  Errors as kda_chunk_fwd (sizes, offsets,
+ * alignment: q, k, v, dO, g and the gradients 16 bytes, beta and dbeta 4; the
+ * outputs may not alias the inputs), KDA_ERROR_WORKSPACE when the workspace is
+ * smaller than queried. */
+kda_status kda_chunk_bwd(const kda_chunk_bwd_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
  * Recurrent decode step ([P1] "How KDA updates its state"; [P3] section 4.5:
  * the state is updated in place at every decoding step).
  *

@@ -205,7 +205,7 @@ def test_ctypes_structs_match_the_header(tmp_path):
     structs = {"kda_chunk_fwd_args": kda.ChunkFwdArgs,
                "kda_recurrent_step_args": kda.RecurrentStepArgs, "kda_gate": kda.Gate,
                "kda_fused_step_args": kda.FusedStepArgs,
-               "kda_spec_verify_args": kda.SpecVerifyArgs}
+               "kda_spec_verify_args": kda.SpecVerifyArgs, "kda_chunk_bwd_args": kda.ChunkBwdArgs}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kda.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -292,3 +292,27 @@ def test_spec_verify_rejects_invalid_arguments(lib):
     va.step.q = 0
     va.step.batch = 0
     assert f(va) == 0
+
+
+def test_chunk_bwd_rejects_invalid_arguments(lib):
+    def args(**kw):
+        a = kda.ChunkBwdArgs()
+        a.num_seqs, a.seq_len, a.num_heads, a.head_dim = 1, 64, 2, 128
+        a.io_dtype, a.scale = kda.KDA_BF16, 1.0
+        base = 1 << 20
+        a.q, a.k, a.v, a.dO, a.g, a.beta = (base + 4096 * i for i in range(6))
+        a.dq, a.dk, a.dv, a.dg, a.dbeta = (base + 4096 * (8 + i) for i in range(5))
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return a
+    size = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(args()), ctypes.byref(size)) == 0
+    # T / 16 + N + 1 slots of H states and partial records
+    assert size.value >= (64 // 16 + 1 + 1) * 2 * 128 * 128 * 4
+    f = lambda a: lib.kda_chunk_bwd(ctypes.byref(a), None)
+    assert f(args(head_dim=64)) == 2
+    assert f(args(num_heads=0)) == 1
+    assert f(args(dq=0)) == 1
+    assert f(args(dk=(1 << 20) + 4)) == 1          # gradients need 16 bytes
+    assert f(args(dv=1 << 20)) == 1                 # output aliases q
+    assert f(args()) == 3                           # no workspace

@@ -1,0 +1,133 @@
+"""GPU parity of the chunked backward (kda_chunk_bwd) against the fp64 oracle.
+
+The oracle is the reverse-mode token loop (pinned by central differences on the
+CPU); the kernel works on 16-token sub-chunks ("How Kimi K3 Engineered Its Way to
+the Frontier", sections "How KDA updates its state" and "FlashKDA steps the state
+once per 16 tokens").  All gradients are fp32; the inputs are the bf16 or fp32
+values the forward takes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+from kda_testutil import announce, rel_err, to64
+
+pytestmark = pytest.mark.gpu
+NAMES = ("dq", "dk", "dv", "dg", "dbeta")
+# Gradients are computed in fp32 from the exact input values (bf16 inputs are
+# exact in fp32), so the fp32 bound applies to both input dtypes.
+TOL_BWD = 1e-4
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_10_amd as m
+    m.library()
+    return m
+
+
+def grads_gpu(kda, inp, dO, dSf, scale=1.0, varlen=True):
+    return kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO,
+                         cu_seqlens=inp["cu_seqlens"] if varlen else None,
+                         cu_seqlens_host=inp["cu_seqlens_host"] if varlen else None,
+                         initial_state=inp["initial_state"], dfinal_state=dSf, scale=scale,
+                         num_seqs=len(inp["lengths"]))
+
+
+def compare(got, ref, tol=TOL_BWD, rows=None):
+    worst = {}
+    for n in NAMES + ("dinitial_state",):
+        r = ref["dS0" if n == "dinitial_state" else n]
+        gt = got[n]
+        if gt is None:
+            continue
+        gt = to64(gt)
+        if rows is not None and n != "dinitial_state":
+            gt, r = gt[rows], r[rows]
+        worst[n] = rel_err(gt, r)
+    print("  max rel err: " + "  ".join(f"{k} {v:.2e}" for k, v in worst.items()), flush=True)
+    for k, v in worst.items():
+        assert v <= tol, (k, v)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_varlen_ragged_vs_oracle(kda, dtype):
+    """Sequences ending inside sub-chunks, one of exactly 16 tokens, an empty one,
+    nonzero initial states and final-state gradients, a non-unit scale."""
+    announce(f"chunk bwd varlen dtype={dtype}")
+    lens = (1, 15, 16, 17, 40, 0, 100, 77)
+    H = 2
+    cfg = ki.PrefillConfig("t", lens, H, dtype, init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=71)
+    gen = torch.Generator(device="cuda").manual_seed(72)
+    T = inp["q"].shape[0]
+    dO = torch.randn((T, H, 128), generator=gen, device="cuda").to(inp["q"].dtype)
+    dSf = torch.randn((len(lens), H, 128, 128), generator=gen, device="cuda") * 0.1
+    got = grads_gpu(kda, inp, dO, dSf, scale=0.8)
+    torch.cuda.synchronize()
+    ref = oracle.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO,
+                               cu_seqlens=inp["cu_seqlens_host"],
+                               initial_state=inp["initial_state"], dS_final=dSf, scale=0.8)
+    compare(got, ref)
+
+
+def test_backward_strong_decay_and_no_state(kda):
+    """Half the tokens at the gate's floor g = -5 (every e^{G} factor far below
+    1), no initial state and no final-state gradient (dS_final = 0)."""
+    announce("chunk bwd strong decay")
+    cfg = ki.PrefillConfig("t", (150, 64), 2, "bf16", varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=73)
+    T = inp["g"].shape[0]
+    inp["g"][: T // 2] = -5.0
+    gen = torch.Generator(device="cuda").manual_seed(74)
+    dO = torch.randn((T, 2, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    got = grads_gpu(kda, inp, dO, None)
+    torch.cuda.synchronize()
+    ref = oracle.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO,
+                               cu_seqlens=inp["cu_seqlens_host"])
+    compare(got, ref)
+
+
+def test_backward_fixed_batch_equals_varlen(kda):
+    announce("chunk bwd fixed batch vs varlen")
+    cfg = ki.PrefillConfig("t", (96, 96), 3, "bf16", init_std=0.1)
+    inp = ki.make_prefill(cfg, device="cuda", seed=75)
+    gen = torch.Generator(device="cuda").manual_seed(76)
+    dO = torch.randn((192, 3, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    a = grads_gpu(kda, inp, dO, None, varlen=False)
+    b = grads_gpu(kda, inp, dO, None, varlen=True)
+    torch.cuda.synchronize()
+    for n in NAMES + ("dinitial_state",):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_backward_full_b4_t8192_h96_last_tokens(kda):
+    """The 4 x 8,192 x 96 bf16 workload's backward, in the launch the benchmark
+    times; the last 64 tokens of three chains checked against the oracle run from
+    the state the forward reaches at token 8,128 (exact for those tokens)."""
+    announce("chunk bwd full b4 t8192 h96")
+    cfg = ki.CONFIGS["kda_prefill_b4_t8192_h96_bf16"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1002)
+    T, H = inp["q"].shape[0], inp["heads"]
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    dO = torch.randn((T, H, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    got = grads_gpu(kda, inp, dO, None, varlen=False)
+    torch.cuda.synchronize()
+    tail = 64
+    for n, h in ((0, 0), (2, 41), (3, 95)):
+        a, b = n * 8192, (n + 1) * 8192
+        sl = lambda t: t[a:b - tail, h:h + 1]
+        _, s_mid = oracle.recurrent(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["g"]),
+                                    sl(inp["beta"]))
+        tl = lambda t: t[b - tail:b, h:h + 1]
+        ref = oracle.recurrent_bwd(tl(inp["q"]), tl(inp["k"]), tl(inp["v"]), tl(inp["g"]),
+                                   tl(inp["beta"]), tl(dO), initial_state=s_mid)
+        sub = {k: (v[b - tail:b, h:h + 1] if v is not None and k != "dinitial_state" else None)
+               for k, v in got.items()}
+        compare(sub, ref)
+    del inp, got
+    torch.cuda.empty_cache()
