@@ -213,7 +213,8 @@ typedef struct kda_chunk_bwd_args {
 } kda_chunk_bwd_args;
 
 /* Bytes of workspace kda_chunk_bwd needs: (T_total / 16 + N + 1) x H x (64 KiB
- * of state + 27,200 B of partial sums).  Host only. */
+ * of state + 27,200 B of partial sums + 3,072 B of per-sub-chunk matrices),
+ * each region 256-B aligned.  Host only. */
 kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *args, size_t *bytes);
 
 /* Enqueue the backward on `stream`.  Errors as kda_chunk_fwd (sizes, offsets,
