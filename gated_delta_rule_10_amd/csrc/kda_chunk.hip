@@ -53,7 +53,6 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRef = 8;           // reference token inside each 16-token sub-tile
 
 // Tile list of the 10 lower (row-tile i, column-tile j) pairs and their owner wave.
 __device__ __forceinline__ int tri_index(int i, int j) { return i * (i + 1) / 2 + j; }
@@ -113,16 +112,11 @@ template <> struct Raw<float> {
   __device__ __forceinline__ float lo() const { return f[0]; }
   __device__ __forceinline__ float hi() const { return f[1]; }
 };
-__device__ __forceinline__ void raw_load(Raw<bf16> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off,
-                                         uint32_t soff) {
-  r.u = buf_load_b32(rs, off, soff);
-}
 __device__ __forceinline__ void raw_load(Raw<float> &r, __amdgpu_buffer_rsrc_t rs, uint32_t off,
                                          uint32_t soff) {
   r.f = buf_load_f32x2(rs, off, soff);
 }
 template <class OpT> __device__ __forceinline__ void raw_zero(Raw<OpT> &r);
-template <> __device__ __forceinline__ void raw_zero(Raw<bf16> &r) { r.u = 0u; }
 template <> __device__ __forceinline__ void raw_zero(Raw<float> &r) { r.f = f32x2{0.f, 0.f}; }
 
 // Gram jobs of waves 4..7: (kind, row tile i, column tile j), kind 0 = A, 1 = P.

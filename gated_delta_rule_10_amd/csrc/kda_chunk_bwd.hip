@@ -67,7 +67,7 @@ struct BwdParams {
   const float *g, *beta, *s0, *dsf;
   float *dq, *dk, *dv, *dg, *dbeta, *ds0;
   const int32_t *cu;
-  int64_t total_tokens;
+  int64_t total_tokens, chains;
   int32_t H, seq_len;
   float scale;
   float *ckpt;     // [slots][H][128][128] states at sub-chunk starts
@@ -97,6 +97,17 @@ __device__ __forceinline__ void seq_range(const BwdParams &p, int n, int64_t &bo
     len = e - bos;
   }
 }
+
+// Workgroups are dealt to the eight XCDs (each with its own L2) by block index
+// mod 8.  A unit of work split into nb parts that read the same inputs gets
+// blocks that share the index mod 8, so its parts meet in one L2: unit =
+// (b / (8 nb)) 8 + b % 8, part = (b % (8 nb)) / 8.  The grid is rounded up
+// to whole groups of 8 units; the surplus blocks return at once.
+__device__ __forceinline__ void xcd_unit(int64_t b, int nb, int64_t &unit, int &part) {
+  unit = (b / (8 * nb)) * 8 + b % 8;
+  part = (int)((b % (8 * nb)) / 8);
+}
+inline int64_t xcd_grid(int64_t units, int nb) { return (units + 7) / 8 * 8 * nb; }
 
 __device__ __forceinline__ int sub_len(int64_t len, int j) {
   const int64_t rest = len - (int64_t)j * kSC;
@@ -297,8 +308,11 @@ struct StatesSmem {
 template <class IO>
 __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) StatesSmem sm;
-  const int blk = blockIdx.x % kNB;
-  const int chain = blockIdx.x / kNB;
+  int64_t unit;
+  int blk;
+  xcd_unit(blockIdx.x, kNB, unit, blk);
+  if (unit >= p.chains) return;
+  const int chain = (int)unit;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
@@ -417,8 +431,11 @@ struct SerialSmem {
 template <class IO>
 __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) SerialSmem sm;
-  const int blk = blockIdx.x % kNB;
-  const int chain = blockIdx.x / kNB;
+  int64_t unit;
+  int blk;
+  xcd_unit(blockIdx.x, kNB, unit, blk);
+  if (unit >= p.chains) return;
+  const int chain = (int)unit;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
@@ -610,30 +627,37 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- 3. finalize
-// Workgroup of 1024 threads per (sequence, head, j0, half of the key channels):
-// sub-chunks j0, j0 + stride, ...; thread (row r, channel c) forms dq, dk, dg of
-// token r, channel c.  The Ab and P terms: row r's pairs (r, s <= r) and the
-// pairs (s >= r, r) in which token r is the earlier one, each with its own
-// e^{G_r - G_s} <= 1.
-constexpr int kFC = 64;  // key channels per finalize workgroup
+// Workgroup of 512 threads per (sequence, head, j0, quarter of the key
+// channels): sub-chunks j0, j0 + stride, ...; thread (row r, channel c) forms
+// dq, dk, dg of token r, channel c.  The Ab and P terms: row r's pairs
+// (r, s <= r) and the pairs (s >= r, r) in which token r is the earlier one,
+// each with its own e^{G_r - G_s} <= 1.  LDS is double-buffered by sub-chunk
+// parity, so three barriers per sub-chunk suffice.
+constexpr int kFC = 32;  // key channels per finalize workgroup
 constexpr int kFT = kFC * kSC;
+
+struct FinSmem {
+  float dA[kSC * kSC], dP[kSC * kSC], sb[kSC];
+  float kx[kSC][kFC], qx[kSC][kFC], gx[kSC][kFC], Gs[kSC][kFC], dGs[kSC][kFC], tl[kSC][kFC];
+};
 
 template <class IO>
 __global__ __launch_bounds__(kFT) void bwd_finalize_kernel(BwdParams p, int stride) {
-  const int per_chain = stride * (kD / kFC);
-  const int chain = blockIdx.x / per_chain, rem = blockIdx.x % per_chain;
-  const int j0 = rem / (kD / kFC), c0 = (rem % (kD / kFC)) * kFC;
+  int64_t unit;
+  int quarter;
+  xcd_unit(blockIdx.x, kD / kFC, unit, quarter);
+  if (unit >= p.chains * stride) return;
+  const int chain = (int)(unit / stride), j0 = (int)(unit % stride), c0 = quarter * kFC;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
   const int t = threadIdx.x, cl = t % kFC, r = t / kFC, c = c0 + cl;
   const IO *q = reinterpret_cast<const IO *>(p.q), *k = reinterpret_cast<const IO *>(p.k);
   const int64_t rowstride = (int64_t)p.H * kD;
-  __shared__ float dA[kSC * kSC], dP[kSC * kSC], sb[kSC];
-  __shared__ float kx[kSC][kFC], qx[kSC][kFC], Gs[kSC][kFC], red[kSC][kFC];
+  __shared__ FinSmem smb[2];
   const int nsub = (int)((len + kSC - 1) / kSC);
   // Loads of one sub-chunk, issued one sub-chunk ahead (unconditional: rows past
-  // L read row L - 1 and are masked at use).
+  // L read row L - 1 and are masked at use; every thread consumes what it loads).
   struct In {
     IO k, q;
     float g, dkt[2], dqt[2], dkb[2], da[2], dp[2], db[2], dgam[2], ab, beta;
@@ -661,87 +685,78 @@ __global__ __launch_bounds__(kFT) void bwd_finalize_kernel(BwdParams p, int stri
     in.beta = p.beta[(t0 + min(t & 15, L - 1)) * p.H + h];
   };
   if (j0 < nsub) fetch(j0);
-  for (int j = j0; j < nsub; j += stride) {
+  int parity = 0;
+  for (int j = j0; j < nsub; j += stride, parity ^= 1) {
+    FinSmem &sm = smb[parity];
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
     const bool live = r < L;
     const int64_t off = (t0 + r) * rowstride + (int64_t)h * kD + c;
     const float kr = live ? to_f32(in.k) : 0.f, qv = live ? to_f32(in.q) : 0.f;
-    kx[r][cl] = kr;
-    qx[r][cl] = qv;
-    red[r][cl] = live ? in.g : 0.f;
+    sm.kx[r][cl] = kr;
+    sm.qx[r][cl] = qv;
+    sm.gx[r][cl] = live ? in.g : 0.f;
     const float dKt = in.dkt[0] + in.dkt[1];
     const float dQt = in.dqt[0] + in.dqt[1];
     const float dKb = in.dkb[0] + in.dkb[1];
-    dA[t & 255] = in.da[0] + in.da[1];  // every thread consumes its loads (equal copies)
-    dP[t & 255] = in.dp[0] + in.dp[1];
-    sb[t & 15] = (t & 15) < L ? in.beta : 0.f;
+    sm.dA[t & 255] = in.da[0] + in.da[1];  // equal copies from both halves of the threads
+    sm.dP[t & 255] = in.dp[0] + in.dp[1];
+    sm.sb[t & 15] = (t & 15) < L ? in.beta : 0.f;
     const float ab = in.ab, db = in.db[0] + in.db[1], dgs = in.dgam[0] + in.dgam[1];
     fetch(j + stride < nsub ? j + stride : j);  // unconditional: static wait counts
     block_sync();
     float Gr = 0.f, Gl = 0.f;
 #pragma unroll
     for (int s = 0; s < kSC; ++s) {
-      const float x = red[s][cl];
+      const float x = sm.gx[s][cl];
       Gr += s <= r ? x : 0.f;
       Gl += x;
     }
-    Gs[r][cl] = Gr;
+    sm.Gs[r][cl] = Gr;
     {  // dbeta_rb = sum_v dW (V - KS) (both halves) + sum_{s<rb} dA_{rb s} Ab_{rb s}:
-       // 16 lanes per row rb (every wave computes; waves 0-3 of the first half store)
+       // 16 lanes per row rb (every wave computes; the first quarter's waves 0-3 store)
       const int rb = (t >> 4) & 15, sb_ = t & 15;
-      float a = sb_ < rb ? dA[rb * kSC + sb_] * ab : 0.f;
+      float a = sb_ < rb ? sm.dA[rb * kSC + sb_] * ab : 0.f;
 #pragma unroll
       for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m);
       if (c0 == 0 && t < kSC * kSC && sb_ == 0 && rb < L)
         p.dbeta[(t0 + rb) * p.H + h] = a + db;
     }
-    const float dgam = dgs * __expf(Gl);
     block_sync();
     const float eg = __expf(Gr), eb = __expf(Gl - Gr);
     float dk = dKt * eg + dKb * eb, dq = dQt * eg;
     float dG = (dKt * kr + dQt * qv) * eg - dKb * kr * eb;
-    const float tail = dKb * kr * eb;  // part of dG of the last row (through G_last)
-    const float br = sb[r];
+    const float br = sm.sb[r];
 #pragma unroll
     for (int s = 0; s < kSC; ++s) {
-      const float Gx = Gs[s][cl], kxs = kx[s][cl];
+      const float Gx = sm.Gs[s][cl], kxs = sm.kx[s][cl];
       if (s <= r) {  // pair (r, s): Ab_rs and P_rs
         const float e = __expf(Gr - Gx);
-        const float da = s < r ? dA[r * kSC + s] * br : 0.f, dp = dP[r * kSC + s];
+        const float da = s < r ? sm.dA[r * kSC + s] * br : 0.f, dp = sm.dP[r * kSC + s];
         dk = fmaf(da * kxs, e, dk);
         dq = fmaf(dp * kxs, e, dq);
         dG = fmaf((da * kr + dp * qv) * kxs, e, dG);
       }
       if (s >= r) {  // pair (s, r): token r is the earlier one
         const float e = __expf(Gx - Gr);
-        const float da = s > r ? dA[s * kSC + r] * sb[s] : 0.f, dp = dP[s * kSC + r];
-        const float coef = (da * kxs + dp * qx[s][cl]) * e;
+        const float da = s > r ? sm.dA[s * kSC + r] * sm.sb[s] : 0.f, dp = sm.dP[s * kSC + r];
+        const float coef = (da * kxs + dp * sm.qx[s][cl]) * e;
         dk += coef;
         dG = fmaf(-coef, kr, dG);
       }
     }
-    block_sync();  // red: g values -> the through-G_last terms
-    red[r][cl] = tail;
+    sm.dGs[r][cl] = dG;
+    sm.tl[r][cl] = dKb * kr * eb;  // through G_last: belongs to the last row's dG
     block_sync();
-    if (r == kSC - 1) {
-      float a = dgam;
+    // dg_r = sum_{s >= r} dG_s + (terms of the last row, which every row's g reaches)
+    float dg = dgs * __expf(Gl);
 #pragma unroll
-      for (int s = 0; s < kSC; ++s) a += red[s][cl];
-      dG += a;
-    }
-    block_sync();
-    red[r][cl] = dG;
-    block_sync();
-    float dg = 0.f;  // dg = reverse cumulative sum of dG within the sub-chunk
-#pragma unroll
-    for (int s = 0; s < kSC; ++s) dg += s >= r ? red[s][cl] : 0.f;
+    for (int s = 0; s < kSC; ++s) dg += (s >= r ? sm.dGs[s][cl] : 0.f) + sm.tl[s][cl];
     if (live) {
       p.dq[off] = dq;
       p.dk[off] = dk;
       p.dg[off] = dg;
     }
-    block_sync();
   }
 }
 
@@ -751,13 +766,15 @@ hipError_t launch_typed(const BwdParams &p, int64_t chains, int stride, hipStrea
                      p, stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_states_kernel<IO>, dim3((unsigned)(chains * kNB)), dim3(kBT), 0, stream, p);
+  hipLaunchKernelGGL(bwd_states_kernel<IO>, dim3((unsigned)xcd_grid(chains, kNB)), dim3(kBT), 0,
+                     stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_serial_kernel<IO>, dim3((unsigned)(chains * kNB)), dim3(kBT), 0, stream, p);
+  hipLaunchKernelGGL(bwd_serial_kernel<IO>, dim3((unsigned)xcd_grid(chains, kNB)), dim3(kBT), 0,
+                     stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_finalize_kernel<IO>, dim3((unsigned)(chains * stride * (kD / kFC))),
+  hipLaunchKernelGGL(bwd_finalize_kernel<IO>, dim3((unsigned)xcd_grid(chains * stride, kD / kFC)),
                      dim3(kFT), 0, stream, p, stride);
   return hipGetLastError();
 }
@@ -813,6 +830,7 @@ hipError_t launch_chunk_bwd(const kda_chunk_bwd_args &a, int64_t total_tokens, i
   p.part = reinterpret_cast<float *>(ws + l.part);
   p.rec = reinterpret_cast<float *>(ws + l.rec);
   const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
+  p.chains = chains;
   const int stride = (int)(max_sub < 1 ? 1 : (max_sub > 64 ? 64 : max_sub));
   if (chains == 0) return hipSuccess;
   return a.io_dtype == KDA_BF16 ? launch_typed<bf16>(p, chains, stride, stream)
