@@ -30,16 +30,20 @@
 //
 // Four launches:
 //  0. prep: per (sub-chunk, head), fully parallel, the matrices that do not
-//     depend on the state: Ab, P (one exponential per channel and pair) and
-//     X = (I + A)^{-1} (forward substitution), kept in the workspace;
+//     depend on the state: Ab, P (matrix-core products of reference-scaled
+//     operands, or one exponential per channel and pair where the decay range
+//     is too wide) and X = (I + A)^{-1} (forward substitution), kept in the
+//     workspace;
 //  1. states: per (sequence, head, half of the value columns) the sub-chunk
 //     forward from the initial state, writing the state at every sub-chunk
 //     start to the workspace;
 //  2. serial: per (sequence, head, half) the sub-chunks in reverse, the state
 //     gradient carried in LDS; it writes dv and, for the terms that sum over
 //     value columns, this half's partial sums to the workspace;
-//  3. finalize: per (sub-chunk, head) the two halves' partials summed and dq,
-//     dk, dg, dbeta formed (the e^{G_r - G_s} terms one channel per thread).
+//  3. finalize: per (sub-chunk, head, half of the key channels) the two
+//     value halves' partials summed and dq, dk, dg, dbeta formed (the
+//     e^{G_r - G_s} terms again as reference-scaled matrix-core products, with
+//     the same per-pair fallback).
 // The 16 x 16 x K products run on fp32 matrix cores (V_MFMA_F32_16X16X4_F32).
 // In the two serial passes eight waves share a sub-chunk: chains of products
 // whose operands a wave produced itself (KS -> W -> U, dU -> dW) stay in
@@ -57,10 +61,14 @@ constexpr int kNB = 2;           // value-column halves per chain
 constexpr int kNC = kD / kNB;    // 64 value columns per workgroup
 constexpr int kBT = 512;         // threads of the serial passes (8 waves)
 constexpr int kPT = 256;         // threads of the prep pass
-constexpr int kLS = kNC + 1;     // row stride of the state halves (odd: no bank conflicts)
-constexpr int kLT = kD + 1;      // row stride of 16 x 128 token matrices
-constexpr int kLB = kNC + 1;     // row stride of 16 x 64 token blocks
-constexpr int kLM = kSC + 1;     // row stride of 16 x 16 matrices
+// LDS row strides of the serial passes: multiples of 4 floats, so a lane reads
+// four consecutive k-values of a k-contiguous operand with one 16-byte load; 4
+// mod 64 banks, so the 16 rows x 4 lane groups of a fragment read hit distinct
+// banks in each 8-lane phase, and column reads (16 g4 + l16) do too.
+constexpr int kLS = kNC + 4;     // row stride of the state halves
+constexpr int kLT = kD + 4;      // row stride of 16 x 128 token matrices
+constexpr int kLB = kNC + 4;     // row stride of 16 x 64 token blocks
+constexpr int kLM = kSC + 1;     // row stride of 16 x 16 matrices (prep pass: odd)
 
 struct BwdParams {
   const void *q, *k, *v, *dO;
@@ -131,11 +139,48 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 ld4(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+
+// As mm, with A row m at a + m lda and B column n at b + n ldb both stored
+// k-contiguous (16-byte aligned): four k-values per 16-byte LDS read.
+__device__ __forceinline__ void mm4(f32x4 &acc, int K, int l16, int g4, const float *a, int lda,
+                                    const float *b, int ldb) {
+  const float *ar = a + l16 * lda + 4 * g4, *bc = b + l16 * ldb + 4 * g4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const f32x4 x = ld4(ar + k0), y = ld4(bc + k0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = mfma(x[t], y[t], acc);
+  }
+}
+// A k-contiguous as in mm4, B read by b(k, n).
+template <class FB>
+__device__ __forceinline__ void mmA4(f32x4 &acc, int K, int l16, int g4, const float *a, int lda,
+                                     FB b) {
+  const float *ar = a + l16 * lda + 4 * g4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const f32x4 x = ld4(ar + k0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = mfma(x[t], b(k0 + 4 * g4 + t, l16), acc);
+  }
+}
+
 // ---------------------------------------------------------------- 0. prep
 // Workgroup per (sequence, head, j0): sub-chunks j0, j0 + stride, ...
+// Ab and P on the matrix cores with the reference M = G at the sub-chunk's
+// token 7: Ab_rs = sum_c (k_rc e^{G_rc - M_c}) (k_sc e^{M_c - G_sc}) and the same
+// with q_r for P, exact up to rounding while every |G - M| stays within
+// kRefSpan (each factor below e^60; masked entries may overflow and are
+// discarded).  Otherwise every pair takes its own exponential per channel.
+constexpr float kRefSpan = 60.f;
 template <class IO>
 __global__ __launch_bounds__(kPT) void bwd_prep_kernel(BwdParams p, int stride) {
-  __shared__ float kx[kSC * kLT], qx[kSC * kLT], G[kSC * kLT], A[kSC * kLM], bt[kSC], tot[kD];
+  __shared__ __attribute__((aligned(16))) float kx[kSC * kLT], qx[kSC * kLT], G[kSC * kLT];
+  __shared__ __attribute__((aligned(16))) float Ke[kSC * kLT], Kd[kSC * kLT], Qe[kSC * kLT];
+  __shared__ float A[kSC * kLM], bt[kSC], tot[kD], wspan[kPT / 64];
   const int chain = blockIdx.x / stride, j0 = blockIdx.x % stride;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
@@ -175,9 +220,47 @@ __global__ __launch_bounds__(kPT) void bwd_prep_kernel(BwdParams p, int stride) 
     const float base = hh ? tot[c] : 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) G[(8 * hh + i) * kLT + c] = base + gr[i];
+    {  // reference-scaled operands; the half-to-token-7 prefix of channel c is known here
+      const float M = hh ? tot[c] : gr[7];  // G_7: the first half's total
+      float span = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * hh + i;
+        const float Gv = base + gr[i], d = Gv - M;
+        const float up = __expf(d), dn = __expf(-d);
+        const float kv_ = kx[r * kLT + c], qv_ = qx[r * kLT + c];
+        Ke[r * kLT + c] = kv_ * up;
+        Qe[r * kLT + c] = qv_ * up;
+        Kd[r * kLT + c] = kv_ * dn;
+        span = fmaxf(span, fabsf(d));
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) span = fmaxf(span, __shfl_xor(span, m));
+      if ((t & 63) == 0) wspan[t >> 6] = span;
+    }
     block_sync();
     float *rec = p.rec + (slot_of(bos, n, j) * p.H + h) * (int64_t)kRec;
-    {  // Ab and P: thread (r, s), every channel, with e^{G_rc - G_sc} (s <= r)
+    float maxspan = 0.f;
+#pragma unroll
+    for (int u = 0; u < kPT / 64; ++u) maxspan = fmaxf(maxspan, wspan[u]);
+    if (maxspan <= kRefSpan) {  // waves 0 and 1: Ab and P tiles
+      const int lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
+      if (w < 2) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mm4(acc, kD, l16, g4, w == 0 ? Ke : Qe, kLT, Kd, kLT);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i, s = l16;
+          if (w == 0) {
+            const float ab = s < r ? acc[i] : 0.f;
+            A[r * kLM + s] = bt[r] * ab;
+            rec[kRecAb + r * kSC + s] = ab;
+          } else {
+            rec[kRecP + r * kSC + s] = s <= r ? acc[i] : 0.f;
+          }
+        }
+      }
+    } else {  // Ab and P: thread (r, s), every channel, with e^{G_rc - G_sc} (s <= r)
       const int r = t / kSC, s = t % kSC;
       float ab = 0.f, pp = 0.f;
       if (s <= r) {
@@ -366,8 +449,7 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
       float vt[4];
       take_tile<IO>(vraw, L, g4, vt);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm(acc, kD, l16, g4, [&](int m, int kk) { return sm.Kt[m * kLT + kk]; },
-         [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
+      mmA4(acc, kD, l16, g4, sm.Kt, kLT, [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
       f32x4 wr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) wr[i] = sm.beta[4 * g4 + i] * (vt[i] - acc[i]);
@@ -382,10 +464,7 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int row = (tw >> 4) + 16 * m;
-        f32x4 s;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = sm.S[row * kLS + col + e];
-        *reinterpret_cast<f32x4 *>(ck + row * kD + col) = s;
+        *reinterpret_cast<f32x4 *>(ck + row * kD + col) = ld4(sm.S + row * kLS + col);
       }
     }
     fetch_v(min(j + 1, nsub - 1));
@@ -482,11 +561,8 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     take_tokens<IO, true>(tok, L, qr, kr, qv, gr);
     // A: stage the state, dO, beta, P, X and the decay totals
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = (t >> 4) + 32 * m;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.S[row * kLS + scol + e] = sr[m][e];
-    }
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<f32x4 *>(sm.S + ((t >> 4) + 32 * m) * kLS + scol) = sr[m];
     sm.beta[t & 15] = (t & 15) < L ? braw : 0.f;
     (t < 256 ? sm.P : sm.X)[((t >> 4) & 15) * kLM + (t & 15)] = pr;
 #pragma unroll
@@ -502,8 +578,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     take_tile<IO>(vraw, L, g4, vd);
     if (w < 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm(acc, kD, l16, g4, [&](int m, int kk) { return sm.Kt[m * kLT + kk]; },
-         [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
+      mmA4(acc, kD, l16, g4, sm.Kt, kLT, [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
       f32x4 wr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -524,8 +599,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
         acc = mfma(scale * sm.P[(4 * g4 + tt) * kLM + l16], vd[tt], acc);
-      mm(acc, kD, l16, g4, [&](int m, int kk) { return sm.Kb[m * kLT + kk]; },
-         [&](int kk, int nn) { return sm.dS[kk * kLS + 16 * vt + nn]; });
+      mmA4(acc, kD, l16, g4, sm.Kb, kLT, [&](int kk, int nn) { return sm.dS[kk * kLS + 16 * vt + nn]; });
       f32x4 dw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) dw = mfma(sm.X[(4 * g4 + tt) * kLM + l16], acc[tt], dw);
@@ -544,8 +618,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     const int ct = w;
     if (w == 0) {  // dA = -tril(dW U^T)
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm(acc, kNC, l16, g4, [&](int m, int kk) { return sm.dW[m * kLB + kk]; },
-         [&](int kk, int nn) { return sm.U[nn * kLB + kk]; });
+      mm4(acc, kNC, l16, g4, sm.dW, kLB, sm.U, kLB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
@@ -553,8 +626,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
       }
     } else if (w == 1) {  // dP = scale tril(dO U^T)
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm(acc, kNC, l16, g4, [&](int m, int kk) { return sm.dOb[m * kLB + kk]; },
-         [&](int kk, int nn) { return sm.U[nn * kLB + kk]; });
+      mm4(acc, kNC, l16, g4, sm.dOb, kLB, sm.U, kLB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
@@ -563,25 +635,26 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     } else if (w == 2) {  // dbeta, W part: sum_v dW (V - KS)
       float a = 0.f;
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv)
-        a = fmaf(sm.dW[l16 * kLB + 16 * g4 + vv], sm.VmKS[l16 * kLB + 16 * g4 + vv], a);
+      for (int v4 = 0; v4 < 16; v4 += 4) {
+        const f32x4 x = ld4(sm.dW + l16 * kLB + 16 * g4 + v4);
+        const f32x4 y = ld4(sm.VmKS + l16 * kLB + 16 * g4 + v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a = fmaf(x[e], y[e], a);
+      }
       a += __shfl_xor(a, 16);
       a += __shfl_xor(a, 32);
       if (g4 == 0) part[kPdB + l16] = a;
     }
     {  // dKt = -(beta dW) S^T, dQt = scale dO S^T, dKb = U dS^T: channel tile ct
       f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-      mm(a0, kNC, l16, g4, [&](int m, int kk) { return -sm.beta[m] * sm.dW[m * kLB + kk]; },
-         [&](int kk, int nn) { return sm.S[(16 * ct + nn) * kLS + kk]; });
-      mm(a1, kNC, l16, g4, [&](int m, int kk) { return scale * sm.dOb[m * kLB + kk]; },
-         [&](int kk, int nn) { return sm.S[(16 * ct + nn) * kLS + kk]; });
-      mm(a2, kNC, l16, g4, [&](int m, int kk) { return sm.U[m * kLB + kk]; },
-         [&](int kk, int nn) { return sm.dS[(16 * ct + nn) * kLS + kk]; });
+      mm4(a0, kNC, l16, g4, sm.dW, kLB, sm.S + 16 * ct * kLS, kLS);
+      mm4(a1, kNC, l16, g4, sm.dOb, kLB, sm.S + 16 * ct * kLS, kLS);
+      mm4(a2, kNC, l16, g4, sm.U, kLB, sm.dS + 16 * ct * kLS, kLS);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = (4 * g4 + i) * kD + 16 * ct + l16;
-        part[kPdKt + o] = a0[i];
-        part[kPdQt + o] = a1[i];
+        part[kPdKt + o] = -sm.beta[4 * g4 + i] * a0[i];  // row factors of -(beta dW) and scale dO
+        part[kPdQt + o] = scale * a1[i];
         part[kPdKb + o] = a2[i];
       }
     }
@@ -589,8 +662,11 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
       const int cc = 16 * ct + l16;
       float a = 0.f;
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv)
-        a = fmaf(sm.dS[cc * kLS + 16 * g4 + vv], sm.S[cc * kLS + 16 * g4 + vv], a);
+      for (int v4 = 0; v4 < 16; v4 += 4) {
+        const f32x4 x = ld4(sm.dS + cc * kLS + 16 * g4 + v4), y = ld4(sm.S + cc * kLS + 16 * g4 + v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a = fmaf(x[e], y[e], a);
+      }
       a += __shfl_xor(a, 16);
       a += __shfl_xor(a, 32);
       if (g4 == 0) part[kPdGam + cc] = a;
@@ -627,136 +703,213 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- 3. finalize
-// Workgroup of 512 threads per (sequence, head, j0, quarter of the key
-// channels): sub-chunks j0, j0 + stride, ...; thread (row r, channel c) forms
-// dq, dk, dg of token r, channel c.  The Ab and P terms: row r's pairs
-// (r, s <= r) and the pairs (s >= r, r) in which token r is the earlier one,
-// each with its own e^{G_r - G_s} <= 1.  LDS is double-buffered by sub-chunk
-// parity, so three barriers per sub-chunk suffice.
-constexpr int kFC = 32;  // key channels per finalize workgroup
-constexpr int kFT = kFC * kSC;
-
-struct FinSmem {
-  float dA[kSC * kSC], dP[kSC * kSC], sb[kSC];
-  float kx[kSC][kFC], qx[kSC][kFC], gx[kSC][kFC], Gs[kSC][kFC], dGs[kSC][kFC], tl[kSC][kFC];
-};
+// Workgroup of 256 threads per (sequence, head, j0, half of the key channels):
+// sub-chunks j0, j0 + stride, ...  Wave w owns channel tile 4 half + w; lane
+// (l16, g4) holds tokens 4 g4 + i of that tile's channel l16 (the matrix-core
+// result layout).
+//
+// The Ab and P terms of dk, dq and dG are sums over token pairs weighted by
+// e^{G_r - G_s}.  With the reference M = G at the sub-chunk's token 7 they are
+// products of 16 x 16 matrices with 16 x 16 channel tiles:
+//   dk_row = e^{G-M} o ((beta dA) (k e^{M-G})),   dq_row = e^{G-M} o (dP (k e^{M-G})),
+//   dk_col = e^{M-G} o ((beta dA)^T (k e^{G-M}) + dP^T (q e^{G-M})),
+//   dG    += k o dk_row + q o dq_row - k o dk_col,
+// exact up to rounding while every |G - M| in the wave's tile stays within
+// kRefSpan (each factor below e^60).  Otherwise the wave sums the pairs one by
+// one, each with its own exponential.
+constexpr int kFT = 256;
 
 template <class IO>
 __global__ __launch_bounds__(kFT) void bwd_finalize_kernel(BwdParams p, int stride) {
+  constexpr int kFH = kD / 2;   // channels per workgroup
+  constexpr int kLF = kFH + 4;  // LDS row stride
+  __shared__ __attribute__((aligned(16))) float kx[kSC * kLF], qx[kSC * kLF], Gs[kSC * kLF];
+  __shared__ float dA[kSC * kLM], dP[kSC * kLM], sb[kSC], tot[4 * kFH];
   int64_t unit;
-  int quarter;
-  xcd_unit(blockIdx.x, kD / kFC, unit, quarter);
+  int half;
+  xcd_unit(blockIdx.x, 2, unit, half);
   if (unit >= p.chains * stride) return;
-  const int chain = (int)(unit / stride), j0 = (int)(unit % stride), c0 = quarter * kFC;
+  const int chain = (int)(unit / stride), j0 = (int)(unit % stride);
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
-  const int t = threadIdx.x, cl = t % kFC, r = t / kFC, c = c0 + cl;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int cl = t & (kFH - 1), hh = t >> 6;  // staging: channel cl, rows 4 hh .. 4 hh + 3
+  const int cs = half * kFH + cl;
   const IO *q = reinterpret_cast<const IO *>(p.q), *k = reinterpret_cast<const IO *>(p.k);
   const int64_t rowstride = (int64_t)p.H * kD;
-  __shared__ FinSmem smb[2];
   const int nsub = (int)((len + kSC - 1) / kSC);
-  // Loads of one sub-chunk, issued one sub-chunk ahead (unconditional: rows past
-  // L read row L - 1 and are masked at use; every thread consumes what it loads).
-  struct In {
-    IO k, q;
-    float g, dkt[2], dqt[2], dkb[2], da[2], dp[2], db[2], dgam[2], ab, beta;
-  } in;
-  const int o = r * kD + c;
-  auto fetch = [&](int j) {
+  for (int j = j0; j < nsub; j += stride) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
-    const float *pa = p.part + (slot_of(bos, n, j) * p.H + h) * kNB * (int64_t)kPart;
-    const int64_t off = (t0 + min(r, L - 1)) * rowstride + (int64_t)h * kD + c;
-    in.k = k[off];
-    in.q = q[off];
-    in.g = p.g[off];
+    const int64_t slot = slot_of(bos, n, j);
+    const float *pa = p.part + (slot * p.H + h) * kNB * (int64_t)kPart;
+    // loads (unconditional: rows past L read row L - 1 and are masked at use)
+    IO kv[4], qv[4];
+    float gv[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      in.dkt[b] = pa[b * kPart + kPdKt + o];
-      in.dqt[b] = pa[b * kPart + kPdQt + o];
-      in.dkb[b] = pa[b * kPart + kPdKb + o];
-      in.da[b] = pa[b * kPart + kPdA + (t & 255)];
-      in.dp[b] = pa[b * kPart + kPdP + (t & 255)];
-      in.db[b] = pa[b * kPart + kPdB + ((t >> 4) & 15)];
-      in.dgam[b] = pa[b * kPart + kPdGam + c];
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = (t0 + min(4 * hh + i, L - 1)) * rowstride + (int64_t)h * kD + cs;
+      kv[i] = k[off];
+      qv[i] = q[off];
+      gv[i] = p.g[off];
     }
-    in.ab = p.rec[(slot_of(bos, n, j) * p.H + h) * (int64_t)kRec + kRecAb + (t & 255)];
-    in.beta = p.beta[(t0 + min(t & 15, L - 1)) * p.H + h];
-  };
-  if (j0 < nsub) fetch(j0);
-  int parity = 0;
-  for (int j = j0; j < nsub; j += stride, parity ^= 1) {
-    FinSmem &sm = smb[parity];
-    const int64_t t0 = bos + (int64_t)j * kSC;
-    const int L = sub_len(len, j);
-    const bool live = r < L;
-    const int64_t off = (t0 + r) * rowstride + (int64_t)h * kD + c;
-    const float kr = live ? to_f32(in.k) : 0.f, qv = live ? to_f32(in.q) : 0.f;
-    sm.kx[r][cl] = kr;
-    sm.qx[r][cl] = qv;
-    sm.gx[r][cl] = live ? in.g : 0.f;
-    const float dKt = in.dkt[0] + in.dkt[1];
-    const float dQt = in.dqt[0] + in.dqt[1];
-    const float dKb = in.dkb[0] + in.dkb[1];
-    sm.dA[t & 255] = in.da[0] + in.da[1];  // equal copies from both halves of the threads
-    sm.dP[t & 255] = in.dp[0] + in.dp[1];
-    sm.sb[t & 15] = (t & 15) < L ? in.beta : 0.f;
-    const float ab = in.ab, db = in.db[0] + in.db[1], dgs = in.dgam[0] + in.dgam[1];
-    fetch(j + stride < nsub ? j + stride : j);  // unconditional: static wait counts
-    block_sync();
-    float Gr = 0.f, Gl = 0.f;
+    const int e = t;  // element of dA, dP, Ab
+    const float da_t = pa[kPdA + e] + pa[kPart + kPdA + e];
+    const float dp_t = pa[kPdP + e] + pa[kPart + kPdP + e];
+    const float bv = p.beta[(t0 + min(t & 15, L - 1)) * p.H + h];
+    const float ab_t = p.rec[(slot * p.H + h) * (int64_t)kRec + kRecAb + e];
+    const float db_t = pa[kPdB + (e >> 4)] + pa[kPart + kPdB + (e >> 4)];
+    const int cc = 16 * w + l16, c = half * kFH + cc;  // local and global channel
+    float pkt[4], pqt[4], pkb[4];
 #pragma unroll
-    for (int s = 0; s < kSC; ++s) {
-      const float x = sm.gx[s][cl];
-      Gr += s <= r ? x : 0.f;
-      Gl += x;
+    for (int i = 0; i < 4; ++i) {
+      const int o = (4 * g4 + i) * kD + c;
+      pkt[i] = pa[kPdKt + o] + pa[kPart + kPdKt + o];
+      pqt[i] = pa[kPdQt + o] + pa[kPart + kPdQt + o];
+      pkb[i] = pa[kPdKb + o] + pa[kPart + kPdKb + o];
     }
-    sm.Gs[r][cl] = Gr;
-    {  // dbeta_rb = sum_v dW (V - KS) (both halves) + sum_{s<rb} dA_{rb s} Ab_{rb s}:
-       // 16 lanes per row rb (every wave computes; the first quarter's waves 0-3 store)
-      const int rb = (t >> 4) & 15, sb_ = t & 15;
-      float a = sb_ < rb ? sm.dA[rb * kSC + sb_] * ab : 0.f;
+    const float pgam = pa[kPdGam + c] + pa[kPart + kPdGam + c];
+    // stage k, q and the cumulative decay G (rows past L: zero, G constant)
+    float gr[4], a = 0.f;
 #pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m);
-      if (c0 == 0 && t < kSC * kSC && sb_ == 0 && rb < L)
-        p.dbeta[(t0 + rb) * p.H + h] = a + db;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * hh + i;
+      const bool live = r < L;
+      kx[r * kLF + cl] = live ? to_f32(kv[i]) : 0.f;
+      qx[r * kLF + cl] = live ? to_f32(qv[i]) : 0.f;
+      a += live ? gv[i] : 0.f;
+      gr[i] = a;
+    }
+    tot[hh * kFH + cl] = a;
+    dA[(e >> 4) * kLM + (e & 15)] = da_t;
+    dP[(e >> 4) * kLM + (e & 15)] = dp_t;
+    sb[t & 15] = (t & 15) < L ? bv : 0.f;
+    {  // dbeta_rb = sum_v dW (V - KS) (both halves) + sum_{s<rb} dA_{rb s} Ab_{rb s}
+      const int rb = e >> 4, s_ = e & 15;
+      float x = s_ < rb ? da_t * ab_t : 0.f;
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+      if (half == 0 && s_ == 0 && rb < L) p.dbeta[(t0 + rb) * p.H + h] = x + db_t;
     }
     block_sync();
-    const float eg = __expf(Gr), eb = __expf(Gl - Gr);
-    float dk = dKt * eg + dKb * eb, dq = dQt * eg;
-    float dG = (dKt * kr + dQt * qv) * eg - dKb * kr * eb;
-    const float br = sm.sb[r];
+    {
+      float base = 0.f;
 #pragma unroll
-    for (int s = 0; s < kSC; ++s) {
-      const float Gx = sm.Gs[s][cl], kxs = sm.kx[s][cl];
-      if (s <= r) {  // pair (r, s): Ab_rs and P_rs
-        const float e = __expf(Gr - Gx);
-        const float da = s < r ? sm.dA[r * kSC + s] * br : 0.f, dp = sm.dP[r * kSC + s];
-        dk = fmaf(da * kxs, e, dk);
-        dq = fmaf(dp * kxs, e, dq);
-        dG = fmaf((da * kr + dp * qv) * kxs, e, dG);
+      for (int u = 0; u < 4; ++u) base += u < hh ? tot[u * kFH + cl] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Gs[(4 * hh + i) * kLF + cl] = base + gr[i];
+    }
+    block_sync();
+    // per-lane operands of the pair products (shared by both tiles)
+    float daA[4], dpA[4], daT[4], dpT[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int kk = 4 * g4 + tt;
+      daA[tt] = dA[l16 * kLM + kk] * sb[l16];
+      dpA[tt] = dP[l16 * kLM + kk];
+      daT[tt] = dA[kk * kLM + l16] * sb[kk];
+      dpT[tt] = dP[kk * kLM + l16];
+    }
+    float kr[4], qr[4], G[4], span = 0.f;
+    const float M = Gs[7 * kLF + cc], Gl = Gs[(kSC - 1) * kLF + cc];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      kr[i] = kx[r * kLF + cc];
+      qr[i] = qx[r * kLF + cc];
+      G[i] = Gs[r * kLF + cc];
+      span = fmaxf(span, fabsf(G[i] - M));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) span = fmaxf(span, __shfl_xor(span, m));
+    const bool fast = __builtin_amdgcn_readfirstlane(span <= kRefSpan ? 1 : 0) != 0;
+    {
+      float dk[4], dq[4], dG[4], tail = 0.f;
+      float ekm[4];  // e^{G - M}
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float eg = __expf(G[i]), eb = __expf(Gl - G[i]);
+        dk[i] = pkt[i] * eg + pkb[i] * eb;
+        dq[i] = pqt[i] * eg;
+        dG[i] = (pkt[i] * kr[i] + pqt[i] * qr[i]) * eg - pkb[i] * kr[i] * eb;
+        tail += pkb[i] * kr[i] * eb;
+        ekm[i] = __expf(G[i] - M);
       }
-      if (s >= r) {  // pair (s, r): token r is the earlier one
-        const float e = __expf(Gx - Gr);
-        const float da = s > r ? sm.dA[s * kSC + r] * sm.sb[s] : 0.f, dp = sm.dP[s * kSC + r];
-        const float coef = (da * kxs + dp * sm.qx[s][cl]) * e;
-        dk += coef;
-        dG = fmaf(-coef, kr, dG);
+      if (fast) {
+        f32x4 Kd, Ke, Qe;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float emk = __expf(M - G[i]);
+          Kd[i] = kr[i] * emk;
+          Ke[i] = kr[i] * ekm[i];
+          Qe[i] = qr[i] * ekm[i];
+        }
+        f32x4 Rk = {0.f, 0.f, 0.f, 0.f}, Rq = Rk, Ck = Rk;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          Rk = mfma(daA[tt], Kd[tt], Rk);
+          Rq = mfma(dpA[tt], Kd[tt], Rq);
+          Ck = mfma(daT[tt], Ke[tt], Ck);
+          Ck = mfma(dpT[tt], Qe[tt], Ck);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float row_k = ekm[i] * Rk[i], row_q = ekm[i] * Rq[i];
+          const float col_k = __expf(M - G[i]) * Ck[i];
+          dk[i] += row_k + col_k;
+          dq[i] += row_q;
+          dG[i] += kr[i] * (row_k - col_k) + qr[i] * row_q;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i;
+          const float br = sb[r];
+#pragma unroll 1
+          for (int s_ = 0; s_ < kSC; ++s_) {
+            const float Gx = Gs[s_ * kLF + cc], kxs = kx[s_ * kLF + cc];
+            const float ex = __expf(s_ <= r ? G[i] - Gx : Gx - G[i]);  // <= 1 for g <= 0
+            // pair (r, s_), s_ <= r
+            const float da = s_ < r ? dA[r * kLM + s_] * br : 0.f;
+            const float dp = s_ <= r ? dP[r * kLM + s_] : 0.f;
+            // pair (s_, r), s_ >= r
+            const float da2 = s_ > r ? dA[s_ * kLM + r] * sb[s_] : 0.f;
+            const float dp2 = s_ >= r ? dP[s_ * kLM + r] : 0.f;
+            const float row = (da * kr[i] + dp * qr[i]) * kxs;
+            const float coef = da2 * kxs + dp2 * qx[s_ * kLF + cc];
+            dk[i] += (da * kxs + coef) * ex;
+            dq[i] += dp * kxs * ex;
+            dG[i] += (row - coef * kr[i]) * ex;
+          }
+        }
+      }
+      // dg_r = sum_{s >= r} dG_s + (terms of the last row: every row's g reaches G_last)
+      float suf[4];
+      suf[3] = dG[3];
+#pragma unroll
+      for (int i = 2; i >= 0; --i) suf[i] = suf[i + 1] + dG[i];
+      float above = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float x = __shfl(suf[0], l16 + 16 * gg);
+        above += gg > g4 ? x : 0.f;
+      }
+      tail += __shfl_xor(tail, 16);
+      tail += __shfl_xor(tail, 32);
+      const float last = tail + pgam * __expf(Gl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
+        if (r < L) {
+          const int64_t off = (t0 + r) * rowstride + (int64_t)h * kD + c;
+          p.dq[off] = dq[i];
+          p.dk[off] = dk[i];
+          p.dg[off] = suf[i] + above + last;
+        }
       }
     }
-    sm.dGs[r][cl] = dG;
-    sm.tl[r][cl] = dKb * kr * eb;  // through G_last: belongs to the last row's dG
     block_sync();
-    // dg_r = sum_{s >= r} dG_s + (terms of the last row, which every row's g reaches)
-    float dg = dgs * __expf(Gl);
-#pragma unroll
-    for (int s = 0; s < kSC; ++s) dg += (s >= r ? sm.dGs[s][cl] : 0.f) + sm.tl[s][cl];
-    if (live) {
-      p.dq[off] = dq;
-      p.dk[off] = dk;
-      p.dg[off] = dg;
-    }
   }
 }
 
@@ -774,7 +927,7 @@ hipError_t launch_typed(const BwdParams &p, int64_t chains, int stride, hipStrea
                      stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_finalize_kernel<IO>, dim3((unsigned)xcd_grid(chains * stride, kD / kFC)),
+  hipLaunchKernelGGL(bwd_finalize_kernel<IO>, dim3((unsigned)xcd_grid(chains * stride, 2)),
                      dim3(kFT), 0, stream, p, stride);
   return hipGetLastError();
 }

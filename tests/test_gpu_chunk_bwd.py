@@ -92,6 +92,29 @@ def test_backward_strong_decay_and_no_state(kda):
     compare(got, ref)
 
 
+def test_backward_extreme_decay_exact_pairs(kda):
+    """Stretches of g = -20 per token: inside such a sub-chunk the reference
+    factors e^{+-(G - G_7)} would exceed e^60, so the prep and finalize passes
+    take every token pair with its own exponential there (the matrix-core path
+    elsewhere, in the same launch)."""
+    announce("chunk bwd extreme decay")
+    cfg = ki.PrefillConfig("t", (70, 41), 2, "f32", init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=79)
+    g = inp["g"]
+    g[3:19] = -20.0          # the first sequence's first sub-chunk and into the second
+    g[75:90, 1] = -20.0      # one head of the second sequence
+    gen = torch.Generator(device="cuda").manual_seed(80)
+    T = g.shape[0]
+    dO = torch.randn((T, 2, 128), generator=gen, device="cuda")
+    dSf = torch.randn((2, 2, 128, 128), generator=gen, device="cuda") * 0.1
+    got = grads_gpu(kda, inp, dO, dSf, scale=0.9)
+    torch.cuda.synchronize()
+    ref = oracle.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO,
+                               cu_seqlens=inp["cu_seqlens_host"],
+                               initial_state=inp["initial_state"], dS_final=dSf, scale=0.9)
+    compare(got, ref)
+
+
 def test_backward_fixed_batch_equals_varlen(kda):
     announce("chunk bwd fixed batch vs varlen")
     cfg = ki.PrefillConfig("t", (96, 96), 3, "bf16", init_std=0.1)
