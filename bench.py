@@ -130,6 +130,17 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
 
 
 BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 4 * D + 4 + 4 * 4 * D + 4     # 3,592
+# Matrix-core work of the backward per 16-token sub-chunk of one head (all 128
+# value columns, d = 128), product by product as the passes compute them; the
+# products run on fp32 matrix cores for both I/O dtypes.
+BWD_FLOPS_PER_SUBCHUNK_HEAD = (
+    (2 * 16 * D * D + 2 * 16 * 16 * D + 2 * D * 16 * D)            # states: KS, U, S update
+    + (2 * 16 * D * D * 2 + 2 * 16 * 16 * D * 5                    # serial: KS, Kb dS; U, P^T dO, dW, dA, dP
+       + 2 * 16 * D * D * 3 + 2 * 2 * D * 16 * D)                  #   dKt, dQt, dKb; dS update
+    + 2 * 2 * 16 * 16 * D                                          # prep: Ab, P
+    + 4 * 2 * 16 * 16 * D)                                         # finalize: pair terms
+BWD_FLOPS_PER_TOKEN_HEAD = BWD_FLOPS_PER_SUBCHUNK_HEAD // 16       # 344,064
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 def time_backward(kda, ki, workload, steps, warmup):
@@ -172,12 +183,17 @@ def time_backward(kda, ki, workload, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     alg = T * H * BWD_BYTES_PER_TOKEN_HEAD
+    flops = T * H * BWD_FLOPS_PER_TOKEN_HEAD
     del x, grads, ws, dO
     torch.cuda.empty_cache()
     return {"ms_per_step": ms, "steps": steps, "tokens_per_s": T / (ms * 1e-3),
             "algorithmic_bytes": alg, "gb_per_s": alg / (ms * 1e-3) / 1e9,
-            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "workload": workload,
-            "kernels": ["bwd_states_kernel", "bwd_serial_kernel", "bwd_finalize_kernel"]}
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_fp32_frac": flops / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+            "workload": workload,
+            "kernels": ["bwd_prep_kernel", "bwd_states_kernel", "bwd_serial_kernel",
+                        "bwd_finalize_kernel"]}
 
 
 def time_decode(kda, ki, steps, warmup=10, kernel="step", window=4):

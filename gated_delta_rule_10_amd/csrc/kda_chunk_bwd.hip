@@ -139,6 +139,22 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// Element at a wave-uniform base plus a 32-bit per-lane byte offset: the
+// address needs no 64-bit per-lane arithmetic (scalar base + vector offset).
+template <class T>
+__device__ __forceinline__ T at(const void *base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <class T>
+__device__ __forceinline__ void put(void *base, uint32_t byte_off, T v) {
+  *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off) = v;
+}
+// Base of token t0, head h in a [T, H, 128] tensor of T_ elements.
+template <class T_>
+__device__ __forceinline__ const T_ *row_base(const void *x, int64_t t0, int64_t rowstride, int h) {
+  return reinterpret_cast<const T_ *>(x) + t0 * rowstride + (int64_t)h * kD;
+}
+
 __device__ __forceinline__ f32x4 ld4(const float *p) {
   return *reinterpret_cast<const f32x4 *>(p);
 }
@@ -155,17 +171,22 @@ __device__ __forceinline__ void mm4(f32x4 &acc, int K, int l16, int g4, const fl
     for (int t = 0; t < 4; ++t) acc = mfma(x[t], y[t], acc);
   }
 }
-// A k-contiguous as in mm4, B read by b(k, n).
+// A k-contiguous as in mm4, B read by b(k, n); two accumulator chains.
 template <class FB>
 __device__ __forceinline__ void mmA4(f32x4 &acc, int K, int l16, int g4, const float *a, int lda,
                                      FB b) {
   const float *ar = a + l16 * lda + 4 * g4;
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const f32x4 x = ld4(ar + k0);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f32x4 x = ld4(ar + k0), y = ld4(ar + k0 + 16);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc = mfma(x[t], b(k0 + 4 * g4 + t, l16), acc);
+    for (int t = 0; t < 4; ++t) {
+      acc = mfma(x[t], b(k0 + 4 * g4 + t, l16), acc);
+      acc2 = mfma(y[t], b(k0 + 16 + 4 * g4 + t, l16), acc2);
+    }
   }
+  acc += acc2;
 }
 
 // ---------------------------------------------------------------- 0. prep
@@ -331,15 +352,15 @@ template <class IO, bool QT> struct TokRegs {
 template <class IO, bool QT>
 __device__ __forceinline__ void load_tokens(const BwdParams &p, int64_t t0, int L, int h, int c,
                                             int qr, TokRegs<IO, QT> &x) {
-  const IO *q = reinterpret_cast<const IO *>(p.q), *k = reinterpret_cast<const IO *>(p.k);
   const int64_t rowstride = (int64_t)p.H * kD;
+  const IO *kb = row_base<IO>(p.k, t0, rowstride, h), *qb = row_base<IO>(p.q, t0, rowstride, h);
+  const float *gb = row_base<float>(p.g, t0, rowstride, h);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = min(4 * qr + i, L - 1);
-    const int64_t off = (t0 + r) * rowstride + (int64_t)h * kD + c;
-    x.k[i] = k[off];
-    if (QT) x.q[i] = q[off];
-    x.g[i] = p.g[off];
+    const uint32_t e = (uint32_t)(min(4 * qr + i, L - 1) * (int)rowstride + c);
+    x.k[i] = at<IO>(kb, e * sizeof(IO));
+    if (QT) x.q[i] = at<IO>(qb, e * sizeof(IO));
+    x.g[i] = at<float>(gb, e * 4u);
   }
 }
 // Masked values: rows past L are zero.
@@ -360,12 +381,12 @@ __device__ __forceinline__ void take_tokens(const TokRegs<IO, QT> &x, int L, int
 template <class IO>
 __device__ __forceinline__ void load_tile(const void *base, const BwdParams &p, int64_t t0, int L,
                                           int h, int col0, int l16, int g4, IO *x) {
-  const IO *b = reinterpret_cast<const IO *>(base);
   const int64_t rowstride = (int64_t)p.H * kD;
+  const IO *b = row_base<IO>(base, t0, rowstride, h);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = min(4 * g4 + i, L - 1);
-    x[i] = b[(t0 + r) * rowstride + (int64_t)h * kD + col0 + l16];
+    const uint32_t e = (uint32_t)(min(4 * g4 + i, L - 1) * (int)rowstride + col0 + l16);
+    x[i] = at<IO>(b, e * sizeof(IO));
   }
 }
 template <class IO>
@@ -418,8 +439,9 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
     load_tokens<IO, false>(p, t0, L, h, c, qr, tok);
-    braw = p.beta[(t0 + min(t & 15, L - 1)) * p.H + h];
-    xr = p.rec[(slot_of(bos, n, j) * p.H + h) * (int64_t)kRec + kRecX + (t & 255)];
+    braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, L - 1) * p.H) * 4u);
+    xr = at<float>(p.rec + (slot_of(bos, n, j) * p.H + h) * (int64_t)kRec + kRecX,
+                   (uint32_t)(t & 255) * 4u);
   };
   auto fetch_v = [&](int j) {
     load_tile<IO>(p.v, p, bos + (int64_t)j * kSC, sub_len(len, j), h, blk * kNC + 16 * (w & 3),
@@ -538,12 +560,12 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     const int L = sub_len(len, j);
     const int64_t slot = slot_of(bos, n, j);
     load_tokens<IO, true>(p, t0, L, h, c, qr, tok);
-    braw = p.beta[(t0 + min(t & 15, L - 1)) * p.H + h];
+    braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, L - 1) * p.H) * 4u);
     const float *ck = p.ckpt + (slot * p.H + h) * (int64_t)(kD * kD) + blk * kNC;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      sr[m] = *reinterpret_cast<const f32x4 *>(ck + ((t >> 4) + 32 * m) * kD + scol);
-    pr = p.rec[(slot * p.H + h) * (int64_t)kRec + kRecP + t];  // P (t < 256), X
+      sr[m] = at<f32x4>(ck, (uint32_t)((((t >> 4) + 32 * m) * kD + scol) * 4));
+    pr = at<float>(p.rec + (slot * p.H + h) * (int64_t)kRec + kRecP, (uint32_t)t * 4u);  // P, X
   };
   auto fetch_vd = [&](int j) {  // v tile (waves 0-3) or dO tile (waves 4-7)
     load_tile<IO>(w < 4 ? p.v : p.dO, p, bos + (int64_t)j * kSC, sub_len(len, j), h,
@@ -593,6 +615,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) sm.U[(4 * g4 + i) * kLB + 16 * w + l16] = u[i];
     } else {
       const int vt = w - 4;
+      float *dvb = p.dv + t0 * rowstride + (int64_t)h * kD + blk * kNC;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.dOb[(4 * g4 + i) * kLB + 16 * vt + l16] = vd[i];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -608,7 +631,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
         const int r = 4 * g4 + i, col = 16 * vt + l16;
         sm.dW[r * kLB + col] = dw[i];
         if (r < L)  // dV = beta dW
-          p.dv[(t0 + r) * rowstride + (int64_t)h * kD + blk * kNC + col] = sm.beta[r] * dw[i];
+          put<float>(dvb, (uint32_t)(r * (int)rowstride + col) * 4u, sm.beta[r] * dw[i]);
       }
     }
     fetch_vd(max(j - 1, 0));
@@ -622,7 +645,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
-        part[kPdA + r * kSC + l16] = l16 < r ? -acc[i] : 0.f;
+        put<float>(part, (uint32_t)(kPdA + r * kSC + l16) * 4u, l16 < r ? -acc[i] : 0.f);
       }
     } else if (w == 1) {  // dP = scale tril(dO U^T)
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -630,7 +653,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
-        part[kPdP + r * kSC + l16] = l16 <= r ? scale * acc[i] : 0.f;
+        put<float>(part, (uint32_t)(kPdP + r * kSC + l16) * 4u, l16 <= r ? scale * acc[i] : 0.f);
       }
     } else if (w == 2) {  // dbeta, W part: sum_v dW (V - KS)
       float a = 0.f;
@@ -643,19 +666,31 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
       }
       a += __shfl_xor(a, 16);
       a += __shfl_xor(a, 32);
-      if (g4 == 0) part[kPdB + l16] = a;
+      if (g4 == 0) put<float>(part, (uint32_t)(kPdB + l16) * 4u, a);
     }
-    {  // dKt = -(beta dW) S^T, dQt = scale dO S^T, dKb = U dS^T: channel tile ct
+    {  // dKt = -(beta dW) S^T, dQt = scale dO S^T, dKb = U dS^T: channel tile ct, one
+       // k-loop with three independent chains (S read once for the first two)
       f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-      mm4(a0, kNC, l16, g4, sm.dW, kLB, sm.S + 16 * ct * kLS, kLS);
-      mm4(a1, kNC, l16, g4, sm.dOb, kLB, sm.S + 16 * ct * kLS, kLS);
-      mm4(a2, kNC, l16, g4, sm.U, kLB, sm.dS + 16 * ct * kLS, kLS);
+      const float *sr_ = sm.S + (16 * ct + l16) * kLS + 4 * g4;
+      const float *dsr = sm.dS + (16 * ct + l16) * kLS + 4 * g4;
+      const int ao = l16 * kLB + 4 * g4;
+#pragma unroll
+      for (int k0 = 0; k0 < kNC; k0 += 16) {
+        const f32x4 sv = ld4(sr_ + k0), dv_ = ld4(dsr + k0);
+        const f32x4 xw = ld4(sm.dW + ao + k0), xo = ld4(sm.dOb + ao + k0), xu = ld4(sm.U + ao + k0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          a0 = mfma(xw[tt], sv[tt], a0);
+          a1 = mfma(xo[tt], sv[tt], a1);
+          a2 = mfma(xu[tt], dv_[tt], a2);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int o = (4 * g4 + i) * kD + 16 * ct + l16;
-        part[kPdKt + o] = -sm.beta[4 * g4 + i] * a0[i];  // row factors of -(beta dW) and scale dO
-        part[kPdQt + o] = scale * a1[i];
-        part[kPdKb + o] = a2[i];
+        const uint32_t o = (uint32_t)((4 * g4 + i) * kD + 16 * ct + l16) * 4u;
+        put<float>(part + kPdKt, o, -sm.beta[4 * g4 + i] * a0[i]);  // row factors -beta, scale
+        put<float>(part + kPdQt, o, scale * a1[i]);
+        put<float>(part + kPdKb, o, a2[i]);
       }
     }
     {  // dGam (before Gam) = rowsum(dS o S), channels of tile ct
@@ -669,28 +704,42 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
       }
       a += __shfl_xor(a, 16);
       a += __shfl_xor(a, 32);
-      if (g4 == 0) part[kPdGam + cc] = a;
+      if (g4 == 0) put<float>(part, (uint32_t)(kPdGam + cc) * 4u, a);
     }
     // dS <- Gam dS + Kt^T (-beta dW) + Qt^T (scale dO): channel tile ct, value tiles 0..3
-    // (this wave alone reads rows of tile ct of dS in this stage)
-#pragma unroll 1
-    for (int vtile = 0; vtile < 4; ++vtile) {
-      f32x4 acc;
+    // as four independent chains (this wave alone reads rows of tile ct of dS here)
+    {
+      f32x4 acc[4];
+      float ktv[4], qtv[4], nb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int cc = 16 * ct + 4 * g4 + i;
-        acc[i] = sm.gam[cc] * sm.dS[cc * kLS + 16 * vtile + l16];
+      for (int tt = 0; tt < 4; ++tt) {
+        const int kk = 4 * g4 + tt;
+        ktv[tt] = sm.Kt[kk * kLT + 16 * ct + l16];
+        qtv[tt] = sm.Qt[kk * kLT + 16 * ct + l16];
+        nb[tt] = -sm.beta[kk];
+      }
+#pragma unroll
+      for (int vtile = 0; vtile < 4; ++vtile) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cc = 16 * ct + 4 * g4 + i;
+          acc[vtile][i] = sm.gam[cc] * sm.dS[cc * kLS + 16 * vtile + l16];
+        }
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int kk = 4 * g4 + tt;
-        acc = mfma(sm.Kt[kk * kLT + 16 * ct + l16],
-                   -sm.beta[kk] * sm.dW[kk * kLB + 16 * vtile + l16], acc);
-        acc = mfma(sm.Qt[kk * kLT + 16 * ct + l16], scale * sm.dOb[kk * kLB + 16 * vtile + l16],
-                   acc);
+#pragma unroll
+        for (int vtile = 0; vtile < 4; ++vtile) {
+          acc[vtile] = mfma(ktv[tt], nb[tt] * sm.dW[kk * kLB + 16 * vtile + l16], acc[vtile]);
+          acc[vtile] = mfma(qtv[tt], scale * sm.dOb[kk * kLB + 16 * vtile + l16], acc[vtile]);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.dS[(16 * ct + 4 * g4 + i) * kLS + 16 * vtile + l16] = acc[i];
+      for (int vtile = 0; vtile < 4; ++vtile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.dS[(16 * ct + 4 * g4 + i) * kLS + 16 * vtile + l16] = acc[vtile][i];
     }
     block_sync();
   }
