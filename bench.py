@@ -143,9 +143,10 @@ BWD_FLOPS_PER_TOKEN_HEAD = BWD_FLOPS_PER_SUBCHUNK_HEAD // 16       # 344,064
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
-def time_backward(kda, ki, workload, steps, warmup):
+def time_backward(kda, ki, workload, steps, warmup, cpu_seconds=0.0):
     """The chunked backward on the prefill workload: gradients of <dO, o> with
-    dO ~ N(0, 1) in the I/O dtype; grads and workspace allocated once."""
+    dO ~ N(0, 1) in the I/O dtype; grads and workspace allocated once.  With
+    cpu_seconds > 0 the oracle's backward is timed beside it (cpu_baseline_bwd)."""
     import torch
     cfg = ki.CONFIGS[workload]
     x = ki.make_prefill(cfg, device="cuda", seed=1002)
@@ -184,6 +185,7 @@ def time_backward(kda, ki, workload, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     alg = T * H * BWD_BYTES_PER_TOKEN_HEAD
     flops = T * H * BWD_FLOPS_PER_TOKEN_HEAD
+    cpu = cpu_baseline_bwd(x, dO, cpu_seconds) if cpu_seconds > 0 else None
     del x, grads, ws, dO
     torch.cuda.empty_cache()
     return {"ms_per_step": ms, "steps": steps, "tokens_per_s": T / (ms * 1e-3),
@@ -193,7 +195,50 @@ def time_backward(kda, ki, workload, steps, warmup):
             "mfma_fp32_frac": flops / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
             "workload": workload,
             "kernels": ["bwd_prep_kernel", "bwd_states_kernel", "bwd_serial_kernel",
-                        "bwd_finalize_kernel"]}
+                        "bwd_finalize_kernel"],
+            "cpu_baseline": cpu}
+
+
+BWD_CPU_TOKENS = 1024  # tokens per chain in the oracle's backward sample
+
+
+def cpu_baseline_bwd(x, dO, seconds):
+    """Time the oracle's backward (the fp64 token loop in reverse mode, as it
+    stands: single-threaded, every state kept) on a bounded sample: one
+    (sequence, head) chain per host thread, its first BWD_CPU_TOKENS tokens,
+    the chains run concurrently from Python threads (the C call releases the
+    interpreter lock), repeated until `seconds` of wall time have passed."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+    oracle.load()
+    cores = min(len(os.sched_getaffinity(0)), oracle.max_threads())
+    cu = x["cu_seqlens_host"]
+    N, H = len(cu) - 1, x["heads"]
+    to = lambda t: t.detach().cpu().double().numpy()
+    samples = []
+    for i in range(cores):
+        n, h = i % N, (i * 7) % H
+        a = cu[n]
+        b = min(cu[n + 1], a + BWD_CPU_TOKENS)
+        sl = lambda t: to(t[a:b, h:h + 1])
+        samples.append((sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                        sl(dO)))
+    run = lambda smp: oracle.recurrent_bwd(*smp)
+    passes, t0 = 0, time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        while True:
+            list(ex.map(run, samples))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                break
+    token_heads = sum(smp[0].shape[0] for smp in samples) * passes
+    return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cores} (sequence, head) chains, the first {BWD_CPU_TOKENS} tokens of "
+                      f"each, oracle backward (fp64 reverse-mode token loop), one chain per "
+                      f"thread, run {passes} times; value = token-heads/s divided by {H} heads",
+            "token_heads_per_s": token_heads / dt, "seconds": dt}
 
 
 def time_decode(kda, ki, steps, warmup=10, kernel="step", window=4):
@@ -464,7 +509,8 @@ def main():
         line["decode"]["workload"] = DECODE_WORKLOAD
     if args.bwd:
         line["backward"] = time_backward(kda, ki, args.workload, max(2, args.steps // 4),
-                                         max(1, args.warmup // 4))
+                                         max(1, args.warmup // 4),
+                                         0.0 if args.no_cpu_baseline else args.cpu_seconds)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds,
                                             pre["gate_params"])
