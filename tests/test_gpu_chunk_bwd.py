@@ -154,3 +154,46 @@ def test_backward_full_b4_t8192_h96_last_tokens(kda):
         compare(sub, ref)
     del inp, got
     torch.cuda.empty_cache()
+
+
+def test_backward_b1_t256_h2_f32_whole(kda):
+    """The 256-token, 2-head fp32 workload, every gradient against the oracle."""
+    announce("chunk bwd b1 t256 h2 f32")
+    cfg = ki.CONFIGS["kda_fwd_b1_t256_h2_f32"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1001)
+    gen = torch.Generator(device="cuda").manual_seed(81)
+    dO = torch.randn(inp["q"].shape, generator=gen, device="cuda")
+    got = grads_gpu(kda, inp, dO, None, varlen=False)
+    torch.cuda.synchronize()
+    ref = oracle.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO,
+                               initial_state=inp["initial_state"])
+    compare(got, ref)
+
+
+def test_backward_t65536_h96_last_tokens(kda):
+    """One 65,536-token sequence, 96 heads, bf16, nonzero initial state, decay
+    floored at -5 (4,096 sub-chunks per chain in the serial passes); the last 64
+    tokens of two chains against the oracle run from the state the forward
+    reaches at token 65,472."""
+    announce("chunk bwd t65536 h96 last tokens")
+    cfg = ki.CONFIGS["kda_prefill_t65536_h96_bf16_s0_gclamp5"]
+    inp = ki.make_prefill(cfg, device="cuda", seed=1003)
+    T, H = inp["q"].shape[0], inp["heads"]
+    gen = torch.Generator(device="cuda").manual_seed(82)
+    dO = torch.randn((T, H, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    got = grads_gpu(kda, inp, dO, None, varlen=False)
+    torch.cuda.synchronize()
+    tail = 64
+    for h in (5, 90):
+        sl = lambda t: t[: T - tail, h:h + 1]
+        s0 = inp["initial_state"][:, h:h + 1]
+        _, s_mid = oracle.recurrent(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["g"]),
+                                    sl(inp["beta"]), initial_state=s0)
+        tl = lambda t: t[T - tail:, h:h + 1]
+        ref = oracle.recurrent_bwd(tl(inp["q"]), tl(inp["k"]), tl(inp["v"]), tl(inp["g"]),
+                                   tl(inp["beta"]), tl(dO), initial_state=s_mid)
+        sub = {k: (v[T - tail:, h:h + 1] if v is not None and k != "dinitial_state" else None)
+               for k, v in got.items()}
+        compare(sub, ref)
+    del inp, got
+    torch.cuda.empty_cache()
