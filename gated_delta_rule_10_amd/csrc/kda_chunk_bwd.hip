@@ -515,20 +515,23 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
 struct SerialSmem {
   float S[kD * kLS];         // incoming state of the sub-chunk, this half's columns
   float dS[kD * kLS];        // state gradient
-  float Kt[kSC * kLT], Qt[kSC * kLT], Kb[kSC * kLT];
+  float Kt[2][kSC * kLT], Qt[2][kSC * kLT], Kb[2][kSC * kLT];  // by sub-chunk parity
   float VmKS[kSC * kLB], U[kSC * kLB], dW[kSC * kLB], dOb[kSC * kLB];
   float P[kSC * kLM], X[kSC * kLM];
   float beta[kSC];
-  float gam[kD];
+  float gam[2][kD];
   float tot[4 * kD];
 };
 
 // ---------------------------------------------------------------- 2. serial
-// Per sub-chunk, in reverse: A stage inputs; B decay-weighted operands;
-// C waves 0-3: KS, W, U (value tile w), waves 4-7: dU = scale P^T dO + Kb dS,
-// dW = X^T dU, dv (value tile w - 4); D wave w, channel tile w: dKt, dQt, dKb,
-// dGam partials and dS <- Gam dS + Kt^T (-beta dW) + Qt^T (scale dO); waves 0-2
-// also dA, dP and the W part of dbeta.
+// Per sub-chunk j, in reverse, three barriers: A stage S, beta, P, X; C waves
+// 0-3: KS, W, U (value tile w), waves 4-7: dU = scale P^T dO + Kb dS,
+// dW = X^T dU, dv (value tile w - 4), and every thread the decay totals of
+// sub-chunk j - 1; D wave w, channel tile w: dKt, dQt, dKb, dGam partials and
+// dS <- Gam dS + Kt^T (-beta dW) + Qt^T (scale dO), waves 0-2 also dA, dP and
+// the W part of dbeta, and every thread the decay-weighted operands of
+// sub-chunk j - 1 into the other LDS buffer (vector work in the shadow of the
+// matrix-core chains).
 template <class IO>
 __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) SerialSmem sm;
@@ -549,17 +552,30 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     sm.dS[cc * kLS + vv] = p.dsf ? p.dsf[((int64_t)chain * kD + cc) * kD + blk * kNC + vv] : 0.f;
   }
   const int nsub = (int)((len + kSC - 1) / kSC);
+  if (nsub == 0) {  // empty sequence: dS0 = dS_final
+    block_sync();
+    if (p.ds0)
+      for (int e = t; e < kD * kNC; e += kBT) {
+        const int cc = e / kNC, vv = e % kNC;
+        p.ds0[((int64_t)chain * kD + cc) * kD + blk * kNC + vv] = sm.dS[cc * kLS + vv];
+      }
+    return;
+  }
   const int64_t rowstride = (int64_t)p.H * kD;
+  // Registers in flight (unconditional loads, every thread consumes what it loads):
+  // tokens of the next sub-chunk, its state / beta / P / X, the v or dO tile.
   TokRegs<IO, true> tok;
   IO vraw[4];
-  float braw = 0.f, pr = 0.f;  // consumed by every thread (as in the states pass)
+  float braw = 0.f, pr = 0.f;
   f32x4 sr[4];
   const int scol = 4 * (t & 15);  // state load: rows (t >> 4) + 32 m, columns scol..scol+3
-  auto fetch = [&](int j) {
+  auto fetch_tokens = [&](int j) {
+    load_tokens<IO, true>(p, bos + (int64_t)j * kSC, sub_len(len, j), h, c, qr, tok);
+  };
+  auto fetch_state = [&](int j) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
     const int64_t slot = slot_of(bos, n, j);
-    load_tokens<IO, true>(p, t0, L, h, c, qr, tok);
     braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, L - 1) * p.H) * 4u);
     const float *ck = p.ckpt + (slot * p.H + h) * (int64_t)(kD * kD) + blk * kNC;
 #pragma unroll
@@ -571,36 +587,49 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
     load_tile<IO>(w < 4 ? p.v : p.dO, p, bos + (int64_t)j * kSC, sub_len(len, j), h,
                   blk * kNC + 16 * (w & 3), l16, g4, vraw);
   };
-  if (nsub > 0) {
-    fetch(nsub - 1);
-    fetch_vd(nsub - 1);
-  }
+  // decay totals of the tokens in `tok` (sub-chunk of length L) to sm.tot
+  auto totals = [&](int L) {
+    float kr[4], qv[4], gr[4];
+    take_tokens<IO, true>(tok, L, qr, kr, qv, gr);
+    sm.tot[qr * kD + c] = (gr[0] + gr[1]) + (gr[2] + gr[3]);
+  };
+  // decay-weighted operands of the tokens in `tok` into buffer b (after totals)
+  auto operands = [&](int L, int b) {
+    float kr[4], qv[4], gr[4];
+    take_tokens<IO, true>(tok, L, qr, kr, qv, gr);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) gr[i] += gr[i - 1];
+    decay_operands<true>(kr, qv, gr, sm.tot, c, qr, sm.Kt[b], sm.Qt[b], sm.Kb[b], sm.gam[b]);
+  };
+  // prologue: operands of the last sub-chunk into buffer 0
+  fetch_tokens(nsub - 1);
+  fetch_state(nsub - 1);
+  fetch_vd(nsub - 1);
+  totals(sub_len(len, nsub - 1));
+  block_sync();
+  operands(sub_len(len, nsub - 1), 0);
+  fetch_tokens(max(nsub - 2, 0));
   for (int j = nsub - 1; j >= 0; --j) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
     const int64_t slot = slot_of(bos, n, j);
-    float kr[4], qv[4], gr[4];
-    take_tokens<IO, true>(tok, L, qr, kr, qv, gr);
-    // A: stage the state, dO, beta, P, X and the decay totals
+    const int b = (nsub - 1 - j) & 1;  // LDS buffer of this sub-chunk's operands
+    const int jn = max(j - 1, 0);      // next sub-chunk (j = 0: sub-chunk 0 again, unused)
+    const int Ln = sub_len(len, jn);
+    // A: stage the state, beta, P, X
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       *reinterpret_cast<f32x4 *>(sm.S + ((t >> 4) + 32 * m) * kLS + scol) = sr[m];
     sm.beta[t & 15] = (t & 15) < L ? braw : 0.f;
     (t < 256 ? sm.P : sm.X)[((t >> 4) & 15) * kLM + (t & 15)] = pr;
-#pragma unroll
-    for (int i = 1; i < 4; ++i) gr[i] += gr[i - 1];
-    sm.tot[qr * kD + c] = gr[3];
-    block_sync();
-    // B
-    decay_operands<true>(kr, qv, gr, sm.tot, c, qr, sm.Kt, sm.Qt, sm.Kb, sm.gam);
-    fetch(max(j - 1, 0));  // unconditional: static wait counts
+    fetch_state(jn);  // unconditional: static wait counts
     block_sync();
     // C
     float vd[4];  // v tile (waves 0-3) or dO tile (waves 4-7)
     take_tile<IO>(vraw, L, g4, vd);
     if (w < 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mmA4(acc, kD, l16, g4, sm.Kt, kLT, [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
+      mmA4(acc, kD, l16, g4, sm.Kt[b], kLT, [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
       f32x4 wr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -622,7 +651,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
         acc = mfma(scale * sm.P[(4 * g4 + tt) * kLM + l16], vd[tt], acc);
-      mmA4(acc, kD, l16, g4, sm.Kb, kLT, [&](int kk, int nn) { return sm.dS[kk * kLS + 16 * vt + nn]; });
+      mmA4(acc, kD, l16, g4, sm.Kb[b], kLT, [&](int kk, int nn) { return sm.dS[kk * kLS + 16 * vt + nn]; });
       f32x4 dw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) dw = mfma(sm.X[(4 * g4 + tt) * kLM + l16], acc[tt], dw);
@@ -634,7 +663,8 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
           put<float>(dvb, (uint32_t)(r * (int)rowstride + col) * 4u, sm.beta[r] * dw[i]);
       }
     }
-    fetch_vd(max(j - 1, 0));
+    fetch_vd(jn);
+    totals(Ln);  // of sub-chunk jn, for its operands in D
     block_sync();
     // D
     float *part = p.part + ((slot * p.H + h) * kNB + blk) * (int64_t)kPart;
@@ -668,6 +698,9 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
       a += __shfl_xor(a, 32);
       if (g4 == 0) put<float>(part, (uint32_t)(kPdB + l16) * 4u, a);
     }
+    // operands of the next sub-chunk into the other buffer, then its tokens' loads
+    operands(Ln, b ^ 1);
+    fetch_tokens(max(j - 2, 0));  // unconditional: static wait counts
     {  // dKt = -(beta dW) S^T, dQt = scale dO S^T, dKb = U dS^T: channel tile ct, one
        // k-loop with three independent chains (S read once for the first two)
       f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
@@ -714,8 +747,8 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int kk = 4 * g4 + tt;
-        ktv[tt] = sm.Kt[kk * kLT + 16 * ct + l16];
-        qtv[tt] = sm.Qt[kk * kLT + 16 * ct + l16];
+        ktv[tt] = sm.Kt[b][kk * kLT + 16 * ct + l16];
+        qtv[tt] = sm.Qt[b][kk * kLT + 16 * ct + l16];
         nb[tt] = -sm.beta[kk];
       }
 #pragma unroll
@@ -723,7 +756,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int cc = 16 * ct + 4 * g4 + i;
-          acc[vtile][i] = sm.gam[cc] * sm.dS[cc * kLS + 16 * vtile + l16];
+          acc[vtile][i] = sm.gam[b][cc] * sm.dS[cc * kLS + 16 * vtile + l16];
         }
       }
 #pragma unroll
