@@ -397,18 +397,20 @@ __device__ __forceinline__ void take_tile(const IO *x, int L, int g4, float *y) 
 
 struct StatesSmem {
   float S[kD * kLS];
-  float Kt[kSC * kLT], Kb[kSC * kLT];
+  float Kt[2][kSC * kLT], Kb[2][kSC * kLT];  // by sub-chunk parity
   float U[kSC * kLB];
   float X[kSC * kLM];
   float beta[kSC];
-  float gam[kD];
+  float gam[2][kD];
   float tot[4 * kD];
 };
 
 // ---------------------------------------------------------------- 1. states
-// Waves 0-3: KS = Kt S, W = beta (V - KS), U = X W for value tile w (registers);
-// waves 4-7: the state checkpoint.  Then all eight: S <- Gam S + Kb^T U, wave w
-// owning channel tile w.
+// Per sub-chunk j, three barriers: A stage beta, X; C waves 0-3: KS = Kt S,
+// W = beta (V - KS), U = X W for value tile w (registers), waves 4-7: the state
+// checkpoint, every thread the decay totals of sub-chunk j + 1; D all eight:
+// S <- Gam S + Kb^T U (wave w owns channel tile w) and the decay-weighted
+// operands of sub-chunk j + 1 into the other LDS buffer.
 template <class IO>
 __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) StatesSmem sm;
@@ -428,18 +430,19 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
     sm.S[cc * kLS + vv] = p.s0 ? p.s0[((int64_t)chain * kD + cc) * kD + blk * kNC + vv] : 0.f;
   }
   const int nsub = (int)((len + kSC - 1) / kSC);
-  // registers for the sub-chunk about to be processed (raw, masked at use)
+  if (nsub == 0) return;
+  // Registers in flight (unconditional loads; X and beta are written to LDS by
+  // every thread, copies of equal values, so every thread consumes its loads):
+  // tokens two sub-chunks ahead, beta and X one ahead, the v tile one ahead.
   TokRegs<IO, false> tok;
   IO vraw[4];
-  // Every thread consumes what it loads (X and beta are written to LDS by all
-  // threads, copies of equal values), so no wave is left with loads it never
-  // waits for.
   float braw = 0.f, xr = 0.f;
-  auto fetch = [&](int j) {
+  auto fetch_tokens = [&](int j) {
+    load_tokens<IO, false>(p, bos + (int64_t)j * kSC, sub_len(len, j), h, c, qr, tok);
+  };
+  auto fetch_small = [&](int j) {
     const int64_t t0 = bos + (int64_t)j * kSC;
-    const int L = sub_len(len, j);
-    load_tokens<IO, false>(p, t0, L, h, c, qr, tok);
-    braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, L - 1) * p.H) * 4u);
+    braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, sub_len(len, j) - 1) * p.H) * 4u);
     xr = at<float>(p.rec + (slot_of(bos, n, j) * p.H + h) * (int64_t)kRec + kRecX,
                    (uint32_t)(t & 255) * 4u);
   };
@@ -447,31 +450,43 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
     load_tile<IO>(p.v, p, bos + (int64_t)j * kSC, sub_len(len, j), h, blk * kNC + 16 * (w & 3),
                   l16, g4, vraw);
   };
-  if (nsub > 0) {
-    fetch(0);
-    fetch_v(0);
-  }
-  for (int j = 0; j < nsub; ++j) {
-    const int L = sub_len(len, j);
+  auto totals = [&](int L) {
     float kr[4], gr[4];
     take_tokens<IO, false>(tok, L, qr, kr, nullptr, gr);
-    // A: small matrices and the decay totals
-    sm.beta[t & 15] = (t & 15) < L ? braw : 0.f;
-    sm.X[((t & 255) >> 4) * kLM + (t & 15)] = xr;
+    sm.tot[qr * kD + c] = (gr[0] + gr[1]) + (gr[2] + gr[3]);
+  };
+  auto operands = [&](int L, int b) {
+    float kr[4], gr[4];
+    take_tokens<IO, false>(tok, L, qr, kr, nullptr, gr);
 #pragma unroll
     for (int i = 1; i < 4; ++i) gr[i] += gr[i - 1];
-    sm.tot[qr * kD + c] = gr[3];
-    block_sync();
-    // B: decay-weighted operands; next sub-chunk's tokens in flight
-    decay_operands<false>(kr, nullptr, gr, sm.tot, c, qr, sm.Kt, nullptr, sm.Kb, sm.gam);
-    fetch(min(j + 1, nsub - 1));  // unconditional: static wait counts
+    decay_operands<false>(kr, nullptr, gr, sm.tot, c, qr, sm.Kt[b], nullptr, sm.Kb[b], sm.gam[b]);
+  };
+  // prologue: operands of sub-chunk 0 into buffer 0
+  fetch_tokens(0);
+  fetch_small(0);
+  fetch_v(0);
+  totals(sub_len(len, 0));
+  block_sync();
+  operands(sub_len(len, 0), 0);
+  fetch_tokens(min(1, nsub - 1));
+  for (int j = 0; j < nsub; ++j) {
+    const int L = sub_len(len, j);
+    const int b = j & 1;
+    const int jn = min(j + 1, nsub - 1);  // next sub-chunk (the last one: itself, unused)
+    const int Ln = sub_len(len, jn);
+    // A: beta and X of this sub-chunk
+    sm.beta[t & 15] = (t & 15) < L ? braw : 0.f;
+    sm.X[((t & 255) >> 4) * kLM + (t & 15)] = xr;
+    fetch_small(jn);  // unconditional: static wait counts
     block_sync();
     // C
     if (w < 4) {
       float vt[4];
       take_tile<IO>(vraw, L, g4, vt);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mmA4(acc, kD, l16, g4, sm.Kt, kLT, [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
+      mmA4(acc, kD, l16, g4, sm.Kt[b], kLT,
+           [&](int kk, int nn) { return sm.S[kk * kLS + 16 * w + nn]; });
       f32x4 wr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) wr[i] = sm.beta[4 * g4 + i] * (vt[i] - acc[i]);
@@ -489,24 +504,37 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
         *reinterpret_cast<f32x4 *>(ck + row * kD + col) = ld4(sm.S + row * kLS + col);
       }
     }
-    fetch_v(min(j + 1, nsub - 1));
+    fetch_v(jn);
+    totals(Ln);  // of the next sub-chunk, for its operands in D
     block_sync();
-    // D: S <- Gam S + Kb^T U, channel tile w, value tiles 0..3
-#pragma unroll 1
-    for (int vtile = 0; vtile < 4; ++vtile) {
-      f32x4 acc;
+    // D: S <- Gam S + Kb^T U, channel tile w, value tiles 0..3 (independent chains);
+    // the next sub-chunk's operands into the other buffer
+    operands(Ln, b ^ 1);
+    fetch_tokens(min(j + 2, nsub - 1));  // unconditional: static wait counts
+    {
+      f32x4 acc[4];
+      float kbv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int cc = 16 * w + 4 * g4 + i;
-        acc[i] = sm.gam[cc] * sm.S[cc * kLS + 16 * vtile + l16];
-      }
+      for (int tt = 0; tt < 4; ++tt) kbv[tt] = sm.Kb[b][(4 * g4 + tt) * kLT + 16 * w + l16];
+#pragma unroll
+      for (int vtile = 0; vtile < 4; ++vtile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cc = 16 * w + 4 * g4 + i;
+          acc[vtile][i] = sm.gam[b][cc] * sm.S[cc * kLS + 16 * vtile + l16];
+        }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int kk = 4 * g4 + tt;
-        acc = mfma(sm.Kb[kk * kLT + 16 * w + l16], sm.U[kk * kLB + 16 * vtile + l16], acc);
+#pragma unroll
+        for (int vtile = 0; vtile < 4; ++vtile)
+          acc[vtile] = mfma(kbv[tt], sm.U[kk * kLB + 16 * vtile + l16], acc[vtile]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.S[(16 * w + 4 * g4 + i) * kLS + 16 * vtile + l16] = acc[i];
+      for (int vtile = 0; vtile < 4; ++vtile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.S[(16 * w + 4 * g4 + i) * kLS + 16 * vtile + l16] = acc[vtile][i];
     }
     block_sync();
   }
