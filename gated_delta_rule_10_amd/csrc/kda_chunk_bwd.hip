@@ -68,7 +68,7 @@ constexpr int kPT = 256;         // threads of the prep pass
 constexpr int kLS = kNC + 4;     // row stride of the state halves
 constexpr int kLT = kD + 4;      // row stride of 16 x 128 token matrices
 constexpr int kLB = kNC + 4;     // row stride of 16 x 64 token blocks
-constexpr int kLM = kSC + 1;     // row stride of 16 x 16 matrices (prep pass: odd)
+constexpr int kLM = kSC + 1;     // row stride of 16 x 16 matrices (odd: column reads)
 
 struct BwdParams {
   const void *q, *k, *v, *dO;
@@ -122,19 +122,10 @@ __device__ __forceinline__ int sub_len(int64_t len, int j) {
   return (int)(rest < kSC ? rest : kSC);
 }
 
-// acc (a 16 x 16 tile; lane holds rows 4 g4 + i, column l16) += sum_{k<K} A(m, k) B(k, n)
-// for K a multiple of 16, on fp32 matrix cores; a(m, k) and b(k, n) read the operands.
-template <class FA, class FB>
-__device__ __forceinline__ void mm(f32x4 &acc, int K, int l16, int g4, FA a, FB b) {
-  for (int k0 = 0; k0 < K; k0 += 16) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kk = k0 + 4 * g4 + t;
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, kk), b(kk, l16), acc, 0, 0, 0);
-    }
-  }
-}
-
+// acc += a b on fp32 matrix cores (V_MFMA_F32_16X16X4_F32): acc is a 16 x 16
+// tile, lane (l16, g4) holding rows 4 g4 + i of column l16; per instruction
+// lane (l16, g4) supplies A[l16][k] and B[k][l16] for its own k, so a 16-deep
+// contraction is four instructions with k = 4 g4 + t (t = 0..3).
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
@@ -159,8 +150,9 @@ __device__ __forceinline__ f32x4 ld4(const float *p) {
   return *reinterpret_cast<const f32x4 *>(p);
 }
 
-// As mm, with A row m at a + m lda and B column n at b + n ldb both stored
-// k-contiguous (16-byte aligned): four k-values per 16-byte LDS read.
+// acc += A B over K (a multiple of 16), with A row m at a + m lda and B column
+// n at b + n ldb both stored k-contiguous (16-byte aligned): four k-values per
+// 16-byte LDS read.
 __device__ __forceinline__ void mm4(f32x4 &acc, int K, int l16, int g4, const float *a, int lda,
                                     const float *b, int ldb) {
   const float *ar = a + l16 * lda + 4 * g4, *bc = b + l16 * ldb + 4 * g4;
