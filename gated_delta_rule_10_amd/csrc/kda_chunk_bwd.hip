@@ -18,7 +18,9 @@
 //   W = beta (V - Kt S),  U = (I + A)^{-1} W,  O = scale (Qt S + P U),
 //   S_next = Gam S + Kb^T U.
 // Every exponent is <= 0 (a cumulative decay, or a difference G_r - G_s with
-// s <= r), so nothing overflows in fp32 for any decay.  The backward of one
+// s <= r), so nothing overflows in fp32 for any decay; the matrix-core form of
+// the e^{G_r - G_s} terms splits them at the sub-chunk's token 7 into two
+// factors and is used only while those stay within e^60.  The backward of one
 // sub-chunk, with dS the gradient of its outgoing state:
 //   dU = scale P^T dO + Kb dS,   dW = (I + A)^{-T} dU,
 //   dA = -tril(dW U^T, -1),      dP = scale tril(dO U^T),
