@@ -257,6 +257,17 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims")
 
 
+def _out_like(out, like, name="out"):
+    """A new output shaped like ``like``, or the caller's, checked (the kernels
+    see only its pointer)."""
+    if out is None:
+        return torch.empty_like(like)
+    _need(out, name, dtype=like.dtype, ndim=like.dim())
+    if out.shape != like.shape:
+        raise ValueError(f"{name} must be {list(like.shape)}")
+    return out
+
+
 def _gate(H, A_log, dt_bias, lower_bound, beta_logits):
     """Fill a kda_gate: the lower-bounded gate when A_log is given, else log-decay g."""
     gt = Gate()
@@ -349,11 +360,15 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
         _need(initial_state, "initial_state", dtype=torch.float32, ndim=4)
         if initial_state.shape != (N, H, D, D):
             raise ValueError(f"initial_state must be [{N}, {H}, {D}, {D}]")
-    o = out if out is not None else torch.empty_like(q)
+    o = _out_like(out, q)
     if not output_final_state:
         final_state = None
     elif final_state is None:
         final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=q.device)
+    else:  # the caller's: the kernels see only its pointer
+        _need(final_state, "final_state", dtype=torch.float32, ndim=4)
+        if final_state.shape != (N, H, D, D):
+            raise ValueError(f"final_state must be [{N}, {H}, {D}, {D}]")
     if cu_seqlens is not None and cu_seqlens_host is None:
         cu_seqlens_host = cu_seqlens.tolist()  # one device-to-host copy
     a, host = _chunk_args(q, N, cu_seqlens, cu_seqlens_host, scale, segments)
@@ -368,6 +383,8 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws_bytes)),
            "kda_chunk_fwd_workspace_size")
     if ws_bytes.value:
+        if workspace is not None:
+            _need(workspace, "workspace", dtype=torch.uint8, ndim=1)
         if workspace is None or workspace.numel() < ws_bytes.value:
             workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=q.device)
         a.workspace = workspace.data_ptr()
@@ -443,6 +460,17 @@ def chunk_bwd(q, k, v, g, beta, dO, cu_seqlens=None, cu_seqlens_host=None, initi
         out.setdefault("dinitial_state", torch.empty((N, H, D, D), **f32))
     else:
         out["dinitial_state"] = None
+    shapes = {"dq": (T, H, D), "dk": (T, H, D), "dv": (T, H, D), "dg": (T, H, D),
+              "dbeta": (T, H), "dinitial_state": (N, H, D, D)}
+    for name, shape in shapes.items():  # caller-supplied outputs: the kernels trust them
+        t = out[name]
+        if t is None:
+            continue
+        _need(t, name, dtype=torch.float32, ndim=len(shape))
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1)
     a = ChunkBwdArgs()
     host = None
     a.num_seqs = N
@@ -493,7 +521,7 @@ def recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=1.0, out=N
     B, H, D = q.shape
     if state_indices is not None:
         _need(state_indices, "state_indices", dtype=torch.int32, ndim=1)
-    o = out if out is not None else torch.empty_like(q)
+    o = _out_like(out, q)
     a = RecurrentStepArgs()
     a.batch, a.num_heads, a.head_dim = B, H, D
     a.io_dtype = _dtype_code(q.dtype)
@@ -565,7 +593,7 @@ def fused_decode_step(q, k, v, g, beta, state, conv_cache, conv_weight, state_in
     Returns o [B, H, 128].
     """
     lib = library()
-    o = out if out is not None else torch.empty_like(q)
+    o = _out_like(out, q)
     a = _fused_args(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices, scale,
                     l2_eps, out_norm, norm_weight, norm_eps, o, A_log, dt_bias, lower_bound,
                     beta_logits, token_dims=2)
@@ -588,7 +616,7 @@ def spec_verify_step(q, k, v, g, beta, state, conv_cache, conv_weight, replay=No
     is dropped.  Other arguments as in fused_decode_step.
     """
     lib = library()
-    o = out if out is not None else torch.empty_like(q)
+    o = _out_like(out, q)
     a = _fused_args(q, k, v, g, beta, state, conv_cache, conv_weight, state_indices, scale,
                     l2_eps, out_norm, norm_weight, norm_eps, o, A_log, dt_bias, lower_bound,
                     beta_logits, token_dims=3)

@@ -115,6 +115,25 @@ def test_backward_extreme_decay_exact_pairs(kda):
     compare(got, ref)
 
 
+def test_backward_rejects_missized_outputs(kda):
+    """Caller-supplied gradient buffers and workspace are checked on the host
+    (the kernels only see pointers); nothing is launched."""
+    cfg = ki.PrefillConfig("t", (32, 32), 2, "bf16")
+    inp = ki.make_prefill(cfg, device="cuda", seed=83)
+    dO = torch.zeros_like(inp["q"])
+    T, H = inp["q"].shape[:2]
+    bad = {"dq": torch.empty((T - 1, H, 128), device="cuda")}
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO, num_seqs=2,
+                      grads=bad)
+    with pytest.raises(TypeError):
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO, num_seqs=2,
+                      grads={"dbeta": torch.empty((T, H), device="cuda", dtype=torch.float64)})
+    with pytest.raises(TypeError):
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO, num_seqs=2,
+                      workspace=torch.empty(16, device="cuda"))
+
+
 def test_backward_fixed_batch_equals_varlen(kda):
     announce("chunk bwd fixed batch vs varlen")
     cfg = ki.PrefillConfig("t", (96, 96), 3, "bf16", init_std=0.1)
