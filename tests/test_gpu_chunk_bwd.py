@@ -115,6 +115,34 @@ def test_backward_extreme_decay_exact_pairs(kda):
     compare(got, ref)
 
 
+@pytest.mark.parametrize("case", ["beta0_g0", "scale0"])
+def test_backward_degenerate_parameters(kda, case):
+    """Degenerate values the method allows: beta = 0 on some tokens (no write,
+    A = 0 there) with g = 0 on some channels (no decay), and scale = 0 (o = 0,
+    so only the final-state gradient drives dq..dbeta)."""
+    announce(f"chunk bwd degenerate {case}")
+    cfg = ki.PrefillConfig("t", (45, 38), 2, "f32", init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=84)
+    gen = torch.Generator(device="cuda").manual_seed(85)
+    T = inp["q"].shape[0]
+    scale = 1.0
+    if case == "beta0_g0":
+        inp["beta"][::3] = 0.0
+        inp["g"][:, :, :40] = 0.0
+    else:
+        scale = 0.0
+    dO = torch.randn((T, 2, 128), generator=gen, device="cuda")
+    dSf = torch.randn((2, 2, 128, 128), generator=gen, device="cuda") * 0.1
+    got = grads_gpu(kda, inp, dO, dSf, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO,
+                               cu_seqlens=inp["cu_seqlens_host"],
+                               initial_state=inp["initial_state"], dS_final=dSf, scale=scale)
+    if case == "scale0":
+        assert float(got["dq"].abs().max()) == 0.0  # q only reaches the loss through o
+    compare(got, ref)
+
+
 def test_backward_rejects_missized_outputs(kda):
     """Caller-supplied gradient buffers and workspace are checked on the host
     (the kernels only see pointers); nothing is launched."""
