@@ -130,10 +130,13 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
     g_first = first.g[tok0 + cc];
   }
 
-  // On large grids each workgroup idles ~3.4 us (127 x 64 clocks) before its state
-  // loads: measured faster on the 512 x 96 step (1.057 against 1.189 ms), equal
-  // bytes; 96 x 64 clocks measured 1.109 and twice 127 x 64 clocks 1.219 ms.
-  if (p.stagger) __builtin_amdgcn_s_sleep(127);
+  // On large grids each workgroup idles before its state loads: ~3.4 us (127 x 64
+  // clocks) for the plain step, half that with the front end, whose own input
+  // loads already delay the state.  Sweep on the 512 x 96 step in steps of
+  // 512 clocks: plain 1.199 ms without, 1.129 / 1.057 / 1.071 / 1.121 ms at
+  // 6,144 / 8,192 / 10,240 / 12,288 clocks; with the front end 1.086 ms
+  // without, 1.048 / 1.061 ms at 4,096 / 8,192 clocks.
+  if (p.stagger) __builtin_amdgcn_s_sleep(FRONT ? 64 : 127);
 
   // the state, before anything waits on it
   f32x4 s[kRPT];
