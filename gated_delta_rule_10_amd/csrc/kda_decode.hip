@@ -81,7 +81,7 @@ struct LoopParams {
   const float *A_log, *dt_bias;
   float gate_scale;        // lower_bound log2(e)
   int32_t beta_logits;
-  int32_t stagger;         // sleep before the state loads (large grids, see the launch)
+  int32_t stagger;         // sleep before the state loads: 0 none, 1 long, 2 short (launch)
 };
 
 // FRONT: the short-convolution front end, the L2 norms and the output norm; without
@@ -122,21 +122,40 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
   };
   // (every thread loads both values, so no branch -- and no wait at its join --
   // comes before the state loads; t / 128 = 3 reads v, unused)
-  IO x_first = IO(0.f);
-  float g_first = 0.f;
+  IO x_cur = IO(0.f);
+  float g_cur = 0.f, b_cur = 0.f;
   if (any) {
-    const int64_t tok0 = ((int64_t)b * first.T * p.H + h) * kD;  // (b, 0, h)
-    x_first = input_ptr(first)[tok0 + cc];
-    g_first = first.g[tok0 + cc];
+    const int64_t row0 = (int64_t)b * first.T * p.H + h;  // (b, 0, h)
+    x_cur = input_ptr(first)[row0 * kD + cc];
+    g_cur = first.g[row0 * kD + cc];
+    b_cur = first.beta[row0];
   }
 
-  // On large grids each workgroup idles before its state loads: ~3.4 us (127 x 64
-  // clocks) for the plain step, half that with the front end, whose own input
-  // loads already delay the state.  Sweep on the 512 x 96 step in steps of
-  // 512 clocks: plain 1.199 ms without, 1.129 / 1.057 / 1.071 / 1.121 ms at
-  // 6,144 / 8,192 / 10,240 / 12,288 clocks; with the front end 1.086 ms
-  // without, 1.048 / 1.061 ms at 4,096 / 8,192 clocks.
-  if (p.stagger) __builtin_amdgcn_s_sleep(FRONT ? 64 : 127);
+  // conv window of this thread's (input, channel): the three previous raw inputs,
+  // also loaded before the state (the first token's front end waits only for them)
+  IO *cache = nullptr;
+  const int64_t tap = (int64_t)p.H * kD;  // elements between a cache's taps
+  IO w0 = IO(0.f), w1 = IO(0.f), w2 = IO(0.f);
+  f32x4 wt = {0.f, 0.f, 0.f, 0.f};
+  if (FRONT && conv_thread) {
+    cache = reinterpret_cast<IO *>(p.conv_cache) + ((int64_t)slot * 3 + ci) * (kW - 1) * tap +
+            (int64_t)h * kD + cc;
+    wt = *reinterpret_cast<const f32x4 *>(p.conv_w + (((int64_t)ci * p.H + h) * kD + cc) * kW);
+    w0 = cache[0];
+    w1 = cache[tap];
+    w2 = cache[2 * tap];
+  }
+  // the output norm's weight of channel t (the two waves that write o)
+  float nw = 1.f;
+  if (FRONT && t < kD && p.norm_w) nw = p.norm_w[t];
+  // On large grids each workgroup idles before its state loads (the small loads
+  // above are issued first): ~3.4 us (127 x 64 clocks) when the call runs one
+  // token per row, half that for longer windows.  Sweep on the 512 x 96 step in
+  // steps of 512 clocks, 4,096 .. 12,288: plain step 1.177 / 1.110 / 0.995 /
+  // 1.010 / 1.052 ms, with the front end 1.086 / 1.032 / 1.016 / 1.054 / 1.112
+  // ms; verification of 4 + 4 tokens 2.17 ms at 4,096 clocks, 2.31 at 8,128.
+  if (p.stagger == 1) __builtin_amdgcn_s_sleep(127);
+  if (p.stagger == 2) __builtin_amdgcn_s_sleep(64);
 
   // the state, before anything waits on it
   f32x4 s[kRPT];
@@ -151,19 +170,6 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
   __shared__ float sss[2];             // output norm: sums of squares of two waves
   __shared__ float su[kD];
 
-  // conv window of this thread's (input, channel): the three previous raw inputs
-  IO *cache = nullptr;
-  const int64_t tap = (int64_t)p.H * kD;  // elements between a cache's taps
-  IO w0 = IO(0.f), w1 = IO(0.f), w2 = IO(0.f);
-  f32x4 wt = {0.f, 0.f, 0.f, 0.f};
-  if (FRONT && conv_thread) {
-    cache = reinterpret_cast<IO *>(p.conv_cache) + ((int64_t)slot * 3 + ci) * (kW - 1) * tap +
-            (int64_t)h * kD + cc;
-    wt = *reinterpret_cast<const f32x4 *>(p.conv_w + (((int64_t)ci * p.H + h) * kD + cc) * kW);
-    w0 = cache[0];
-    w1 = cache[tap];
-    w2 = cache[2 * tap];
-  }
   float gate_a = 0.f, gate_dt = 0.f;
   if constexpr (GATE) {
     if (!conv_thread) {
@@ -172,15 +178,37 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
     }
   }
 
-  // pre: the token is the call's first, whose input was loaded above
-  auto token = [&](const Tokens &tk, int j, bool pre) {
+  // Inputs of the call's token k (phase a's tokens, then phase b's), clamped to
+  // the last one: issued one token ahead, so no token waits on its own loads.
+  // (the phase's pointers are picked with the token-uniform condition first and
+  // only then per lane: a per-lane pick through a reference into the arguments
+  // would load the pointer itself from memory before every prefetch)
+  auto load_inputs = [&](int k, IO &x, float &g, float &bt) {
+    const int kk = k < na + nb ? k : na + nb - 1;
+    const bool in_a = kk < na;
+    const int j = in_a ? kk : kk - na;
+    const int64_t row = ((int64_t)b * (in_a ? p.a.T : p.b.T) + j) * p.H + h;
+    const IO *qp = reinterpret_cast<const IO *>(in_a ? p.a.q : p.b.q);
+    const IO *kp = reinterpret_cast<const IO *>(in_a ? p.a.k : p.b.k);
+    const IO *vp = reinterpret_cast<const IO *>(in_a ? p.a.v : p.b.v);
+    const float *gp = in_a ? p.a.g : p.b.g;
+    const float *bp = in_a ? p.a.beta : p.b.beta;
+    const IO *src = ci == 0 ? qp : ci == 1 ? kp : vp;
+    x = src[row * kD + cc];
+    g = gp[row * kD + cc];
+    bt = bp[row];
+  };
+  // token j of phase tk, the call's token k; its inputs are in x_cur, g_cur, b_cur
+  auto token = [&](const Tokens &tk, int j, int k) {
     const int64_t row = ((int64_t)b * tk.T + j) * p.H + h;  // (b, j, h)
     const int64_t tok = row * kD;
+    IO x_nxt;
+    float g_nxt, b_nxt;
     // 1. front end
     if (conv_thread && !FRONT) {
-      sx[ci][cc] = to_f32(pre ? x_first : input_ptr(tk)[tok + cc]);
+      sx[ci][cc] = to_f32(x_cur);
     } else if (conv_thread) {
-      const IO xn = pre ? x_first : input_ptr(tk)[tok + cc];
+      const IO xn = x_cur;
       float y = wt[0] * to_f32(w0);
       y = fmaf(wt[1], to_f32(w1), y);
       y = fmaf(wt[2], to_f32(w2), y);
@@ -191,12 +219,13 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
       sx[ci][cc] = y * sigmoid_fast(y);
     } else {
       const int c = t - 3 * kD;
-      const float x = pre ? g_first : tk.g[tok + c];
+      const float x = g_cur;
       if constexpr (GATE)
         sa[c] = fast_exp2(gate_log2(x, gate_a, gate_dt, p.gate_scale));
       else
         sa[c] = fast_exp2(x * kLog2e);
     }
+    load_inputs(k + 1, x_nxt, g_nxt, b_nxt);
     block_sync();
     // 2. L2 norms of q and k, and q.k of the normalised vectors
     if (t < 64) {
@@ -242,7 +271,7 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
         r += rr[j2 * kD + t];
         y += yy[j2 * kD + t];
       }
-      const float bt = p.beta_logits ? sigmoid_fast(tk.beta[row]) : tk.beta[row];
+      const float bt = p.beta_logits ? sigmoid_fast(b_cur) : b_cur;
       const float u = bt * (sx[2][t] - ik * r);
       su[t] = u;
       o = p.scale * (iq * y + sc[2] * u);
@@ -258,15 +287,18 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
     if (t < kD && tk.o) {
       if (FRONT && p.out_norm) {
         const float inv = 1.f / sqrtf((sss[0] + sss[1]) * (1.f / kD) + p.norm_eps);
-        o *= inv * (p.norm_w ? p.norm_w[t] : 1.f);
+        o *= inv * nw;
       }
       reinterpret_cast<IO *>(tk.o)[tok + t] = from_f32<IO>(o);
     }
+    x_cur = x_nxt;  // many barriers after the loads were issued
+    g_cur = g_nxt;
+    b_cur = b_nxt;
   };
 
   for (int j = 0; j < na; ++j) {
     if (j > 0) block_sync();  // the previous token's reads of sx, su, sc are done
-    token(p.a, j, j == 0);
+    token(p.a, j, j);
   }
   if (na > 0) {  // write back the committed state and conv window
 #pragma unroll
@@ -280,7 +312,7 @@ __global__ __launch_bounds__(kNT) void decode_loop_kernel(LoopParams p) {
   }
   for (int j = 0; j < nb; ++j) {
     if (na > 0 || j > 0) block_sync();
-    token(p.b, j, na == 0 && j == 0);
+    token(p.b, j, na + j);
   }
 }
 
@@ -322,7 +354,8 @@ hipError_t launch(const kda_fused_step_args &a, LoopParams lp, hipStream_t strea
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 0;
-  lp.stagger = cus > 0 && blocks >= 32u * (unsigned)cus ? 1 : 0;
+  const bool one_token = (int64_t)lp.a.T + lp.b.T <= 1;
+  lp.stagger = cus > 0 && blocks >= 32u * (unsigned)cus ? (one_token ? 1 : 2) : 0;
   const bool gate = a.gate.mode == KDA_GATE_LOWER_BOUND;
   if (a.io_dtype == KDA_BF16)
     return gate ? launch_typed<bf16, true, FRONT>(lp, blocks, stream)
