@@ -201,6 +201,8 @@ def library(path: str = LIB_PATH):
     lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(ChunkBwdArgs), ctypes.c_void_p]
     lib.kda_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(ChunkBwdArgs),
                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_bwd_min_workspace_size.argtypes = [ctypes.POINTER(ChunkBwdArgs),
+                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_fused_decode_step.argtypes = [ctypes.POINTER(FusedStepArgs), ctypes.c_void_p]
     lib.kda_spec_verify_step.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     lib.kda_conv_cache_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
@@ -394,8 +396,11 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     return o, final_state
 
 
-def chunk_bwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None) -> int:
-    """Workspace bytes for the backward of a prefill of ``q``'s shape (host only)."""
+def chunk_bwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None, minimum=False) -> int:
+    """Workspace bytes for the backward of a prefill of ``q``'s shape (host only):
+    the whole pack in one pass, or with ``minimum`` the smallest workspace the
+    backward accepts (the largest single sequence's; smaller workspaces are used
+    for groups of sequences in turn)."""
     lib = library()
     T, H, D = q.shape
     a = ChunkBwdArgs()
@@ -412,15 +417,15 @@ def chunk_bwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None) -> int:
     a.io_dtype = _dtype_code(q.dtype)
     a.scale = 1.0
     out = ctypes.c_size_t(0)
-    _check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(out)),
-           "kda_chunk_bwd_workspace_size")
+    query = lib.kda_chunk_bwd_min_workspace_size if minimum else lib.kda_chunk_bwd_workspace_size
+    _check(query(ctypes.byref(a), ctypes.byref(out)), "kda_chunk_bwd_workspace_size")
     del host
     return int(out.value)
 
 
 def chunk_bwd(q, k, v, g, beta, dO, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
               dfinal_state=None, scale=1.0, num_seqs=None, want_dinitial=True, workspace=None,
-              grads=None):
+              grads=None, max_workspace_bytes=None):
     """Backward of chunk_fwd (log-decay g, beta as given): gradients of
     L = <dO, o> + <dfinal_state, S_T>.
 
@@ -428,6 +433,10 @@ def chunk_bwd(q, k, v, g, beta, dO, cu_seqlens=None, cu_seqlens_host=None, initi
     [N, H, 128, 128] fp32 or None.  Returns a dict of fp32 dq, dk, dv, dg
     [T, H, 128], dbeta [T, H] and dinitial_state [N, H, 128, 128] (None unless
     want_dinitial).  ``grads`` may pass preallocated outputs with those keys.
+    ``workspace`` (uint8) is used as given: at least the minimum size, and below
+    the whole pack's the sequences run in groups.  Without one, a workspace for
+    the whole pack is allocated, or of ``max_workspace_bytes`` if that is less
+    (but not below the minimum).
     """
     lib = library()
     _need(q, "q", ndim=3)
@@ -491,11 +500,16 @@ def chunk_bwd(q, k, v, g, beta, dO, cu_seqlens=None, cu_seqlens_host=None, initi
     a.dq, a.dk, a.dv, a.dg, a.dbeta = (out[n].data_ptr() for n in ("dq", "dk", "dv", "dg",
                                                                      "dbeta"))
     a.dinitial_state = None if out["dinitial_state"] is None else out["dinitial_state"].data_ptr()
-    ws_bytes = ctypes.c_size_t(0)
-    _check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(ws_bytes)),
-           "kda_chunk_bwd_workspace_size")
-    if workspace is None or workspace.numel() < ws_bytes.value:
-        workspace = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(full)),
+               "kda_chunk_bwd_workspace_size")
+        _check(lib.kda_chunk_bwd_min_workspace_size(ctypes.byref(a), ctypes.byref(least)),
+               "kda_chunk_bwd_min_workspace_size")
+        size = full.value
+        if max_workspace_bytes is not None:
+            size = max(least.value, min(size, int(max_workspace_bytes)))
+        workspace = torch.empty(max(size, 1), dtype=torch.uint8, device=q.device)
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _check(lib.kda_chunk_bwd(ctypes.byref(a), _stream(q)), "kda_chunk_bwd")
     del host

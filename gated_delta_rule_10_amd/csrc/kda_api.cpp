@@ -210,12 +210,21 @@ kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *a, size_t *byt
   return KDA_SUCCESS;
 }
 
+kda_status kda_chunk_bwd_min_workspace_size(const kda_chunk_bwd_args *a, size_t *bytes) {
+  if (!bytes) return KDA_ERROR_INVALID_VALUE;
+  int64_t T = 0, ms = 0;
+  const kda_status st = check_bwd_args(a, &T, &ms, false);
+  if (st != KDA_SUCCESS) return st;
+  *bytes = kda::chunk_bwd_min_workspace_bytes(*a);
+  return KDA_SUCCESS;
+}
+
 kda_status kda_chunk_bwd(const kda_chunk_bwd_args *a, void *stream) {
   int64_t T = 0, ms = 0;
   const kda_status st = check_bwd_args(a, &T, &ms, true);
   if (st != KDA_SUCCESS) return st;
-  const size_t need = kda::chunk_bwd_workspace_bytes(T, a->num_seqs, a->num_heads);
-  if (!a->workspace || a->workspace_bytes < need) return KDA_ERROR_WORKSPACE;
+  const size_t need = kda::chunk_bwd_min_workspace_bytes(*a);
+  if (T > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERROR_WORKSPACE;
   if (((uintptr_t)a->workspace & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   return launch_status(kda::launch_chunk_bwd(*a, T, ms, (hipStream_t)stream));
 }

@@ -77,8 +77,10 @@ struct BwdParams {
   const float *g, *beta, *s0, *dsf;
   float *dq, *dk, *dv, *dg, *dbeta, *ds0;
   const int32_t *cu;
-  int64_t total_tokens, chains;
-  int32_t H, seq_len;
+  int64_t total_tokens;
+  int64_t chains;   // (sequence, head) chains of this launch: sequences seq0 .. seq0 + chains / H
+  int64_t slot0;    // sub-chunk slot of the launch's first sub-chunk (workspace origin)
+  int32_t H, seq_len, seq0;
   float scale;
   float *ckpt;     // [slots][H][128][128] states at sub-chunk starts
   float *part;     // [slots][H][kNB][kPart] partial sums of the serial pass
@@ -91,10 +93,11 @@ constexpr int kRecAb = 0, kRecP = 256, kRecX = 512, kRec = 768;
 constexpr int kPdA = 0, kPdP = 256, kPdB = 512, kPdKt = 528, kPdQt = kPdKt + 2048,
               kPdKb = kPdQt + 2048, kPdGam = kPdKb + 2048, kPart = kPdGam + 128;
 
-// Sub-chunk slot of sub-chunk j of a sequence starting at token bos: distinct
-// for all (sequence n, j), below T_total / 16 + N + 1.
-__device__ __forceinline__ int64_t slot_of(int64_t bos, int n, int j) {
-  return bos / kSC + n + j;
+// Sub-chunk slot of sub-chunk j of sequence n starting at token bos, relative
+// to the launch's first: distinct for all (n, j) of the launch, below the slot
+// count its workspace was laid out for (slot_count on the host).
+__device__ __forceinline__ int64_t slot_of(const BwdParams &p, int64_t bos, int n, int j) {
+  return bos / kSC + n + j - p.slot0;
 }
 
 __device__ __forceinline__ void seq_range(const BwdParams &p, int n, int64_t &bos, int64_t &len) {
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kPT) void bwd_prep_kernel(BwdParams p, int stride) 
   __shared__ __attribute__((aligned(16))) float kx[kSC * kLT], qx[kSC * kLT], G[kSC * kLT];
   __shared__ __attribute__((aligned(16))) float Ke[kSC * kLT], Kd[kSC * kLT], Qe[kSC * kLT];
   __shared__ float A[kSC * kLM], bt[kSC], tot[kD], wspan[kPT / 64];
-  const int chain = blockIdx.x / stride, j0 = blockIdx.x % stride;
+  const int chain = p.seq0 * p.H + blockIdx.x / stride, j0 = blockIdx.x % stride;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kPT) void bwd_prep_kernel(BwdParams p, int stride) 
       if ((t & 63) == 0) wspan[t >> 6] = span;
     }
     block_sync();
-    float *rec = p.rec + (slot_of(bos, n, j) * p.H + h) * (int64_t)kRec;
+    float *rec = p.rec + (slot_of(p, bos, n, j) * p.H + h) * (int64_t)kRec;
     float maxspan = 0.f;
 #pragma unroll
     for (int u = 0; u < kPT / 64; ++u) maxspan = fmaxf(maxspan, wspan[u]);
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
   int blk;
   xcd_unit(blockIdx.x, kNB, unit, blk);
   if (unit >= p.chains) return;
-  const int chain = (int)unit;
+  const int chain = p.seq0 * p.H + (int)unit;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
   auto fetch_small = [&](int j) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, sub_len(len, j) - 1) * p.H) * 4u);
-    xr = at<float>(p.rec + (slot_of(bos, n, j) * p.H + h) * (int64_t)kRec + kRecX,
+    xr = at<float>(p.rec + (slot_of(p, bos, n, j) * p.H + h) * (int64_t)kRec + kRecX,
                    (uint32_t)(t & 255) * 4u);
   };
   auto fetch_v = [&](int j) {
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.U[(4 * g4 + i) * kLB + 16 * w + l16] = u[i];
     } else {  // checkpoint of the state at this sub-chunk's start (16 lanes per row)
-      float *ck = p.ckpt + (slot_of(bos, n, j) * p.H + h) * (int64_t)(kD * kD) + blk * kNC;
+      float *ck = p.ckpt + (slot_of(p, bos, n, j) * p.H + h) * (int64_t)(kD * kD) + blk * kNC;
       const int tw = t - 256, col = 4 * (tw & 15);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
   int blk;
   xcd_unit(blockIdx.x, kNB, unit, blk);
   if (unit >= p.chains) return;
-  const int chain = (int)unit;
+  const int chain = p.seq0 * p.H + (int)unit;
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
   auto fetch_state = [&](int j) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
-    const int64_t slot = slot_of(bos, n, j);
+    const int64_t slot = slot_of(p, bos, n, j);
     braw = at<float>(p.beta + t0 * p.H + h, (uint32_t)(min(t & 15, L - 1) * p.H) * 4u);
     const float *ck = p.ckpt + (slot * p.H + h) * (int64_t)(kD * kD) + blk * kNC;
 #pragma unroll
@@ -634,7 +637,7 @@ __global__ __launch_bounds__(kBT) void bwd_serial_kernel(BwdParams p) {
   for (int j = nsub - 1; j >= 0; --j) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
-    const int64_t slot = slot_of(bos, n, j);
+    const int64_t slot = slot_of(p, bos, n, j);
     const int b = (nsub - 1 - j) & 1;  // LDS buffer of this sub-chunk's operands
     const int jn = max(j - 1, 0);      // next sub-chunk (j = 0: sub-chunk 0 again, unused)
     const int Ln = sub_len(len, jn);
@@ -833,7 +836,7 @@ __global__ __launch_bounds__(kFT) void bwd_finalize_kernel(BwdParams p, int stri
   int half;
   xcd_unit(blockIdx.x, 2, unit, half);
   if (unit >= p.chains * stride) return;
-  const int chain = (int)(unit / stride), j0 = (int)(unit % stride);
+  const int chain = p.seq0 * p.H + (int)(unit / stride), j0 = (int)(unit % stride);
   const int n = chain / p.H, h = chain % p.H;
   int64_t bos, len;
   seq_range(p, n, bos, len);
@@ -846,7 +849,7 @@ __global__ __launch_bounds__(kFT) void bwd_finalize_kernel(BwdParams p, int stri
   for (int j = j0; j < nsub; j += stride) {
     const int64_t t0 = bos + (int64_t)j * kSC;
     const int L = sub_len(len, j);
-    const int64_t slot = slot_of(bos, n, j);
+    const int64_t slot = slot_of(p, bos, n, j);
     const float *pa = p.part + (slot * p.H + h) * kNB * (int64_t)kPart;
     // loads (unconditional: rows past L read row L - 1 and are masked at use)
     IO kv[4], qv[4];
@@ -1051,6 +1054,22 @@ WorkspaceLayout layout(int64_t total_tokens, int32_t num_seqs, int32_t heads) {
   return l;
 }
 
+// Token range of sequence n (host side: cu_seqlens_host, or the fixed length).
+struct Span {
+  int64_t bos, len;
+};
+Span span_of(const kda_chunk_bwd_args &a, int32_t n) {
+  if (a.cu_seqlens) return {a.cu_seqlens_host[n], (int64_t)a.cu_seqlens_host[n + 1] - a.cu_seqlens_host[n]};
+  return {(int64_t)n * a.seq_len, a.seq_len};
+}
+// Workspace of sequences n0 .. n1 - 1 run in one launch: with bos0 their first
+// token and T their tokens, every relative slot (bos / 16 - bos0 / 16) + (n - n0)
+// + j stays below T / 16 + (n1 - n0) + 1.
+size_t group_bytes(const kda_chunk_bwd_args &a, int32_t n0, int32_t n1) {
+  const Span f = span_of(a, n0), l = span_of(a, n1 - 1);
+  return layout(l.bos + l.len - f.bos, n1 - n0, a.num_heads).total;
+}
+
 }  // namespace
 
 // Workspace: sub-chunk slots T_total / 16 + N + 1, each holding H states
@@ -1059,8 +1078,22 @@ size_t chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t
   return layout(total_tokens, num_seqs, heads).total;
 }
 
+// The smallest workspace the backward runs in: the largest single sequence's.
+size_t chunk_bwd_min_workspace_bytes(const kda_chunk_bwd_args &a) {
+  size_t m = 0;
+  for (int32_t n = 0; n < a.num_seqs; ++n) {
+    const size_t b = group_bytes(a, n, n + 1);
+    if (b > m) m = b;
+  }
+  return m;
+}
+
+// Sequences are independent, so a workspace smaller than the whole pack's is
+// used for consecutive groups of sequences, each as large as fits, one launch
+// sequence (prep, states, serial, finalize) per group.
 hipError_t launch_chunk_bwd(const kda_chunk_bwd_args &a, int64_t total_tokens, int64_t max_sub,
                             hipStream_t stream) {
+  (void)max_sub;
   BwdParams p;
   p.q = a.q;
   p.k = a.k;
@@ -1081,17 +1114,32 @@ hipError_t launch_chunk_bwd(const kda_chunk_bwd_args &a, int64_t total_tokens, i
   p.H = a.num_heads;
   p.seq_len = a.seq_len;
   p.scale = a.scale;
-  const WorkspaceLayout l = layout(total_tokens, a.num_seqs, a.num_heads);
   char *ws = reinterpret_cast<char *>(a.workspace);
-  p.ckpt = reinterpret_cast<float *>(ws + l.ck);
-  p.part = reinterpret_cast<float *>(ws + l.part);
-  p.rec = reinterpret_cast<float *>(ws + l.rec);
-  const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
-  p.chains = chains;
-  const int stride = (int)(max_sub < 1 ? 1 : (max_sub > 64 ? 64 : max_sub));
-  if (chains == 0) return hipSuccess;
-  return a.io_dtype == KDA_BF16 ? launch_typed<bf16>(p, chains, stride, stream)
-                                : launch_typed<float>(p, chains, stride, stream);
+  for (int32_t n0 = 0; n0 < a.num_seqs;) {
+    int32_t n1 = n0 + 1;
+    while (n1 < a.num_seqs && group_bytes(a, n0, n1 + 1) <= a.workspace_bytes) ++n1;
+    const Span f = span_of(a, n0);
+    const WorkspaceLayout l = layout(span_of(a, n1 - 1).bos + span_of(a, n1 - 1).len - f.bos,
+                                     n1 - n0, a.num_heads);
+    p.ckpt = reinterpret_cast<float *>(ws + l.ck);
+    p.part = reinterpret_cast<float *>(ws + l.part);
+    p.rec = reinterpret_cast<float *>(ws + l.rec);
+    p.seq0 = n0;
+    p.slot0 = f.bos / kSC + n0;
+    p.chains = (int64_t)(n1 - n0) * a.num_heads;
+    int64_t ms = 1;
+    for (int32_t n = n0; n < n1; ++n) {
+      const int64_t sub = (span_of(a, n).len + kSC - 1) / kSC;
+      if (sub > ms) ms = sub;
+    }
+    const int stride = (int)(ms > 64 ? 64 : ms);
+    const hipError_t e = a.io_dtype == KDA_BF16
+                             ? launch_typed<bf16>(p, p.chains, stride, stream)
+                             : launch_typed<float>(p, p.chains, stride, stream);
+    if (e != hipSuccess) return e;
+    n0 = n1;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -44,6 +44,7 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
 
 // Chunked backward: workspace size and the three launches.
 size_t chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t heads);
+size_t chunk_bwd_min_workspace_bytes(const kda_chunk_bwd_args &a);
 hipError_t launch_chunk_bwd(const kda_chunk_bwd_args &a, int64_t total_tokens, int64_t max_sub,
                             hipStream_t stream);
 

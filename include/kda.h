@@ -212,15 +212,22 @@ typedef struct kda_chunk_bwd_args {
   size_t workspace_bytes;
 } kda_chunk_bwd_args;
 
-/* Bytes of workspace kda_chunk_bwd needs: (T_total / 16 + N + 1) x H x (64 KiB
- * of state + 27,200 B of partial sums + 3,072 B of per-sub-chunk matrices),
- * each region 256-B aligned.  Host only. */
+/* Bytes of workspace for the whole pack in one pass: (T_total / 16 + N + 1) x
+ * H x (64 KiB of state + 27,200 B of partial sums + 3,072 B of per-sub-chunk
+ * matrices), each region 256-B aligned.  Host only. */
 kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *args, size_t *bytes);
+
+/* The smallest workspace kda_chunk_bwd accepts: the largest single sequence's
+ * requirement (its length / 16 + 2 slots).  A workspace between this and
+ * kda_chunk_bwd_workspace_size is used for consecutive groups of sequences,
+ * each group as large as fits, one after another on the stream; the results
+ * are the same bits.  Host only. */
+kda_status kda_chunk_bwd_min_workspace_size(const kda_chunk_bwd_args *args, size_t *bytes);
 
 /* Enqueue the backward on `stream`.  Errors as kda_chunk_fwd (sizes, offsets,
  * alignment: q, k, v, dO, g and the gradients 16 bytes, beta and dbeta 4; the
  * outputs may not alias the inputs), KDA_ERROR_WORKSPACE when the workspace is
- * smaller than queried. */
+ * smaller than kda_chunk_bwd_min_workspace_size. */
 kda_status kda_chunk_bwd(const kda_chunk_bwd_args *args, void *stream);
 
 /* ------------------------------------------------------------------------

@@ -8,6 +8,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import gated_delta_rule_10_amd as kda
@@ -316,3 +317,30 @@ def test_chunk_bwd_rejects_invalid_arguments(lib):
     assert f(args(dk=(1 << 20) + 4)) == 1          # gradients need 16 bytes
     assert f(args(dv=1 << 20)) == 1                 # output aliases q
     assert f(args()) == 3                           # no workspace
+
+
+def test_chunk_bwd_minimum_workspace_is_the_largest_sequence(lib):
+    """The backward runs in any workspace from the largest single sequence's
+    requirement up (groups of sequences in turn); below it KDA_ERROR_WORKSPACE
+    comes back before anything is launched."""
+    lens = [100, 37, 5000, 0, 64]
+    cu = (ctypes.c_int32 * (len(lens) + 1))(*[int(x) for x in np.concatenate([[0], np.cumsum(lens)])])
+    a = kda.ChunkBwdArgs()
+    a.num_seqs, a.num_heads, a.head_dim = len(lens), 3, 128
+    a.cu_seqlens_host, a.cu_seqlens = cu, 16
+    a.io_dtype, a.scale = kda.KDA_BF16, 1.0
+    full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(full)) == 0
+    assert lib.kda_chunk_bwd_min_workspace_size(ctypes.byref(a), ctypes.byref(least)) == 0
+    assert 0 < least.value < full.value
+    one = kda.ChunkBwdArgs()  # the 5000-token sequence alone
+    one.num_seqs, one.seq_len, one.num_heads, one.head_dim = 1, 5000, 3, 128
+    one.io_dtype, one.scale = kda.KDA_BF16, 1.0
+    alone = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(one), ctypes.byref(alone)) == 0
+    assert least.value == alone.value
+    base = 1 << 20
+    a.q, a.k, a.v, a.dO, a.g, a.beta = (base + 4096 * i for i in range(6))
+    a.dq, a.dk, a.dv, a.dg, a.dbeta = (base + 4096 * (8 + i) for i in range(5))
+    a.workspace, a.workspace_bytes = 1 << 30, least.value - 1
+    assert lib.kda_chunk_bwd(ctypes.byref(a), None) == 3

@@ -162,6 +162,44 @@ def test_backward_rejects_missized_outputs(kda):
                       workspace=torch.empty(16, device="cuda"))
 
 
+def test_backward_small_workspace_runs_sequence_groups_bitwise(kda):
+    """A workspace below the whole pack's is used for groups of sequences in
+    turn: the same bits as one pass, down to the minimum (the largest single
+    sequence's requirement); fixed batches group the same way."""
+    announce("chunk bwd sequence groups")
+    lens = (40, 200, 17, 0, 96, 150, 33)
+    cfg = ki.PrefillConfig("t", lens, 2, "bf16", init_std=0.2, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=86)
+    gen = torch.Generator(device="cuda").manual_seed(87)
+    T = inp["q"].shape[0]
+    dO = torch.randn((T, 2, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    dSf = torch.randn((len(lens), 2, 128, 128), generator=gen, device="cuda") * 0.1
+    kw = dict(cu_seqlens=inp["cu_seqlens"], cu_seqlens_host=inp["cu_seqlens_host"],
+              initial_state=inp["initial_state"], dfinal_state=dSf, scale=0.9,
+              num_seqs=len(lens))
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dO)
+    whole = kda.chunk_bwd(*args, **kw)
+    full = kda.chunk_bwd_workspace_size(inp["q"], cu_seqlens_host=inp["cu_seqlens_host"])
+    least = kda.chunk_bwd_workspace_size(inp["q"], cu_seqlens_host=inp["cu_seqlens_host"],
+                                         minimum=True)
+    assert least < full
+    for size in (least, (least + full) // 2):
+        ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+        got = kda.chunk_bwd(*args, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        for n in NAMES + ("dinitial_state",):
+            assert torch.equal(got[n], whole[n]), (size, n)
+    fb = ki.PrefillConfig("t", (80,) * 5, 2, "bf16")
+    x = ki.make_prefill(fb, device="cuda", seed=88)
+    dO2 = torch.randn(x["q"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    a2 = (x["q"], x["k"], x["v"], x["g"], x["beta"], dO2)
+    one = kda.chunk_bwd(*a2, num_seqs=5)
+    small = kda.chunk_bwd(*a2, num_seqs=5, max_workspace_bytes=1)  # one sequence per group
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(small[n], one[n]), n
+
+
 def test_backward_fixed_batch_equals_varlen(kda):
     announce("chunk bwd fixed batch vs varlen")
     cfg = ki.PrefillConfig("t", (96, 96), 3, "bf16", init_std=0.1)
