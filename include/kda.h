@@ -66,14 +66,14 @@ extern "C" {
 typedef enum kda_status {
   KDA_SUCCESS = 0,
   KDA_ERROR_INVALID_VALUE = 1, /* null pointer, bad size, bad alignment, bad offsets */
-  KDA_ERROR_UNSUPPORTED = 2,   /* a valid request this build does not implement     */
+  KDA_ERROR_UNSUPPORTED = 2,   /* a valid request the library does not implement    */
   KDA_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required        */
   KDA_ERROR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch          */
 } kda_status;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
-/* Head dimension (d_k = d_v) and chunk length this build implements. */
+/* Head dimension (d_k = d_v) and chunk length the library implements. */
 #define KDA_HEAD_DIM 128
 #define KDA_CHUNK 64
 
