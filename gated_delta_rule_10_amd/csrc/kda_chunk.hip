@@ -43,6 +43,8 @@
 //  * fp32 I/O uses the same kernel with fp32 operands (V_MFMA_F32_16X16X4_F32),
 //    the intra-chunk products in two channel halves, and 64 value columns per
 //    workgroup so the operand buffers fit in the 160 KiB of LDS.
+#include <queue>
+#include <vector>
 #include <type_traits>
 
 #include "kda_chunk_common.h"
@@ -757,6 +759,13 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkParams p) {
   }
 }
 
+// Clears the hand-over flags of the balanced schedule before its launch (a
+// kernel rather than a memset, so the sequence can be captured in a graph).
+__global__ void clear_flags_kernel(int32_t *flag, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) flag[i] = 0;
+}
+
 template <class OpT, int DV>
 hipError_t launch_typed(const ChunkParams &p, int64_t items, hipStream_t stream) {
   if (p.gate)
@@ -769,6 +778,57 @@ hipError_t launch_typed(const ChunkParams &p, int64_t items, hipStream_t stream)
 }
 
 }  // namespace
+
+// Item lengths (chunks) of run w of the balanced schedule, in order; the host
+// mirror of run_shape / run_item.
+static int run_lengths(int64_t C, int64_t n, int64_t L, int64_t w, int64_t *len) {
+  const int64_t total = C * n, s = w * L, e = s + L < total ? s + L : total;
+  if (e <= s) return 0;
+  const int64_t c_lo = s / n, c_hi = (e - 1) / n, tail0 = s - c_lo * n, head1 = e - c_hi * n;
+  int m = 0;
+  if (head1 < n) len[m++] = head1;
+  for (int64_t c = c_lo + (tail0 > 0); c <= c_hi - (head1 < n); ++c) len[m++] = n;
+  if (tail0 > 0) len[m++] = n - tail0;
+  return m;
+}
+
+// Whether the balanced schedule beats whole chains: the finishing time of the
+// items dispatched round by round, workgroup i to accelerator complex i mod 8
+// and there to the first free unit, each item costing its chunks plus one for
+// the pipeline's start, against ceil(C / U) n for whole chains.
+static bool balanced_schedule_pays(int64_t C, int64_t n, int U, ChunkPlan *pl) {
+  const int64_t total = C * n, L = (total + U - 1) / U, W = (total + L - 1) / L;
+  const int64_t K = L / n + 2;  // items per run at most
+  if (W > 4096 || K > 64 || total >= ((int64_t)1 << 30)) return false;
+  std::vector<int64_t> len((size_t)(W * K), -1);
+  int64_t rounds = 0;
+  for (int64_t w = 0; w < W; ++w) {
+    int64_t l[66];
+    const int m = run_lengths(C, n, L, w, l);
+    for (int k = 0; k < m; ++k) len[(size_t)(k * W + w)] = l[k];
+    if (m > rounds) rounds = m;
+  }
+  const int xcd = U % 8 == 0 ? 8 : 1, per = U / xcd;
+  int64_t finish = 0;
+  for (int x = 0; x < xcd; ++x) {
+    std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+    for (int u = 0; u < per; ++u) free_at.push(0);
+    for (int64_t i = x; i < rounds * W; i += xcd) {
+      const int64_t c = len[(size_t)i];
+      if (c < 0) continue;
+      const int64_t t = free_at.top() + c + 1;
+      free_at.pop();
+      free_at.push(t);
+      if (t > finish) finish = t;
+    }
+  }
+  const int64_t whole = ((C + U - 1) / U) * (n + 1);
+  if (10 * finish > 9 * whole) return false;
+  pl->ho_len = L;
+  pl->ho_workers = W;
+  pl->ho_rounds = rounds;
+  return true;
+}
 
 kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
   ChunkPlan pl;
@@ -800,11 +860,14 @@ kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
   int64_t P = a.segments > 1 ? a.segments : 1;
   pl.seg_front = false;
   const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
-  if (a.segments == 0 && a.io_dtype == KDA_BF16 && pl.max_chunks >= 8) {
-    int cus = 0, dev = 0;
+  int cus = 0;
+  if (a.segments == 0 && a.io_dtype == KDA_BF16) {
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 0;
+  }
+  if (pl.max_chunks >= 8) {
     if (cus > 0 && chains <= cus) {
       P = 3;
       pl.seg_front = true;
@@ -823,6 +886,19 @@ kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
     pl.seg_state_off = off;
     pl.seg_state_bytes = (size_t)a.num_seqs * a.num_heads * 3 * pl.segments * kD * kD * 4;
     off += pl.seg_state_bytes;
+  }
+  // Equal-length chains that do not fill whole rounds of the compute units (C
+  // chains of n chunks, U units, C mod U != 0): runs of L = ceil(C n / U)
+  // consecutive chunks of the chains laid end to end, a chain cut between two
+  // runs handing its state over (run_shape).  Where the units, taking the
+  // runs' items round by round as they free up, finish clearly before whole
+  // chains would (1.5 n instead of 2 n for 384 chains on 256 units), the
+  // prefill uses it.
+  if (cus > 0 && pl.segments <= 1 && !pl.varlen && chains > cus && chains % cus != 0 &&
+      pl.max_chunks >= 2 && balanced_schedule_pays(chains, pl.max_chunks, cus, &pl)) {
+    pl.ho_off = off;
+    pl.ho_bytes = (size_t)pl.ho_workers * (kD * kD * 4 + 4);
+    off += (pl.ho_bytes + 255) & ~(size_t)255;
   }
   pl.total_bytes = off;
   *plan = pl;
@@ -871,6 +947,21 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
   p.ws = nullptr;
   p.chain0 = 0;
   p.nchains = (int32_t)chains;
+  p.ho_state = nullptr;
+  p.ho_flag = nullptr;
+  p.ho_len = 0;
+  if (plan.ho_workers > 0) {
+    char *base = (char *)a.workspace + plan.ho_off;
+    p.ho_state = reinterpret_cast<float *>(base);
+    p.ho_flag = reinterpret_cast<int32_t *>(base + (size_t)plan.ho_workers * kD * kD * 4);
+    p.ho_len = plan.ho_len;
+    p.pass = kPassHandoff;
+    hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((plan.ho_workers + 255) / 256)),
+                       dim3(256), 0, stream, p.ho_flag, plan.ho_workers);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return run(plan.ho_workers * plan.ho_rounds);
+  }
   if (plan.segments <= 1) {
     p.pass = 0;
     return run(chains * VS);

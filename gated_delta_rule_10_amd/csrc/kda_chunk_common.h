@@ -41,7 +41,15 @@ struct ChunkParams {
   const float *A_log, *dt_bias;
   float gate_scale;
   int32_t gate, beta_logits;
+  // balanced schedule of equal-length chains (pass kPassHandoff): the chains'
+  // chunks laid end to end are cut into runs of ho_len chunks, one per
+  // workgroup; a chain cut in two hands its state over through ho_state
+  float *ho_state;       // [workgroups][128 x 128] fp32 handed-over states
+  int32_t *ho_flag;      // [workgroups] set to 1 once that state is stored
+  int64_t ho_len;        // chunks per workgroup
 };
+
+constexpr int kPassHandoff = 3;
 
 // Segment items ("Kimi K3 -- Training and Infrastructure Notes", section 4.1):
 // a run evaluates a segment from its incoming state; the two trackers of a
@@ -68,6 +76,8 @@ struct ChunkItem {
   int h, vs;
   const float *s0;
   float *sf;
+  const int32_t *wait;  // flag to see set before s0 is read (null = none)
+  int32_t *signal;      // flag to set once sf is stored (null = none)
   bool write_o, zero_v, skip;
 };
 
@@ -136,6 +146,81 @@ __device__ __forceinline__ ChunkItem decode_item(const ChunkParams &p, int VS) {
   r.len = len;
   r.write_o = mode == kRun;
   r.zero_v = mode == kTrackM;
+  r.wait = nullptr;
+  r.signal = nullptr;
+  return r;
+}
+
+// Balanced schedule of C chains of n chunks each (fixed-length batch, C above
+// the number of compute units).  The chunks of chains 0 .. C-1, laid end to
+// end, are cut into W runs of L = ho_len >= n chunks.  Run w starts with the
+// tail of a chain cut by run w-1 (or at a chain start), holds whole chains,
+// and ends with the head of a chain that run w+1 finishes (or at a chain end);
+// since L >= n a chain is cut at most once.  Items are numbered round by
+// round, blockIdx.x = k W + w for item k of run w, k = 0 first: the head (its
+// state goes to ho_state[w] and ho_flag[w] is set), then the whole chains,
+// then the tail (it waits for ho_flag[w-1]).  A tail waits for a head of a
+// lower-numbered workgroup, dispatched earlier, that never waits itself.
+struct RunShape {
+  int c_lo, c_hi;  // first and last chain touched
+  int tail0;       // first chunk of the tail of chain c_lo (0: no tail)
+  int head1;       // end chunk of the head of chain c_hi (n: no head)
+  int count;       // items of the run
+};
+// 32-bit arithmetic (the host enables the schedule for C n < 2^30 only).
+__device__ __forceinline__ RunShape run_shape(const ChunkParams &p, int n, int w) {
+  const int total = p.nchains * n, L = (int)p.ho_len;
+  const int s = w * L, e = s + L < total ? s + L : total;
+  RunShape r;
+  r.c_lo = s / n;
+  r.c_hi = (e - 1) / n;
+  r.tail0 = s - r.c_lo * n;
+  r.head1 = e - r.c_hi * n;
+  const int whole = (r.c_hi - (r.head1 < n)) - (r.c_lo + (r.tail0 > 0)) + 1;
+  r.count = (r.head1 < n) + (whole > 0 ? whole : 0) + (r.tail0 > 0);
+  if (e <= s) r.count = 0;
+  return r;
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ ChunkItem run_item(const ChunkParams &p) {
+  const int n = (p.seq_len + kC - 1) / kC;
+  const int L = (int)p.ho_len;
+  const int W = (p.nchains * n + L - 1) / L;
+  const int k = uniform((int)blockIdx.x / W);
+  const int w = uniform((int)blockIdx.x - k * W);
+  const RunShape rs = run_shape(p, n, w);
+  ChunkItem r;
+  r.wait = nullptr;
+  r.signal = nullptr;
+  r.skip = k >= uniform(rs.count);  // the run has fewer items than this round
+  if (r.skip) return r;
+  const bool head = rs.head1 < n;
+  // role: 1 = head, 2 = tail, 0 = whole chain
+  const int role = uniform(head && k == 0 ? 1 : (rs.tail0 > 0 && k == rs.count - 1) ? 2 : 0);
+  const int chain = uniform(role == 1 ? rs.c_hi
+                                      : role == 2 ? rs.c_lo
+                                                  : rs.c_lo + (rs.tail0 > 0) + (k - (int)head));
+  const int c0 = uniform(role == 2 ? rs.tail0 : 0);
+  const int c1 = uniform(role == 1 ? rs.head1 : n);
+  const int srank = chain / p.H;
+  r.h = chain - srank * p.H;
+  r.vs = 0;
+  r.chain = chain;
+  const int t0 = c0 * kC, t1 = c1 * kC < p.seq_len ? c1 * kC : p.seq_len;
+  r.bos = (int64_t)srank * p.seq_len + t0;
+  r.len = t1 - t0;
+  r.s0 = p.s0 ? p.s0 + (int64_t)chain * (kD * kD) : nullptr;
+  r.sf = p.sfinal ? p.sfinal + (int64_t)chain * (kD * kD) : nullptr;
+  if (role == 1) {
+    r.sf = p.ho_state + (int64_t)w * (kD * kD);
+    r.signal = p.ho_flag + w;
+  } else if (role == 2) {
+    r.s0 = p.ho_state + (int64_t)(w - 1) * (kD * kD);
+    r.wait = p.ho_flag + (w - 1);
+  }
+  r.write_o = true;
+  r.zero_v = false;
+  r.skip = r.len <= 0;
   return r;
 }
 

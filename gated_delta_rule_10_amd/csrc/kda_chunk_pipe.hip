@@ -779,12 +779,30 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   }
 }
 
+// State hand-over between the workgroups of the balanced schedule.  The head's
+// final state is stored by the consumer waves; every thread's release fence at
+// device scope, a barrier, then the flag.  The tail's reader polls the flag
+// (bounded: after ~2^22 polls it goes on, so every wave exits), then a barrier
+// and an acquire fence in every thread before the state is read.
+__device__ __forceinline__ void publish_state(int32_t *flag, int tid) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void await_state(const int32_t *flag, int tid) {
+  if (tid == 0) {
+    for (int i = 0; i < (1 << 22); ++i) {
+      if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 template <bool GATE>
 __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
-  const ChunkItem itm = decode_item(p, 1);
-  if (itm.skip) return;  // uniform: the whole workgroup
-  const int nblk = (int)((itm.len + kC - 1) / kC);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -796,6 +814,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
     sm.buf[b].pm[(32 * t + rr) * kLDC + skpos(32 * t + 16 + cc)] = (bf16)0.f;
   }
 
+  const ChunkItem itm = p.pass == kPassHandoff ? run_item(p) : decode_item(p, 1);
+  if (itm.skip) return;  // uniform: the whole workgroup
+  if (itm.wait) await_state(itm.wait, tid);
+  const int nblk = (int)((itm.len + kC - 1) / kC);
+
   // The two roles run separate loops with the same barriers (one before the
   // loop, two per iteration) and leave them at the same iteration: every wave
   // reads the same LDS flag after the same barrier.  In iteration it the
@@ -805,6 +828,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
     producer_loop<GATE>(p, itm, sm, w - 4, lane, nblk);
   else
     consumer_loop(p, itm, sm, w, lane);
+  if (itm.signal) publish_state(itm.signal, tid);
 }
 
 }  // namespace

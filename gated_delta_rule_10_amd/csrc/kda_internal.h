@@ -35,6 +35,10 @@ struct ChunkPlan {
   // workspace layout (byte offsets)
   size_t order_off = 0, order_bytes = 0;      // int32 [N] longest-first sequence order
   size_t seg_state_off = 0, seg_state_bytes = 0;  // fp32 segment M / S~ / S_in buffers
+  // balanced schedule of equal-length chains: workgroups, chunks per
+  // workgroup, and the hand-over states + flags
+  int64_t ho_workers = 0, ho_len = 0, ho_rounds = 0;
+  size_t ho_off = 0, ho_bytes = 0;
   size_t total_bytes = 0;
 };
 

@@ -198,6 +198,27 @@ def test_segments_fixed_batch_without_initial_state(kda):
     assert rel_err(to64(s1), to64(s0)) <= TOL[torch.bfloat16]
 
 
+def test_balanced_schedule_hands_states_over(kda):
+    """A fixed-length batch with more chains than compute units (3 x 96 = 288
+    chains of 16 chunks, the last one ragged) and a nonzero initial state: the
+    automatic schedule cuts chains between workgroups, which hand the state over;
+    against the oracle on cut chains and against whole chains (segments=1)."""
+    announce("chunk balanced schedule b3 t1000 h96")
+    cfg = ki.PrefillConfig("t", (1000, 1000, 1000), 96, "bf16", init_std=0.02)
+    inp = ki.make_prefill(cfg, device="cuda", seed=71)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the cut points below assume 256 compute units")
+    assert kda.chunk_fwd_workspace_size(inp["q"], num_seqs=3, segments=0) > 0
+    o0, s0 = run(kda, inp, varlen=False)
+    o1, s1 = run(kda, inp, varlen=False, segments=1)
+    torch.cuda.synchronize()
+    # runs of 18 chunks: chain 1 cut at chunk 2, chain 112 = (1, 16) at chunk 8,
+    # chain 286 = (2, 94) at chunk 14; chain 0 whole
+    check_chains(inp, o0, s0, [(0, 0), (0, 1), (1, 16), (2, 94)], torch.bfloat16)
+    assert rel_err(to64(o0), to64(o1)) <= TOL[torch.bfloat16]
+    assert rel_err(to64(s0), to64(s1)) <= 1e-4
+
+
 # ----------------------------------------------------------- full-size workloads
 def test_full_b4_t8192_h96_sampled(kda):
     """B=4, T=8192, H=96, bf16, zero initial state -- the benchmark workload, in the
@@ -207,7 +228,9 @@ def test_full_b4_t8192_h96_sampled(kda):
     inp = ki.make_prefill(cfg, device="cuda", seed=1002)
     o, sf = run(kda, inp, varlen=False)
     torch.cuda.synchronize()
-    check_chains(inp, o, sf, [(0, 0), (1, 17), (2, 50), (3, 95), (0, 63), (3, 1)],
+    # 384 chains on 256 units run as 256 runs of 192 chunks; (0, 1) and (3, 1)
+    # are cut at chunk 64 and handed over between two workgroups
+    check_chains(inp, o, sf, [(0, 0), (0, 1), (1, 17), (2, 50), (3, 95), (0, 63), (3, 1)],
                  torch.bfloat16)
 
 
