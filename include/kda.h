@@ -133,7 +133,12 @@ typedef struct kda_gate {
  * head).  segments = 0 lets the library choose: for bf16 I/O, sequences of
  * at least 8 chunks and no more num_seqs * num_heads chains than the current
  * device has compute units, every sequence is split into three segments whose
- * first one takes half of the chunks; otherwise no split.
+ * first one takes half of the chunks; otherwise no split.  Also in automatic
+ * mode, a fixed-length bf16 batch with more chains than compute units, not a
+ * whole multiple of them, may run as equal runs of chunks per workgroup: a
+ * chain cut at a chunk boundary between two workgroups hands its state over
+ * through the workspace (one 128 x 128 fp32 state and a flag per workgroup),
+ * so the result is the same recurrence up to rounding at the cut.
  * ---------------------------------------------------------------------- */
 typedef struct kda_chunk_fwd_args {
   int32_t num_seqs;               /* N >= 1                                              */
