@@ -155,14 +155,20 @@ __device__ __forceinline__ Split split(const f32x4 &x) {
 }
 __device__ __forceinline__ f32x4 tn(const Split &b, const Split &c) {
   // Bh^T Ct + Bt^T Ch as one 32-deep product (the two 16-deep operand pairs
-  // side by side in each lane's 8 k-slots), then Bh^T Ch
+  // side by side in each lane's 8 k-slots) and Bh^T Ch as a 16-deep one, each
+  // into an accumulator of its own, summed on the vector unit.  Chaining the
+  // 16-deep product onto the 32-deep one's accumulator (different matrix
+  // instructions back to back on the same registers) made the result depend on
+  // timing: it occasionally took the chained accumulator before the first
+  // product had landed.
   Frag<bf16> x, y;
   x.v = __builtin_shufflevector(b.h.v, b.t.v, 0, 1, 2, 3, 4, 5, 6, 7);
   y.v = __builtin_shufflevector(c.t.v, c.h.v, 0, 1, 2, 3, 4, 5, 6, 7);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  mma(acc, x, y);
-  mma16(acc, b.h, c.h);
-  return acc;
+  f32x4 tail = {0.f, 0.f, 0.f, 0.f};
+  mma(tail, x, y);
+  f32x4 head = {0.f, 0.f, 0.f, 0.f};
+  mma16(head, b.h, c.h);
+  return head + tail;
 }
 
 // Gram jobs of producer wave P: (kind, row tile i, column tile j).

@@ -98,14 +98,63 @@ def test_bounded_gate_slow_decay_and_long_memory(kda):
     check_chains(inp, o, sf, [(0, 0), (0, 1), (1, 0), (1, 1)], torch.bfloat16)
 
 
-def test_deterministic(kda):
-    announce("chunk determinism")
+def poisoned_run(kda, inp, poison, segments=0):
+    """One prefill whose o, final state and workspace start filled with `poison`,
+    so that any element no launch writes (or any read of unwritten workspace)
+    shows up in the result."""
+    N = len(inp["lengths"])
+    T, H, D = inp["q"].shape
+    o = torch.full_like(inp["q"], poison)
+    sf = torch.full((N, H, D, D), poison, dtype=torch.float32, device=inp["q"].device)
+    wsb = kda.chunk_fwd_workspace_size(inp["q"], num_seqs=N,
+                                       cu_seqlens_host=inp["cu_seqlens_host"], segments=segments)
+    ws = torch.full(((wsb + 3) // 4 + 1,), poison, dtype=torch.float32, device=inp["q"].device)
+    kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                  cu_seqlens=inp["cu_seqlens"], cu_seqlens_host=inp["cu_seqlens_host"],
+                  initial_state=inp["initial_state"], num_seqs=N, out=o, final_state=sf,
+                  workspace=ws.view(torch.uint8), segments=segments)
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def where_different(name, a, b, cu=None):
+    """'' when a and b are the same bits, else which (token, head) rows or
+    (sequence, head) states differ and by how much."""
+    a = a.float().cpu().numpy()
+    b = b.float().cpu().numpy()
+    d = a.view(np.uint32) != b.view(np.uint32)
+    if not d.any():
+        return ""
+    idx = np.argwhere(d)
+    if cu is not None:  # o: map tokens to (sequence, row in sequence)
+        seq = np.searchsorted(np.asarray(cu), idx[:, 0], side="right") - 1
+        where = sorted({(int(s), int(h)) for s, h in zip(seq, idx[:, 1])})
+        rows = f"tokens {int(idx[:, 0].min())}..{int(idx[:, 0].max())}"
+    else:
+        where = sorted({(int(n), int(h)) for n, h in idx[:, :2]})
+        rows = f"key rows {int(idx[:, 2].min())}..{int(idx[:, 2].max())}"
+    return (f"{name}: {int(d.sum())} elements differ in (sequence, head) {where[:12]}, {rows}, "
+            f"max |diff| {float(np.nanmax(np.abs(a[d] - b[d]))):.3e}")
+
+
+@pytest.mark.parametrize("segments", [0, 1])
+def test_deterministic(kda, segments):
+    """The same inputs give the same bits, with the outputs and the workspace
+    poisoned before each call (NaN, then a finite value): every output element
+    is written and nothing unwritten is read.  segments = 0 takes the automatic
+    three-segment split here (16 chains of up to 16 chunks); 1 runs whole chains."""
+    announce(f"chunk determinism segments={segments}")
     cfg = ki.PrefillConfig("t", (1000, 37), 8, "bf16", init_std=0.1, varlen=True)
     inp = ki.make_prefill(cfg, device="cuda", seed=3)
-    o1, s1 = run(kda, inp)
-    o2, s2 = run(kda, inp)
-    torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    cu = inp["cu_seqlens_host"]
+    o1, s1 = poisoned_run(kda, inp, float("nan"), segments)
+    assert torch.isfinite(o1).all(), "o has elements no launch wrote (or non-finite values)"
+    assert torch.isfinite(s1).all(), "final state not fully written (or non-finite)"
+    for poison in (float("nan"), 7.0, 0.0):
+        o2, s2 = poisoned_run(kda, inp, poison, segments)
+        msg = "; ".join(m for m in (where_different("o", o1, o2, cu),
+                                     where_different("S_final", s1, s2)) if m)
+        assert not msg, f"poison {poison}: {msg}"
 
 
 def test_split_and_resume(kda):
