@@ -16,6 +16,8 @@ __all__ = [
     "KDAError",
     "chunk_fwd",
     "chunk_fwd_workspace_size",
+    "chunk_fwd_no_alloc",
+    "no_alloc_max_workspace",
     "chunk_bwd",
     "chunk_bwd_workspace_size",
     "recurrent_step",
@@ -195,6 +197,10 @@ def library(path: str = LIB_PATH):
                            "`python -m gated_delta_rule_10_amd.build`")
     lib = ctypes.CDLL(path)
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd_no_alloc.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd_no_alloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_no_alloc_max_workspace.argtypes = []
+    lib.kda_chunk_fwd_no_alloc_max_workspace.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkFwdArgs),
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(RecurrentStepArgs), ctypes.c_void_p]
@@ -328,23 +334,12 @@ def chunk_fwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None, segments=0)
     return int(out.value)
 
 
-def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
-              output_final_state=True, scale=1.0, segments=0, num_seqs=None, out=None,
-              final_state=None, workspace=None, A_log=None, dt_bias=None, lower_bound=-5.0,
-              beta_logits=False):
-    """Chunkwise KDA prefill forward.
-
-    q, k, v: [T, H, 128] bf16 or fp32 (same dtype); g: [T, H, 128] fp32 log-decay;
-    beta: [T, H] fp32; cu_seqlens: int32 [N+1] on the device (packed batch) or None
-    for ``num_seqs`` (default 1, or initial_state.shape[0]) sequences of equal
-    length; initial_state: [N, H, 128, 128] fp32 or None.
-    With ``A_log`` ([H] fp32) g holds raw gate logits and the kernels apply the
-    lower-bounded gate lower_bound * sigmoid(exp(A_log) (g + dt_bias)) (dt_bias
-    [H, 128] fp32 or None); with ``beta_logits`` beta holds logits (sigmoid
-    applied in the kernels).
-    Returns (o [T, H, 128], final_state [N, H, 128, 128] fp32 or None).
-    """
-    lib = library()
+def _chunk_fwd_setup(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state,
+                     output_final_state, scale, segments, num_seqs, out, final_state, A_log,
+                     dt_bias, lower_bound, beta_logits, allocate):
+    """Check the tensors and fill kda_chunk_fwd_args (everything but the
+    workspace).  With ``allocate`` a missing o / final state is allocated;
+    without, the caller must pass them.  Returns (args, host array, o, final)."""
     _need(q, "q", ndim=3)
     for name, t in (("k", k), ("v", v)):
         _need(t, name, dtype=q.dtype, ndim=3)
@@ -362,10 +357,15 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
         _need(initial_state, "initial_state", dtype=torch.float32, ndim=4)
         if initial_state.shape != (N, H, D, D):
             raise ValueError(f"initial_state must be [{N}, {H}, {D}, {D}]")
+    if out is None and not allocate:
+        raise ValueError("out is required (this call allocates nothing)")
     o = _out_like(out, q)
     if not output_final_state:
         final_state = None
     elif final_state is None:
+        if not allocate:
+            raise ValueError("final_state is required with output_final_state "
+                             "(this call allocates nothing)")
         final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=q.device)
     else:  # the caller's: the kernels see only its pointer
         _need(final_state, "final_state", dtype=torch.float32, ndim=4)
@@ -381,6 +381,29 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     a.initial_state = None if initial_state is None else initial_state.data_ptr()
     a.final_state = None if final_state is None else final_state.data_ptr()
     a.o = o.data_ptr()
+    return a, host, o, final_state
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+              output_final_state=True, scale=1.0, segments=0, num_seqs=None, out=None,
+              final_state=None, workspace=None, A_log=None, dt_bias=None, lower_bound=-5.0,
+              beta_logits=False):
+    """Chunkwise KDA prefill forward.
+
+    q, k, v: [T, H, 128] bf16 or fp32 (same dtype); g: [T, H, 128] fp32 log-decay;
+    beta: [T, H] fp32; cu_seqlens: int32 [N+1] on the device (packed batch) or None
+    for ``num_seqs`` (default 1, or initial_state.shape[0]) sequences of equal
+    length; initial_state: [N, H, 128, 128] fp32 or None.
+    With ``A_log`` ([H] fp32) g holds raw gate logits and the kernels apply the
+    lower-bounded gate lower_bound * sigmoid(exp(A_log) (g + dt_bias)) (dt_bias
+    [H, 128] fp32 or None); with ``beta_logits`` beta holds logits (sigmoid
+    applied in the kernels).
+    Returns (o [T, H, 128], final_state [N, H, 128, 128] fp32 or None).
+    """
+    lib = library()
+    a, host, o, final_state = _chunk_fwd_setup(
+        q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, output_final_state, scale,
+        segments, num_seqs, out, final_state, A_log, dt_bias, lower_bound, beta_logits, True)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws_bytes)),
            "kda_chunk_fwd_workspace_size")
@@ -394,6 +417,30 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens=None, cu_seqlens_host=None, initial_s
     _check(lib.kda_chunk_fwd(ctypes.byref(a), _stream(q)), "kda_chunk_fwd")
     del host
     return o, final_state
+
+
+def chunk_fwd_no_alloc(q, k, v, g, beta, out, final_state=None, cu_seqlens=None,
+                       cu_seqlens_host=None, initial_state=None, output_final_state=True,
+                       scale=1.0, segments=0, num_seqs=None, A_log=None, dt_bias=None,
+                       lower_bound=-5.0, beta_logits=False):
+    """chunk_fwd for callers that cannot allocate: the same computation (same
+    bits) with the workspace taken from the library's per-GPU buffer of
+    no_alloc_max_workspace() bytes.  ``out`` (and ``final_state`` unless
+    output_final_state is False) must be given; nothing is allocated on the
+    device.  Calls that overlap in time on one GPU race on the buffer.  Raises
+    KDAError (KDA_ERROR_WORKSPACE) when the call needs a larger workspace."""
+    lib = library()
+    a, host, o, final_state = _chunk_fwd_setup(
+        q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, output_final_state, scale,
+        segments, num_seqs, out, final_state, A_log, dt_bias, lower_bound, beta_logits, False)
+    _check(lib.kda_chunk_fwd_no_alloc(ctypes.byref(a), _stream(q)), "kda_chunk_fwd_no_alloc")
+    del host
+    return o, final_state
+
+
+def no_alloc_max_workspace() -> int:
+    """Bytes of the per-GPU buffer behind chunk_fwd_no_alloc."""
+    return int(library().kda_chunk_fwd_no_alloc_max_workspace())
 
 
 def chunk_bwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None, minimum=False) -> int:

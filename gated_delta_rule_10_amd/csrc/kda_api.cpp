@@ -201,6 +201,26 @@ kda_status kda_chunk_fwd(const kda_chunk_fwd_args *a, void *stream) {
   return launch_status(kda::launch_chunk_fwd(*a, plan, (hipStream_t)stream));
 }
 
+kda_status kda_chunk_fwd_no_alloc(const kda_chunk_fwd_args *a, void *stream) {
+  int64_t T = 0;
+  const kda_status st = check_chunk_args(a, &T, true);
+  if (st != KDA_SUCCESS) return st;
+  kda::ChunkPlan plan;
+  const kda_status ps = kda::plan_chunk_fwd(*a, &plan);
+  if (ps != KDA_SUCCESS) return ps;
+  if (plan.total_bytes > kda::kNoAllocScratchBytes) return KDA_ERROR_WORKSPACE;
+  kda_chunk_fwd_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (plan.total_bytes > 0) {
+    if (kda::no_alloc_scratch(&b.workspace) != hipSuccess) return KDA_ERROR_LAUNCH;
+    b.workspace_bytes = kda::kNoAllocScratchBytes;
+  }
+  return launch_status(kda::launch_chunk_fwd(b, plan, (hipStream_t)stream));
+}
+
+size_t kda_chunk_fwd_no_alloc_max_workspace(void) { return kda::kNoAllocScratchBytes; }
+
 kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *a, size_t *bytes) {
   if (!bytes) return KDA_ERROR_INVALID_VALUE;
   int64_t T = 0, ms = 0;

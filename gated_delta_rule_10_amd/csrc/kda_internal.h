@@ -43,6 +43,11 @@ struct ChunkPlan {
 };
 
 kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan);
+
+// The per-GPU scratch buffer of kda_chunk_fwd_no_alloc: its size, and its device
+// address on the current device (looked up on the first call per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t no_alloc_scratch(void **addr);
 hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
                             hipStream_t stream);
 

@@ -38,7 +38,9 @@
  *    formula has scale = 1.
  *  - Ownership: the caller allocates and owns every buffer (device memory unless
  *    a field says host).  The library allocates no device memory, keeps no
- *    pointer after a call returns and holds no mutable global state.
+ *    pointer after a call returns and holds no mutable global state -- except
+ *    the per-GPU scratch buffer of kda_chunk_fwd_no_alloc (a static device
+ *    array reserved when the library is loaded).
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Work is enqueued asynchronously; no call synchronises the host.
  *  - Errors: arguments are validated on the host before anything is enqueued.
@@ -183,6 +185,29 @@ kda_status kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args *args, size_t *
  * KDA_ERROR_UNSUPPORTED for head_dim != 128 or chunk_size != 64;
  * KDA_ERROR_WORKSPACE when the workspace is smaller than queried. */
 kda_status kda_chunk_fwd(const kda_chunk_fwd_args *args, void *stream);
+
+/* The prefill forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It computes exactly what kda_chunk_fwd
+ * computes (same kernels, same plan, same bits) but takes its workspace from a
+ * buffer the library holds: one static device array of
+ * kda_chunk_fwd_no_alloc_max_workspace() bytes (64 MiB) per GPU, reserved when
+ * the library is loaded and held until the process ends.  args->workspace and
+ * args->workspace_bytes are ignored.  The call allocates nothing.
+ * Limit: returns KDA_ERROR_WORKSPACE, touching no buffer, when the plan needs
+ * more than that (kda_chunk_fwd_workspace_size tells how much a call needs;
+ * e.g. 56.6 MiB for one 65,536-token sequence of 96 heads split into three
+ * segments).  Other errors as kda_chunk_fwd; KDA_ERROR_LAUNCH also when the
+ * buffer's device address cannot be looked up.
+ * Every call on a GPU shares that GPU's buffer and leaves its contents behind:
+ * all the prefill reads from it is written earlier in the same call (the
+ * hand-over flags are cleared by a kernel at the start of each call), so the
+ * previous contents never matter, but calls that overlap in time on one GPU race
+ * on the buffer and must be ordered by the caller (one stream, or events). */
+kda_status kda_chunk_fwd_no_alloc(const kda_chunk_fwd_args *args, void *stream);
+
+/* Size in bytes of the per-GPU buffer of kda_chunk_fwd_no_alloc. */
+size_t kda_chunk_fwd_no_alloc_max_workspace(void);
 
 /* ------------------------------------------------------------------------
  * Chunked backward ([P1] "How KDA updates its state": the recurrence;

@@ -96,6 +96,22 @@ def test_chunk_fwd_rejects_invalid_arguments(lib, field, value, status):
         0 if pointer_field else status)
 
 
+def test_no_alloc_prefill_validates_on_the_host(lib):
+    """The allocation-free prefill checks its arguments as kda_chunk_fwd does and
+    refuses, before any GPU work, a plan whose workspace exceeds its buffer."""
+    assert lib.kda_chunk_fwd_no_alloc_max_workspace() == 64 << 20
+    for field, value, status in (("head_dim", 64, 2), ("num_heads", 0, 1), ("q", 0, 1),
+                                 ("g", (1 << 20) + 4, 1)):
+        a = _args(**{field: value})
+        assert lib.kda_chunk_fwd_no_alloc(ctypes.byref(a), None) == status
+    # 96 heads x 64 explicit segments: 3 x 64 states per chain, far beyond 64 MiB
+    a = _args(seq_len=8192, num_heads=96, segments=64)
+    size = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(size)) == 0
+    assert size.value > lib.kda_chunk_fwd_no_alloc_max_workspace()
+    assert lib.kda_chunk_fwd_no_alloc(ctypes.byref(a), None) == 3
+
+
 def test_chunk_fwd_rejects_bad_cu_seqlens(lib):
     for host in ([1, 5, 9], [0, 9, 5]):
         arr = (ctypes.c_int32 * 3)(*host)
