@@ -1,10 +1,13 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-A step is one chunked prefill forward of the 4 x 8,192-token, 96-head bf16
-workload (chunk 64, fp32 state, outputs + final states), inputs resident in HBM
-before the timed region.  The recurrent decode workload (512 sequences x 96
-heads, fp32 states in HBM, 1000 in-place steps) is timed after it and reported
-in the same JSON line.
+A step is one chunked prefill forward (chunk 64, fp32 state, outputs + final
+states) of the largest workload that fits one GPU: the varlen pack of 32
+sequences, lengths log-uniform in [1K, 256K] summing to 1,048,576 tokens, 96
+heads, bf16 -- inputs resident in HBM before the timed region.  The 4 x 8,192 x
+96 batch and the single 65,536-token sequence (nonzero initial state, decay
+floor -5) are timed after it and reported as extra prefill lines; the recurrent
+decode workload (512 sequences x 96 heads, fp32 states in HBM, 1000 in-place
+steps) last, in the same JSON line.
 
 With --front gate the prefill reads raw gate logits (fp32, in place of g), per-head
 A_log and per-channel dt_bias, and beta logits, and applies K3's lower-bounded gate
@@ -34,7 +37,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill tokens/s + % MFMA peak; decode step GB/s + % HBM peak"
-PREFILL_WORKLOAD = "kda_prefill_b4_t8192_h96_bf16"
+PREFILL_WORKLOAD = "kda_prefill_varlen32_t1m_h96_bf16"
+EXTRA_WORKLOADS = "kda_prefill_b4_t8192_h96_bf16,kda_prefill_t65536_h96_bf16_s0_gclamp5"
 DECODE_WORKLOAD = "kda_decode_b512_h96_bf16_f32state"
 D, C = 128, 64
 FLOP_PER_TOKEN_HEAD = 6 * D * D + C * (3 * D + 2 * D)          # 139,264
@@ -49,8 +53,8 @@ BF16_PEAK_TFLOPS = 2516.6
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-kernel", choices=("step", "fused", "spec"), default="step",
@@ -62,13 +66,15 @@ def parse():
     ap.add_argument("--bwd", action="store_true",
                     help="also time the chunked backward on the prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-chains-per-core", type=int, default=2)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle sample until this much wall time has passed")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy a state pool of this many MiB once (the plain "
                          "copy kernel whose hardware byte counters scale the prefill's)")
     ap.add_argument("--workload", default=PREFILL_WORKLOAD)
+    ap.add_argument("--extra", default=EXTRA_WORKLOADS,
+                    help="comma-separated further prefill workloads, timed after the headline "
+                         "one and reported under prefill_workloads ('' for none)")
     ap.add_argument("--segments", type=int, default=0,
                     help="segments per sequence (0 = the library's automatic choice)")
     ap.add_argument("--gate-params", choices=("matched", "heavy"), default="matched",
@@ -82,6 +88,21 @@ def parse():
                          "WRITE_SIZE counter_collection.csv files (taken with "
                          "--copy-calibration-mib) and exit; needs no GPU")
     return ap.parse_args()
+
+
+def prefill_summary(pre, steps):
+    """Throughput of a timed prefill against the fixed accounting (per token-head
+    139,264 FLOP and 1,540 B, plus 64 KiB per chain for the final state and,
+    when given, the initial state)."""
+    H, tokens, N, ms = pre["heads"], pre["tokens"], pre["seqs"], pre["ms"]
+    tok_s = tokens / (ms * 1e-3)
+    tflops = tok_s * H * FLOP_PER_TOKEN_HEAD / 1e12
+    alg = tokens * H * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES * (
+        2 if pre["x"]["initial_state"] is not None else 1)
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"ms_per_step": ms, "steps": steps, "sequences": N, "tokens": tokens, "heads": H,
+            "tokens_per_s": tok_s, "tflops": tflops, "mfma_peak_frac": tflops / BF16_PEAK_TFLOPS,
+            "gb_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": alg}
 
 
 def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
@@ -129,6 +150,7 @@ def time_prefill(kda, ki, workload, steps, warmup, segments=0, front="logdecay",
     return res
 
 
+PREFILL_BWD_WORKLOAD = "kda_prefill_b4_t8192_h96_bf16"  # the backward's timed workload
 BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 4 * D + 4 + 4 * 4 * D + 4     # 3,592
 # Matrix-core work of the backward per 16-token sub-chunk of one head (all 128
 # value columns, d = 128), product by product as the passes compute them; the
@@ -303,20 +325,25 @@ def time_decode(kda, ki, steps, warmup=10, kernel="step", window=4):
                 **extra)
 
 
-def cpu_baseline(x, chains_per_core, seconds, gp=None):
-    """Time the fp64 oracle on a bounded sample of the same workload's chains.
+def baseline_chains(x):
+    """The (sequence, head) chains the oracle baseline times: heads 0, 31, 63 and
+    95 (spread over the 96) of every sequence, up to 32 sequences."""
+    N, H = len(x["lengths"]), x["heads"]
+    heads = sorted({round(i * (H - 1) / 3) for i in range(4)}) if H >= 4 else list(range(H))
+    return [(n, h) for h in heads for n in range(min(N, 32))]
 
-    The sample (cores x chains_per_core whole (sequence, head) chains) is run
-    repeatedly until `seconds` of wall time have passed; the rate is the mean.
-    With gate parameters `gp` the oracle's gate and beta sigmoid run inside the
-    timed loop too."""
+
+def cpu_baseline(x, seconds, gp=None):
+    """Time the fp64 oracle (as it stands: OpenMP over chains) on a bounded
+    sample of the same workload: the chains of baseline_chains, whole, run
+    repeatedly until `seconds` of wall time have passed (at least once); the rate
+    is the mean.  With gate parameters `gp` the oracle's gate and beta sigmoid run
+    inside the timed loop too."""
     import numpy as np
     import oracle
-    cores = len(os.sched_getaffinity(0))
-    nchains = max(1, cores * chains_per_core)
+    chains = baseline_chains(x)
     cu = x["cu_seqlens_host"]
-    N, H = len(cu) - 1, x["heads"]
-    chains = [(i % N, (i * 7) % H) for i in range(nchains)]
+    H = x["heads"]
     to = lambda t: t.detach().cpu().double().numpy()
     qs, ks, vs, gs, bs, lens = [], [], [], [], [], []
     for n, h in chains:
@@ -326,10 +353,12 @@ def cpu_baseline(x, chains_per_core, seconds, gp=None):
     cu2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     cat = lambda xs: np.concatenate(xs, axis=0)[:, None]
     args = (cat(qs), cat(ks), cat(vs), cat(gs), np.concatenate(bs)[:, None])
+    del qs, ks, vs, gs, bs
     if gp is not None:
         A_np, dt_np = to(gp["A_log"]), to(gp["dt_bias"])
     oracle.load()
-    threads = min(cores, oracle.max_threads(), nchains)
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, oracle.max_threads(), len(chains))
     passes, t0 = 0, time.perf_counter()
     while True:
         if gp is not None:  # per token: the gate of its chain's head, then the loop
@@ -346,10 +375,13 @@ def cpu_baseline(x, chains_per_core, seconds, gp=None):
         if dt >= seconds:
             break
     token_heads = int(cu2[-1]) * passes
+    heads = sorted({h for _, h in chains})
+    nseq = len({n for n, _ in chains})
     return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nchains} (sequence, head) chains of {lens[0]} tokens each "
-                      f"({int(cu2[-1])} token-heads, fp64 token loop, OpenMP over chains), "
-                      f"run {passes} times; value = token-heads/s divided by {H} heads",
+            "sample": f"heads {heads} of {nseq} sequences of the same workload: {len(chains)} "
+                      f"(sequence, head) chains, {int(cu2[-1])} token-heads (fp64 token loop, "
+                      f"OpenMP over chains on {threads} threads), run {passes} times; value = "
+                      f"token-heads/s divided by {H} heads",
             "token_heads_per_s": token_heads / dt, "seconds": dt}
 
 
@@ -357,10 +389,18 @@ PREFILL_KERNEL = "chunk_fwd_pipe_kernel"
 PREFILL_SOURCES = ["gated_delta_rule_10_amd/csrc/kda_chunk_pipe.hip",
                    "gated_delta_rule_10_amd/csrc/kda_chunk_common.h",
                    "gated_delta_rule_10_amd/csrc/kda_device.h"]
-TRAFFIC_RECORDS = {
-    "logdecay": os.path.join(ROOT, "profiles", "chunk_fwd_bf16_b4_t8192_h96_traffic.json"),
-    "gate": os.path.join(ROOT, "profiles", "chunk_fwd_gate_bf16_b4_t8192_h96_traffic.json"),
+TRAFFIC_NAMES = {
+    "kda_prefill_varlen32_t1m_h96_bf16": "chunk_fwd_bf16_varlen32_t1m_h96",
+    "kda_prefill_b4_t8192_h96_bf16": "chunk_fwd_bf16_b4_t8192_h96",
+    "kda_prefill_t65536_h96_bf16_s0_gclamp5": "chunk_fwd_bf16_t65536_h96",
 }
+
+
+def traffic_record_path(workload, front="logdecay"):
+    name = TRAFFIC_NAMES.get(workload, workload)
+    if front == "gate":
+        name = name.replace("chunk_fwd_", "chunk_fwd_gate_")
+    return os.path.join(ROOT, "profiles", name + "_traffic.json")
 
 
 def sources_digest(files):
@@ -374,7 +414,7 @@ def sources_digest(files):
 def measured_traffic(workload, front="logdecay"):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE readings,
     or None when they were taken on other kernel sources or another workload."""
-    path = TRAFFIC_RECORDS[front]
+    path = traffic_record_path(workload, front)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -422,7 +462,7 @@ def record_traffic(fetch_csv, write_csv, workload, mib, front="logdecay"):
                                 "fetch_scale": fscale, "write_scale": wscale},
            "read_bytes": round(fk * 1024 * fscale), "write_bytes": round(wk * 1024 * wscale)}
     rec["traffic_bytes"] = rec["read_bytes"] + rec["write_bytes"]
-    with open(TRAFFIC_RECORDS[front], "w") as fh:
+    with open(traffic_record_path(workload, front), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
@@ -471,49 +511,55 @@ def main():
 
     pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup, args.segments,
                        args.front, args.gate_params)
-    H, tokens, N = pre["heads"], pre["tokens"], pre["seqs"]
-    ms = pre["ms"]
-    tok_s = tokens / (ms * 1e-3)
-    tflops = tok_s * H * FLOP_PER_TOKEN_HEAD / 1e12
-    alg_bytes = tokens * H * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES * (
-        2 if pre["x"]["initial_state"] is not None else 1)
-    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    head = prefill_summary(pre, args.steps)
     line = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": N, "seq_len": tokens // N,
-                   "heads": H, "head_dim": D, "chunk": C, "state": "fp32",
-                   "segments": args.segments, "front": args.front,
+        "config": {"workload": args.workload, "sequences": pre["seqs"],
+                   "tokens": pre["tokens"], "heads": pre["heads"], "head_dim": D, "chunk": C,
+                   "state": "fp32", "segments": args.segments, "front": args.front,
                    **({"gate_params": args.gate_params} if args.front == "gate" else {})},
-        "tflops": tflops,
-        "mfma_peak_frac": tflops / BF16_PEAK_TFLOPS,
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+        "tflops": head["tflops"],
+        "mfma_peak_frac": head["mfma_peak_frac"],
+        "roofline": {"bound": "hbm", "achieved": head["gb_per_s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["hbm_frac"],
                      "traffic": measured_traffic(args.workload, args.front),
                      "kernel": PREFILL_KERNEL,
-                     "bytes_per_launch": alg_bytes},
+                     "bytes_per_launch": head["bytes_per_launch"]},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_seconds, pre["gate_params"])
+    del pre
+    torch.cuda.empty_cache()
+    extras = [w for w in args.extra.split(",") if w and w != args.workload]
+    if extras:
+        line["prefill_workloads"] = {}
+    for wl in extras:
+        steps = max(args.steps, 20)
+        p = time_prefill(kda, ki, wl, steps, max(args.warmup, 5), args.segments, args.front,
+                         args.gate_params)
+        line["prefill_workloads"][wl] = {**prefill_summary(p, steps),
+                                         "traffic": measured_traffic(wl, args.front)}
+        del p
+        torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel,
                                      window=args.spec_window)
         line["decode"]["workload"] = DECODE_WORKLOAD
     if args.bwd:
-        line["backward"] = time_backward(kda, ki, args.workload, max(2, args.steps // 4),
-                                         max(1, args.warmup // 4),
+        line["backward"] = time_backward(kda, ki, PREFILL_BWD_WORKLOAD, max(2, args.steps // 2),
+                                         max(1, args.warmup // 2),
                                          0.0 if args.no_cpu_baseline else args.cpu_seconds)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_chains_per_core, args.cpu_seconds,
-                                            pre["gate_params"])
     if args.copy_calibration_mib > 0:
         line["copy_calibration"] = copy_calibration(kda, args.copy_calibration_mib)
     print(json.dumps(line), flush=True)
