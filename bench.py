@@ -329,7 +329,7 @@ def baseline_chains(x):
     """The (sequence, head) chains the oracle baseline times: heads 0, 31, 63 and
     95 (spread over the 96) of every sequence, up to 32 sequences."""
     N, H = len(x["lengths"]), x["heads"]
-    heads = sorted({round(i * (H - 1) / 3) for i in range(4)}) if H >= 4 else list(range(H))
+    heads = sorted({i * (H - 1) // 3 for i in range(4)}) if H >= 4 else list(range(H))
     return [(n, h) for h in heads for n in range(min(N, 32))]
 
 
@@ -492,6 +492,11 @@ def copy_calibration(kda, mib):
             "ms": ms, "gb_per_s": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def note(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -512,6 +517,7 @@ def main():
     pre = time_prefill(kda, ki, args.workload, args.steps, args.warmup, args.segments,
                        args.front, args.gate_params)
     head = prefill_summary(pre, args.steps)
+    note(f"{args.workload}: {head['ms_per_step']:.3f} ms per prefill")
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -539,6 +545,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre["x"], args.cpu_seconds, pre["gate_params"])
+        note(f"oracle baseline: {line['cpu_baseline']['value']:.0f} tokens/s")
     del pre
     torch.cuda.empty_cache()
     extras = [w for w in args.extra.split(",") if w and w != args.workload]
@@ -550,12 +557,14 @@ def main():
                          args.gate_params)
         line["prefill_workloads"][wl] = {**prefill_summary(p, steps),
                                          "traffic": measured_traffic(wl, args.front)}
+        note(f"{wl}: {line['prefill_workloads'][wl]['ms_per_step']:.3f} ms per prefill")
         del p
         torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel,
                                      window=args.spec_window)
         line["decode"]["workload"] = DECODE_WORKLOAD
+        note("decode timed")
     if args.bwd:
         line["backward"] = time_backward(kda, ki, PREFILL_BWD_WORKLOAD, max(2, args.steps // 2),
                                          max(1, args.warmup // 2),
