@@ -18,6 +18,11 @@ __all__ = [
     "chunk_fwd_workspace_size",
     "chunk_fwd_no_alloc",
     "no_alloc_max_workspace",
+    "device_status",
+    "set_handoff_poll_limit",
+    "handoff_poll_limit",
+    "balanced_schedule",
+    "DEVICE_HANDOFF_TIMEOUT",
     "chunk_bwd",
     "chunk_bwd_workspace_size",
     "recurrent_step",
@@ -54,6 +59,7 @@ class KDAError(RuntimeError):
 
 GATE_LOG_DECAY = 0
 GATE_LOWER_BOUND = 1
+DEVICE_HANDOFF_TIMEOUT = 0x1  # KDA_DEVICE_HANDOFF_TIMEOUT
 
 
 class Gate(ctypes.Structure):
@@ -222,6 +228,17 @@ def library(path: str = LIB_PATH):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kda_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
     lib.kda_state_bytes.restype = ctypes.c_size_t
+    lib.kda_device_status.argtypes = [ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_uint32)]
+    lib.kda_device_status.restype = ctypes.c_int
+    lib.kda_set_handoff_poll_limit.argtypes = [ctypes.c_int32]
+    lib.kda_set_handoff_poll_limit.restype = ctypes.c_int
+    lib.kda_handoff_poll_limit.argtypes = []
+    lib.kda_handoff_poll_limit.restype = ctypes.c_int32
+    lib.kda_balanced_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.kda_balanced_schedule.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -441,6 +458,45 @@ def chunk_fwd_no_alloc(q, k, v, g, beta, out, final_state=None, cu_seqlens=None,
 def no_alloc_max_workspace() -> int:
     """Bytes of the per-GPU buffer behind chunk_fwd_no_alloc."""
     return int(library().kda_chunk_fwd_no_alloc_max_workspace())
+
+
+def device_status(clear: bool = True, device=None) -> int:
+    """KDA_DEVICE_* bits the kernels have set on the current (or given) GPU since
+    the last clear, read after the current stream's queued work has finished."""
+    lib = library()
+    bits = ctypes.c_uint32(0)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _check(lib.kda_device_status(_stream(torch.empty(0, device=dev)), 1 if clear else 0,
+                                     ctypes.byref(bits)), "kda_device_status")
+    return int(bits.value)
+
+
+def set_handoff_poll_limit(polls: int) -> None:
+    """Polls of a hand-over flag before a balanced-schedule workgroup gives up
+    (process-wide; 0 = give up at once, for tests of that path)."""
+    _check(library().kda_set_handoff_poll_limit(int(polls)), "kda_set_handoff_poll_limit")
+
+
+def handoff_poll_limit() -> int:
+    return int(library().kda_handoff_poll_limit())
+
+
+def balanced_schedule(num_seqs: int, seq_len: int, num_heads: int, compute_units: int):
+    """The balanced schedule the prefill would use for this fixed-length batch on
+    a GPU with `compute_units` units (host only): a list of (chain, first chunk,
+    end chunk, role, wait workgroup) per workgroup in dispatch order, or None when
+    the prefill runs whole chains."""
+    lib = library()
+    n = ctypes.c_int64(0)
+    _check(lib.kda_balanced_schedule(num_seqs, seq_len, num_heads, compute_units, None, 0,
+                                     ctypes.byref(n)), "kda_balanced_schedule")
+    if n.value == 0:
+        return None
+    buf = (ctypes.c_int32 * (5 * n.value))()
+    _check(lib.kda_balanced_schedule(num_seqs, seq_len, num_heads, compute_units, buf, n.value,
+                                     ctypes.byref(n)), "kda_balanced_schedule")
+    return [tuple(buf[5 * i:5 * i + 5]) for i in range(n.value)]
 
 
 def chunk_bwd_workspace_size(q, num_seqs=None, cu_seqlens_host=None, minimum=False) -> int:

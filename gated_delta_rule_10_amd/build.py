@@ -16,7 +16,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_state_io.hip", "kda_chunk.hip",
-           "kda_chunk_pipe.hip", "kda_chunk_bwd.hip", "kda_noalloc.hip"]
+           "kda_chunk_pipe.hip", "kda_chunk_bwd.hip", "kda_noalloc.hip", "kda_status.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every device build.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "kda_chunk_common.h"
 #include "kda_internal.h"
 
 namespace {
@@ -220,6 +221,50 @@ kda_status kda_chunk_fwd_no_alloc(const kda_chunk_fwd_args *a, void *stream) {
 }
 
 size_t kda_chunk_fwd_no_alloc_max_workspace(void) { return kda::kNoAllocScratchBytes; }
+
+kda_status kda_device_status(void *stream, int32_t clear, uint32_t *bits) {
+  if (!bits) return KDA_ERROR_INVALID_VALUE;
+  uint32_t v = 0;
+  const hipError_t e = kda::read_device_status((hipStream_t)stream, clear != 0, &v);
+  if (e != hipSuccess) return KDA_ERROR_LAUNCH;
+  *bits = v;
+  return KDA_SUCCESS;
+}
+
+kda_status kda_set_handoff_poll_limit(int32_t polls) {
+  if (polls < 0) return KDA_ERROR_INVALID_VALUE;
+  kda::set_handoff_poll_limit(polls);
+  return KDA_SUCCESS;
+}
+
+int32_t kda_handoff_poll_limit(void) { return kda::handoff_poll_limit(); }
+
+kda_status kda_balanced_schedule(int32_t num_seqs, int32_t seq_len, int32_t num_heads,
+                                 int32_t compute_units, int32_t *items, int64_t capacity,
+                                 int64_t *count) {
+  if (!count || num_seqs < 1 || seq_len < 0 || num_heads < 1 || compute_units < 1)
+    return KDA_ERROR_INVALID_VALUE;
+  const int64_t chains = (int64_t)num_seqs * num_heads;
+  const int64_t n = ((int64_t)seq_len + KDA_CHUNK - 1) / KDA_CHUNK;
+  if (chains >= ((int64_t)1 << 30)) return KDA_ERROR_INVALID_VALUE;
+  kda::ChunkPlan plan;
+  *count = 0;
+  if (!kda::balanced_schedule_applies(chains, n, compute_units, &plan)) return KDA_SUCCESS;
+  const int64_t blocks = plan.ho_workers * plan.ho_rounds;
+  *count = blocks;
+  if (!items) return KDA_SUCCESS;
+  if (capacity < blocks) return KDA_ERROR_INVALID_VALUE;
+  for (int64_t b = 0; b < blocks; ++b) {
+    const kda::RunItem it = kda::run_item_at((int)chains, (int)n, (int)plan.ho_len, (int)b);
+    int32_t *o = items + 5 * b;
+    o[0] = it.chain;
+    o[1] = it.c0;
+    o[2] = it.c1;
+    o[3] = it.chain < 0 ? 0 : it.role;
+    o[4] = it.chain >= 0 && it.role == 2 ? it.w - 1 : -1;
+  }
+  return KDA_SUCCESS;
+}
 
 kda_status kda_chunk_bwd_workspace_size(const kda_chunk_bwd_args *a, size_t *bytes) {
   if (!bytes) return KDA_ERROR_INVALID_VALUE;

@@ -779,16 +779,16 @@ hipError_t launch_typed(const ChunkParams &p, int64_t items, hipStream_t stream)
 
 }  // namespace
 
-// Item lengths (chunks) of run w of the balanced schedule, in order; the host
-// mirror of run_shape / run_item.
+// Item lengths (chunks) of run w of the balanced schedule, in order, as the
+// kernels take them (run_item_at).
 static int run_lengths(int64_t C, int64_t n, int64_t L, int64_t w, int64_t *len) {
-  const int64_t total = C * n, s = w * L, e = s + L < total ? s + L : total;
-  if (e <= s) return 0;
-  const int64_t c_lo = s / n, c_hi = (e - 1) / n, tail0 = s - c_lo * n, head1 = e - c_hi * n;
+  const int W = run_workers((int)C, (int)n, (int)L);
   int m = 0;
-  if (head1 < n) len[m++] = head1;
-  for (int64_t c = c_lo + (tail0 > 0); c <= c_hi - (head1 < n); ++c) len[m++] = n;
-  if (tail0 > 0) len[m++] = n - tail0;
+  for (int k = 0;; ++k) {
+    const RunItem it = run_item_at((int)C, (int)n, (int)L, k * W + (int)w);
+    if (it.chain < 0) break;
+    len[m++] = it.c1 - it.c0;
+  }
   return m;
 }
 
@@ -828,6 +828,12 @@ static bool balanced_schedule_pays(int64_t C, int64_t n, int U, ChunkPlan *pl) {
   pl->ho_workers = W;
   pl->ho_rounds = rounds;
   return true;
+}
+
+// Equal chains that do not fill whole rounds of the units, two chunks or more
+// each, where the schedule pays.
+bool balanced_schedule_applies(int64_t C, int64_t n, int U, ChunkPlan *pl) {
+  return U > 0 && C > U && C % U != 0 && n >= 2 && balanced_schedule_pays(C, n, U, pl);
 }
 
 kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
@@ -894,8 +900,8 @@ kda_status plan_chunk_fwd(const kda_chunk_fwd_args &a, ChunkPlan *plan) {
   // runs' items round by round as they free up, finish clearly before whole
   // chains would (1.5 n instead of 2 n for 384 chains on 256 units), the
   // prefill uses it.
-  if (cus > 0 && pl.segments <= 1 && !pl.varlen && chains > cus && chains % cus != 0 &&
-      pl.max_chunks >= 2 && balanced_schedule_pays(chains, pl.max_chunks, cus, &pl)) {
+  if (pl.segments <= 1 && !pl.varlen &&
+      balanced_schedule_applies(chains, pl.max_chunks, cus, &pl)) {
     pl.ho_off = off;
     pl.ho_bytes = (size_t)pl.ho_workers * (kD * kD * 4 + 4);
     off += (pl.ho_bytes + 255) & ~(size_t)255;
@@ -950,11 +956,16 @@ hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
   p.ho_state = nullptr;
   p.ho_flag = nullptr;
   p.ho_len = 0;
+  p.ho_polls = 0;
+  p.status = nullptr;
   if (plan.ho_workers > 0) {
     char *base = (char *)a.workspace + plan.ho_off;
     p.ho_state = reinterpret_cast<float *>(base);
     p.ho_flag = reinterpret_cast<int32_t *>(base + (size_t)plan.ho_workers * kD * kD * 4);
     p.ho_len = plan.ho_len;
+    p.ho_polls = handoff_poll_limit();
+    const hipError_t es = device_status_word(&p.status);
+    if (es != hipSuccess) return es;
     p.pass = kPassHandoff;
     hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((plan.ho_workers + 255) / 256)),
                        dim3(256), 0, stream, p.ho_flag, plan.ho_workers);

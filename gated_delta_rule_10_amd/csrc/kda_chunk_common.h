@@ -47,6 +47,8 @@ struct ChunkParams {
   float *ho_state;       // [workgroups][128 x 128] fp32 handed-over states
   int32_t *ho_flag;      // [workgroups] set to 1 once that state is stored
   int64_t ho_len;        // chunks per workgroup
+  int32_t ho_polls;      // polls of a hand-over flag before a tail gives up
+  uint32_t *status;      // the GPU's status word (KDA_DEVICE_* bits), or null
 };
 
 constexpr int kPassHandoff = 3;
@@ -79,6 +81,7 @@ struct ChunkItem {
   const int32_t *wait;  // flag to see set before s0 is read (null = none)
   int32_t *signal;      // flag to set once sf is stored (null = none)
   bool write_o, zero_v, skip;
+  bool poison;          // the incoming state never arrived: start from NaN
 };
 
 // Chunks [lo, hi) of segment seg of a sequence of nch chunks split into pn.
@@ -148,6 +151,7 @@ __device__ __forceinline__ ChunkItem decode_item(const ChunkParams &p, int VS) {
   r.zero_v = mode == kTrackM;
   r.wait = nullptr;
   r.signal = nullptr;
+  r.poison = false;
   return r;
 }
 
@@ -168,8 +172,8 @@ struct RunShape {
   int count;       // items of the run
 };
 // 32-bit arithmetic (the host enables the schedule for C n < 2^30 only).
-__device__ __forceinline__ RunShape run_shape(const ChunkParams &p, int n, int w) {
-  const int total = p.nchains * n, L = (int)p.ho_len;
+__host__ __device__ inline RunShape run_shape(int nchains, int n, int L, int w) {
+  const int total = nchains * n;
   const int s = w * L, e = s + L < total ? s + L : total;
   RunShape r;
   r.c_lo = s / n;
@@ -181,27 +185,47 @@ __device__ __forceinline__ RunShape run_shape(const ChunkParams &p, int n, int w
   if (e <= s) r.count = 0;
   return r;
 }
+// Workgroups of the schedule: W runs, items of round k at k W .. k W + W - 1.
+__host__ __device__ inline int run_workers(int nchains, int n, int L) {
+  return (nchains * n + L - 1) / L;
+}
+// Item of workgroup `block`: chunks [c0, c1) of chain `chain` (chain < 0: the
+// run has no item in this round), role 1 = head (stores its state for run
+// w + 1), 2 = tail (takes the state run w - 1 stores), 0 = whole chain.  The
+// kernels and the host's schedule model both take their items from here.
+struct RunItem {
+  int chain, c0, c1, role, w;
+};
+__host__ __device__ inline RunItem run_item_at(int nchains, int n, int L, int block) {
+  const int W = run_workers(nchains, n, L);
+  const int k = block / W, w = block - k * W;
+  const RunShape rs = run_shape(nchains, n, L, w);
+  RunItem r;
+  r.w = w;
+  r.chain = -1;
+  r.c0 = r.c1 = 0;
+  r.role = 0;
+  if (k >= rs.count) return r;
+  const bool head = rs.head1 < n;
+  r.role = head && k == 0 ? 1 : (rs.tail0 > 0 && k == rs.count - 1) ? 2 : 0;
+  r.chain = r.role == 1 ? rs.c_hi : r.role == 2 ? rs.c_lo : rs.c_lo + (rs.tail0 > 0) + (k - (int)head);
+  r.c0 = r.role == 2 ? rs.tail0 : 0;
+  r.c1 = r.role == 1 ? rs.head1 : n;
+  return r;
+}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ ChunkItem run_item(const ChunkParams &p) {
   const int n = (p.seq_len + kC - 1) / kC;
-  const int L = (int)p.ho_len;
-  const int W = (p.nchains * n + L - 1) / L;
-  const int k = uniform((int)blockIdx.x / W);
-  const int w = uniform((int)blockIdx.x - k * W);
-  const RunShape rs = run_shape(p, n, w);
+  const RunItem it = run_item_at(p.nchains, n, (int)p.ho_len, (int)blockIdx.x);
   ChunkItem r;
   r.wait = nullptr;
   r.signal = nullptr;
-  r.skip = k >= uniform(rs.count);  // the run has fewer items than this round
+  r.poison = false;
+  r.skip = uniform(it.chain) < 0;  // the run has fewer items than this round
   if (r.skip) return r;
-  const bool head = rs.head1 < n;
-  // role: 1 = head, 2 = tail, 0 = whole chain
-  const int role = uniform(head && k == 0 ? 1 : (rs.tail0 > 0 && k == rs.count - 1) ? 2 : 0);
-  const int chain = uniform(role == 1 ? rs.c_hi
-                                      : role == 2 ? rs.c_lo
-                                                  : rs.c_lo + (rs.tail0 > 0) + (k - (int)head));
-  const int c0 = uniform(role == 2 ? rs.tail0 : 0);
-  const int c1 = uniform(role == 1 ? rs.head1 : n);
+  const int role = uniform(it.role), w = uniform(it.w);
+  const int chain = uniform(it.chain);
+  const int c0 = uniform(it.c0), c1 = uniform(it.c1);
   const int srank = chain / p.H;
   r.h = chain - srank * p.H;
   r.vs = 0;

@@ -66,6 +66,7 @@ struct Smem {
   bf16 v[64 * kLDK];           // v of the current chunk (rows = tokens, natural columns)
   float qtot[4][128];          // next chunk: sum of log2-decay over each 16-token quarter
   int flag[4];                 // next chunk: no positive log-decay in quarter pw
+  int handoff_arrived;         // the tail's hand-over flag was seen set
 };
 static_assert(sizeof(Buf) % 16 == 0, "buffer alignment");
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget exceeded");
@@ -618,7 +619,8 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[c2][ct][e] = itm.s0[(16 * ct + 4 * g4 + e) * kD + vcol + 16 * c2 + l16];
+          acc[c2][ct][e] = itm.poison ? __builtin_nanf("")
+                                      : itm.s0[(16 * ct + 4 * g4 + e) * kD + vcol + 16 * c2 + l16];
   } else {
     const float diag = itm.zero_v ? 1.f : 0.f;  // identity for the M tracker
 #pragma unroll
@@ -787,23 +789,32 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
 
 // State hand-over between the workgroups of the balanced schedule.  The head's
 // final state is stored by the consumer waves; every thread's release fence at
-// device scope, a barrier, then the flag.  The tail's reader polls the flag
-// (bounded: after ~2^22 polls it goes on, so every wave exits), then a barrier
-// and an acquire fence in every thread before the state is read.
+// device scope, a barrier, then the flag.  The tail's reader polls the flag, at
+// most p.ho_polls times so that every wave exits; then a barrier and an acquire
+// fence in every thread before the state is read.  A tail that gives up sets
+// KDA_DEVICE_HANDOFF_TIMEOUT in the GPU's status word and runs from a NaN state,
+// so its o rows and the chain's final state come out NaN instead of wrong.
 __device__ __forceinline__ void publish_state(int32_t *flag, int tid) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void await_state(const int32_t *flag, int tid) {
+__device__ __forceinline__ bool await_state(const ChunkParams &p, const int32_t *flag, int tid,
+                                            int *arrived) {
   if (tid == 0) {
-    for (int i = 0; i < (1 << 22); ++i) {
-      if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-      __builtin_amdgcn_s_sleep(8);
+    int ok = 0;
+    for (int i = 0; i < p.ho_polls && !ok; ++i) {
+      ok = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      if (!ok) __builtin_amdgcn_s_sleep(8);
     }
+    if (!ok && p.status)
+      __hip_atomic_fetch_or(p.status, (uint32_t)KDA_DEVICE_HANDOFF_TIMEOUT, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+    *arrived = ok;
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return *arrived != 0;
 }
 
 template <bool GATE>
@@ -820,9 +831,9 @@ __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
     sm.buf[b].pm[(32 * t + rr) * kLDC + skpos(32 * t + 16 + cc)] = (bf16)0.f;
   }
 
-  const ChunkItem itm = p.pass == kPassHandoff ? run_item(p) : decode_item(p, 1);
+  ChunkItem itm = p.pass == kPassHandoff ? run_item(p) : decode_item(p, 1);
   if (itm.skip) return;  // uniform: the whole workgroup
-  if (itm.wait) await_state(itm.wait, tid);
+  if (itm.wait) itm.poison = !await_state(p, itm.wait, tid, &sm.handoff_arrived);
   const int nblk = (int)((itm.len + kC - 1) / kC);
 
   // The two roles run separate loops with the same barriers (one before the

@@ -51,6 +51,18 @@ hipError_t no_alloc_scratch(void **addr);
 hipError_t launch_chunk_fwd(const kda_chunk_fwd_args &a, const ChunkPlan &plan,
                             hipStream_t stream);
 
+// Balanced schedule of C equal chains of n chunks on U compute units: whether
+// the prefill uses it, and if so its runs (ho_len, ho_workers, ho_rounds).
+bool balanced_schedule_applies(int64_t C, int64_t n, int U, ChunkPlan *pl);
+
+// The per-GPU status word (KDA_DEVICE_* bits) and the polls a tail workgroup of
+// the balanced schedule makes before giving up on its hand-over flag.
+constexpr int32_t kDefaultHandoffPolls = 1 << 22;
+hipError_t device_status_word(uint32_t **addr);
+hipError_t read_device_status(hipStream_t stream, bool clear, uint32_t *bits);
+int32_t handoff_poll_limit();
+void set_handoff_poll_limit(int32_t polls);
+
 // Chunked backward: workspace size and the three launches.
 size_t chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t heads);
 size_t chunk_bwd_min_workspace_bytes(const kda_chunk_bwd_args &a);

@@ -40,7 +40,9 @@
  *    a field says host).  The library allocates no device memory, keeps no
  *    pointer after a call returns and holds no mutable global state -- except
  *    the per-GPU scratch buffer of kda_chunk_fwd_no_alloc (a static device
- *    array reserved when the library is loaded).
+ *    array reserved when the library is loaded), the per-GPU device status
+ *    word (kda_device_status) and the process-wide hand-over poll limit
+ *    (kda_set_handoff_poll_limit).
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Work is enqueued asynchronously; no call synchronises the host.
  *  - Errors: arguments are validated on the host before anything is enqueued.
@@ -208,6 +210,56 @@ kda_status kda_chunk_fwd_no_alloc(const kda_chunk_fwd_args *args, void *stream);
 
 /* Size in bytes of the per-GPU buffer of kda_chunk_fwd_no_alloc. */
 size_t kda_chunk_fwd_no_alloc_max_workspace(void);
+
+/* ------------------------------------------------------------------------
+ * Failures detected on the device.  A kernel cannot return a status to the
+ * host call that enqueued it; what it detects it ORs into a status word the
+ * library keeps on each GPU, and it makes the affected outputs NaN.
+ *   KDA_DEVICE_HANDOFF_TIMEOUT: in the balanced schedule of kda_chunk_fwd, a
+ *     workgroup that continues a chain gave up waiting for the state of the
+ *     workgroup that began it (it polls its flag a bounded number of times so
+ *     that every wave exits).  That workgroup ran from a NaN state: its o rows
+ *     and the chain's final state are NaN.  The wait is on a workgroup
+ *     dispatched earlier that never waits itself, so it is not expected to
+ *     happen; it is reported rather than left to hang or to yield a silent
+ *     wrong state.
+ * ---------------------------------------------------------------------- */
+#define KDA_DEVICE_HANDOFF_TIMEOUT 0x1u
+
+/* Read the current GPU's status word in stream order: waits until the work
+ * enqueued on `stream` before the call has finished, then stores the bits set
+ * since the last clear in *bits (0 = no device-side failure).  With clear != 0
+ * the word is reset in the same atomic exchange.  Bits set by work on other
+ * streams appear once that work has run.  Errors: KDA_ERROR_INVALID_VALUE for a
+ * null `bits`; KDA_ERROR_LAUNCH when the runtime fails (bits untouched).
+ * Synchronises the host with `stream`; not for use under graph capture. */
+kda_status kda_device_status(void *stream, int32_t clear, uint32_t *bits);
+
+/* Polls of a hand-over flag before a workgroup of the balanced schedule gives
+ * up (default 4,194,304, several seconds; each poll is followed by a short
+ * sleep).  Process-wide; read when a prefill is enqueued.  0 makes every
+ * workgroup that continues a chain give up without polling: the failure path
+ * of KDA_DEVICE_HANDOFF_TIMEOUT, for tests.  Errors: KDA_ERROR_INVALID_VALUE
+ * for a negative count. */
+kda_status kda_set_handoff_poll_limit(int32_t polls);
+int32_t kda_handoff_poll_limit(void);
+
+/* The balanced schedule kda_chunk_fwd would use for a fixed-length batch of
+ * num_seqs sequences of seq_len tokens and num_heads heads in automatic mode
+ * (segments = 0, bf16) on a GPU with `compute_units` compute units -- host only,
+ * no GPU needed.  *count receives the number of workgroups of the launch (0 when
+ * the prefill would run whole chains instead).  If items is not NULL and
+ * capacity >= *count, items[5 i .. 5 i + 4] describe workgroup i in dispatch
+ * order: chain (sequence * num_heads + head, or -1 for a workgroup with no
+ * work), first chunk, end chunk (64-token chunks, end exclusive), role (0 =
+ * whole chain, 1 = begins a chain that another workgroup finishes, 2 = finishes
+ * a chain from the state of workgroup items[5 i + 4]), and that workgroup's
+ * index (-1 for roles 0 and 1).  Errors: KDA_ERROR_INVALID_VALUE for sizes
+ * below 1 (seq_len below 0), a null count, or a capacity below *count with
+ * items given (then *count is still set). */
+kda_status kda_balanced_schedule(int32_t num_seqs, int32_t seq_len, int32_t num_heads,
+                                 int32_t compute_units, int32_t *items, int64_t capacity,
+                                 int64_t *count);
 
 /* ------------------------------------------------------------------------
  * Chunked backward ([P1] "How KDA updates its state": the recurrence;
