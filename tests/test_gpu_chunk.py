@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import kda_inputs as ki
-from kda_testutil import TOL, announce, oracle_chains, rel_err, to64
+from kda_testutil import TOL, announce, check_prefill_chains, rel_err, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -34,17 +34,7 @@ def run(kda, inp, scale=1.0, varlen=True, **kw):
 
 
 def check_chains(inp, o, sf, chains, dtype, scale=1.0):
-    ref = oracle_chains(inp, chains, scale=scale)
-    cu = inp["cu_seqlens_host"]
-    worst_o = worst_s = 0.0
-    for (n, h), (o_ref, s_ref) in ref.items():
-        a, b = cu[n], cu[n + 1]
-        if b > a:
-            worst_o = max(worst_o, rel_err(to64(o[a:b, h]), o_ref))
-        worst_s = max(worst_s, rel_err(to64(sf[n, h]), s_ref))
-    print(f"  max rel err: o {worst_o:.3e}  S_final {worst_s:.3e}", flush=True)
-    assert worst_o <= TOL[dtype], worst_o
-    assert worst_s <= TOL[dtype], worst_s
+    check_prefill_chains(inp, o, sf, chains, dtype, scale=scale)
 
 
 def test_fp32_forward_b1_t256_h2(kda):

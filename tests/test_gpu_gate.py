@@ -13,7 +13,7 @@ import torch
 
 import kda_inputs as ki
 import oracle
-from kda_testutil import TOL, announce, oracle_chains, rel_err, to64
+from kda_testutil import TOL, announce, check_prefill_chains, rel_err, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -44,17 +44,7 @@ def run(kda, inp, gp, lower_bound=-5.0, gate=True, beta_logits=True, varlen=True
 
 
 def check(inp, fr, o, sf, chains, dtype, scale=1.0):
-    ref = oracle_chains(inp, chains, scale=scale, front=fr)
-    cu = inp["cu_seqlens_host"]
-    worst_o = worst_s = 0.0
-    for (n, h), (o_ref, s_ref) in ref.items():
-        a, b = cu[n], cu[n + 1]
-        if b > a:
-            worst_o = max(worst_o, rel_err(to64(o[a:b, h]), o_ref))
-        worst_s = max(worst_s, rel_err(to64(sf[n, h]), s_ref))
-    print(f"  max rel err: o {worst_o:.3e}  S_final {worst_s:.3e}", flush=True)
-    assert worst_o <= TOL[dtype], worst_o
-    assert worst_s <= TOL[dtype], worst_s
+    check_prefill_chains(inp, o, sf, chains, dtype, scale=scale, front=fr)
 
 
 # Gate parameter sets: "floor" puts many tokens near the bound (16-token windows),
