@@ -24,9 +24,16 @@
 // So the state is carried pre-scaled: the accumulator holds S' during a window
 // and is multiplied by 2^{G_end - Gm} 2^{Gm(next)} when the next one starts.
 // Every exponent is G_r - Gm or Gm - G_r, bounded by half the window's range of
-// G.  A chunk whose range exceeds 128 (2^64 either way) is processed as four
-// 16-token windows instead (under the pages' lower bound a 16-token range is at
-// most 115).
+// G.  A chunk whose range exceeds 128 (2^64 either way) needs one reference per
+// 16-token quarter instead (under the pages' lower bound a 16-token range is at
+// most 115).  With the gate front end such a chunk stays one window in quarter
+// mode: every quarter's operands use its own reference (its token 8), the Gram
+// tiles needed are the diagonal ones (quarters meet only through the state),
+// and the consumers take the window in four steps, quarter q from the state
+// after quarters 0 .. q-1 -- factors 2^{end_{q-1} - ref_{q-1}} 2^{ref_q} bring it
+// from one reference to the next.  With log-decay input it runs as four
+// 16-token windows, which need no second consumer path (registers are the
+// limit of the non-gate kernel).
 //
 // Workgroup of 8 waves, one (sequence, head) chain:
 //  * waves 4..7 (producers): per window, the elementwise work (decay factors,
@@ -69,6 +76,18 @@ struct Smem {
   int handoff_arrived;         // the tail's hand-over flag was seen set
 };
 static_assert(sizeof(Buf) % 16 == 0, "buffer alignment");
+
+// Quarter mode keeps six per-channel factor vectors in Lm's upper tiles, which
+// no mode writes otherwise: slot k = tile (0,1), (0,2), (0,3), (1,2), (1,3),
+// (2,3); channel c at float (c / 8) * (kLDC / 2) + c % 8 of its slot, so four
+// consecutive channels 4 m .. 4 m + 3 are one aligned 16-byte access.  Slots
+// 0..2 hold the end factors of quarters 0..2, slots 3..5 the reference factors
+// of quarters 1..3.
+__device__ __forceinline__ float *quarter_slot(Buf &B, int k) {
+  const int i = k < 3 ? 0 : (k < 5 ? 1 : 2);
+  const int j = k < 3 ? k + 1 : (k < 5 ? k - 1 : 3);
+  return reinterpret_cast<float *>(B.lm + 16 * i * kLDC + 16 * j);
+}
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget exceeded");
 static_assert(kLDK * 2 >= 128 * 2 + 16, "v rows need 16 spare bytes");
 
@@ -464,11 +483,17 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   block_sync();
   slow = !decide();
 
+  bool prev_quarters = false;  // the consumers run a quarter-mode window in this iteration
   for (int it = 0;; ++it) {
     Buf &B = sm.buf[it & 1];
     const Buf &Bprev = sm.buf[(it + 1) & 1];
+    const bool cur_quarters = GATE && blk < nblk && slow;
     const int Lc = (int)rows_of(blk);
-    const int nwin = slow ? (Lc + 15) / 16 : 1;
+    // A chunk too wide for one reference: with the gate front end, one window in
+    // quarter mode (each quarter, the rows of one wave, with its own reference);
+    // with log-decay input, four 16-token windows
+    const bool sixteen = !GATE && slow;
+    const int nwin = sixteen ? (Lc + 15) / 16 : 1;
     const bool last = win == nwin - 1;  // last window of the chunk
     // ====================== phase 1: operands of window it
     if (blk < nblk) {
@@ -476,12 +501,12 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
 #pragma unroll
         for (int j = 0; j < 4; ++j) Rb[j] = sigmoid_fast(Rb[j]);
       }
-      const int row_lo = slow ? 16 * win : 0;
-      const int row_hi = slow ? (16 * win + 16 < Lc ? 16 * win + 16 : Lc) : Lc;
+      const int row_lo = sixteen ? 16 * win : 0;
+      const int row_hi = sixteen ? (16 * win + 16 < Lc ? 16 * win + 16 : Lc) : Lc;
       // this window's reference and end per channel, relative to its start; the
       // lanes' offset to it (a 16-token window is quarter win, so only its wave
-      // holds its tokens)
-      const bool mine = !slow || pw == win;
+      // holds its tokens; in quarter mode every wave takes its own quarter's)
+      const bool mine = !sixteen || pw == win;
       float off[8], wref[8], wend[8];
       if (!slow) {
         if constexpr (GATE) {
@@ -505,19 +530,26 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
           off[i] = -wref[i];
         }
       }
-      const bool writer = (slow ? pw == win : pw == 0) && ts == 0;
+      // The reference factor 2^{ref} (times the previous window's end factor for
+      // the window's first reference) and the end factor 2^{end - ref}: one
+      // wave's lanes of co; in quarter mode wave q for its quarter, the factors
+      // that are not the window's first or last going to Lm's upper tiles
+      const bool quarters = GATE && slow;
+      const bool writer = ts == 0 && (quarters || (slow ? pw == win : pw == 0));
       if (writer) {
         f32x4 mf[2], po[2];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float prev = it > 0 ? Bprev.post[8 * co + i] : 1.f;
+          const float prev = (it > 0 && (!quarters || pw == 0)) ? Bprev.post[8 * co + i] : 1.f;
           mf[i >> 2][i & 3] = prev * fast_exp2(wref[i]);
           po[i >> 2][i & 3] = fast_exp2(wend[i] - wref[i]);
         }
-        *reinterpret_cast<f32x4 *>(B.mfac + 8 * co) = mf[0];
-        *reinterpret_cast<f32x4 *>(B.mfac + 8 * co + 4) = mf[1];
-        *reinterpret_cast<f32x4 *>(B.post + 8 * co) = po[0];
-        *reinterpret_cast<f32x4 *>(B.post + 8 * co + 4) = po[1];
+        float *md = (!quarters || pw == 0) ? B.mfac + 8 * co : quarter_slot(B, 2 + pw) + co * (kLDC / 2);
+        float *pd = (!quarters || pw == 3) ? B.post + 8 * co : quarter_slot(B, pw) + co * (kLDC / 2);
+        *reinterpret_cast<f32x4 *>(md) = mf[0];
+        *reinterpret_cast<f32x4 *>(md + 4) = mf[1];
+        *reinterpret_cast<f32x4 *>(pd) = po[0];
+        *reinterpret_cast<f32x4 *>(pd + 4) = po[1];
       }
       if (co == 0) {
 #pragma unroll
@@ -527,7 +559,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
         B.info[0] = row_lo;
         B.info[1] = row_hi;
         B.info[2] = blk * kC;
-        B.info[3] = 1;
+        B.info[3] = quarters ? 2 : 1;  // 2: quarter mode
       }
       // one window's operands; in a 16-token window the other waves write zeros
       auto operands = [&](bool keep) {
@@ -599,6 +631,12 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       }
     }
     block_sync();
+    if (prev_quarters) {
+      // the consumers' quarter steps 1..3 of the previous window
+#pragma unroll 1
+      for (int k = 0; k < 6; ++k) block_sync();
+    }
+    prev_quarters = cur_quarters;
     if (fresh) slow = !decide();
     if (!sm.buf[it & 1].info[3]) break;
   }
@@ -606,6 +644,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
 
 // ---------------------------------------------------------------- consumers
 // Consumer wave cw owns value columns 32 cw .. 32 cw + 31 of the state.
+template <bool GATE>
 __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkItem &itm,
                                               Smem &sm, const int cw, const int lane) {
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -633,142 +672,318 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   }
   block_sync();
 
-  // Window it - 1 in iteration it: Y and O^T products in the first phase, the
-  // substitution, state update and o stores in the second.
   int it = 0;
-  for (;; ++it) {
-    f32x4 accY[2][4], accOT[2][4];
-    // ====================== phase 1: Y and O^T products, one diagonal inverse
-    if (it > 0) {
+  if constexpr (GATE) {
+    // Window it - 1 in iteration it: Y and O^T products in the first phase, the
+    // substitution, state update and o stores in the second.  A quarter-mode
+    // window runs as four such steps, one per 16-token quarter q: step q brings
+    // the state after quarters 0 .. q-1 to quarter q's reference and does the
+    // work of row tile q alone (U_q = X_qq Y_q: the quarters meet only through
+    // the state); the producers pass the extra barriers idle.
+    for (;; ++it) {
+      f32x4 accY[2][4], accOT[2][4];
       Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
-      // bring the state to this window's scale
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const f32x4 m = *reinterpret_cast<const f32x4 *>(B.mfac + 16 * ct + 4 * g4);
-        acc[0][ct] *= m;
-        acc[1][ct] *= m;
-      }
-      Frag<bf16> sf[2][4];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], g4);
-      // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16])
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const bf16x4 v4 = lds_read_tr(sm.v + (16 * s4 + 4 * g4 + (l16 >> 2)) * kLDK + vcol +
-                                        16 * c2 + 4 * (l16 & 3));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
-          accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-      // O^T = S'^T Qr^T, sharing the S' fragments with Y
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          Frag<bf16> xb, xq;
-          lds_frag_ch(xb, B.nkr, 16 * s4 + l16, kk, g4);
-          lds_frag_ch(xq, B.qr, 16 * s4 + l16, kk, g4);
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            mma(accY[c2][s4], xb, sf[c2][kk]);
-            mma(accOT[c2][s4], sf[c2][kk], xq);
+      const bool quarters = it > 0 && B.info[3] == 2;
+      const int nstep = quarters ? 4 : 1;
+  #pragma unroll 1
+      for (int q = 0; q < nstep; ++q) {
+        const int t_lo = quarters ? q : 0, t_hi = quarters ? q + 1 : 4;  // row tiles of this step
+        // ====================== phase 1: Y and O^T products, one diagonal inverse
+        if (it > 0) {
+          // bring the state to this step's scale: the window's multiplier, or the
+          // end factor of quarter q - 1 times the reference factor of quarter q
+          if (q == 0) {
+  #pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+              const f32x4 m = *reinterpret_cast<const f32x4 *>(B.mfac + 16 * ct + 4 * g4);
+              acc[0][ct] *= m;
+              acc[1][ct] *= m;
+            }
+          } else {
+            const float *fe = quarter_slot(B, q - 1), *fr = quarter_slot(B, 2 + q);
+  #pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+              const int o = (2 * ct + (g4 >> 1)) * (kLDC / 2) + 4 * (g4 & 1);
+              const f32x4 m = *reinterpret_cast<const f32x4 *>(fe + o) *
+                              *reinterpret_cast<const f32x4 *>(fr + o);
+              acc[0][ct] *= m;
+              acc[1][ct] *= m;
+            }
           }
-        }
-      // diagonal block cw of the triangular system, for the next phase
-      inverse(B, cw, l16, g4);
-    }
-    block_sync();
-    // ====================== phase 2: U, O, state update, o stores
-    if (it > 0) {
-      Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
-      const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
-      // U = (I + beta A)^{-1} Y by block forward substitution:
-      //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
-      f32x4 accU[2][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int k = 0; k < i; ++k) {
-          Frag4<bf16> la;
-          lds_frag4(la, B.lm, kLDC, 16 * i + l16, 16 * k, g4);
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            Frag4<bf16> uk;
-            acc_frag4(uk, accU[c2][k]);
-            mma16(accY[c2][i], la, uk);
-          }
-        }
-        Frag4<bf16> xd;
-        lds_frag4(xd, B.lm, kLDC, 16 * i + l16, 16 * i, g4);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          Frag4<bf16> yi;
-          acc_frag4(yi, accY[c2][i]);
-          accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-          mma16(accU[c2][i], xd, yi);
-        }
-      }
-      Frag<bf16> uf[2][2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[c2][kk], accU[c2][2 * kk], accU[c2][2 * kk + 1]);
-      // O^T += U^T P^T     (lane holds O[16 rt + l16][vcol + 16 c2 + 4 g4 + e])
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          if (kk <= rt / 2) {
-            Frag<bf16> xp;
-            lds_frag_ck(xp, B.pm, kLDC, 16 * rt + l16, 32 * kk, g4);
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) mma(accOT[c2][rt], uf[c2][kk], xp);
-          }
-        }
-      // S' += Kc^T U   (Kc^T fragments by transposing loads of the row-major Kc)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16 *base = B.kc + chpos(16 * ct + 4 * (l16 & 3));
-          const int r0 = 32 * kk + 4 * g4 + (l16 >> 2);
-          const bf16x4 lo = lds_read_tr(base + r0 * kLDK);
-          const bf16x4 hi = lds_read_tr(base + (r0 + 16) * kLDK);
-          Frag<bf16> a;
-          a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
-        }
-      // o rows of this window: staged through this wave's own 32 columns of the
-      // window's nKr rows (read by no one after phase 1), so each store writes
-      // 64 contiguous bytes of a row
-      if (itm.write_o) {
-        bf16 *stage = B.nkr + vcol;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
+          Frag<bf16> sf[2][4];
+  #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2)
-            store4<bf16>(stage + (16 * rt + l16) * kLDK + 16 * c2 + 4 * g4, accOT[c2][rt] * p.scale);
-        const __amdgpu_buffer_rsrc_t ors = make_rsrc(
-            reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
-            (uint32_t)row_hi * (uint32_t)rowstride * 2u);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int r = 16 * k + l16;
-          const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
-          if (r >= row_lo)
-            buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
+  #pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], g4);
+          if (q == 0) {
+            // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16]);
+            // beta V of every tile now: the producers replace V in this step's phase 2
+  #pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
+  #pragma unroll
+              for (int c2 = 0; c2 < 2; ++c2) {
+                const bf16x4 v4 = lds_read_tr(sm.v + (16 * s4 + 4 * g4 + (l16 >> 2)) * kLDK + vcol +
+                                              16 * c2 + 4 * (l16 & 3));
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
+                accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+          }
+          // O^T = S'^T Qr^T, sharing the S' fragments with Y
+  #pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+  #pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              if (s4 < t_lo || s4 >= t_hi) continue;
+              Frag<bf16> xb, xq;
+              lds_frag_ch(xb, B.nkr, 16 * s4 + l16, kk, g4);
+              lds_frag_ch(xq, B.qr, 16 * s4 + l16, kk, g4);
+  #pragma unroll
+              for (int c2 = 0; c2 < 2; ++c2) {
+                mma(accY[c2][s4], xb, sf[c2][kk]);
+                mma(accOT[c2][s4], sf[c2][kk], xq);
+              }
+            }
+          // diagonal block cw of the triangular system, for the next phase
+          if (q == 0) inverse(B, cw, l16, g4);
+        }
+        block_sync();
+        // ====================== phase 2: U, O, state update, o stores
+        if (it > 0) {
+          const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
+          // U = (I + beta A)^{-1} Y by block forward substitution:
+          //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
+          // (quarter mode: U_q = X_qq Y_q, the other tiles zero)
+          f32x4 accU[2][4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (i < t_lo || i >= t_hi) {
+  #pragma unroll
+              for (int c2 = 0; c2 < 2; ++c2) accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+              continue;
+            }
+            if (!quarters) {
+  #pragma unroll
+              for (int k = 0; k < i; ++k) {
+                Frag4<bf16> la;
+                lds_frag4(la, B.lm, kLDC, 16 * i + l16, 16 * k, g4);
+  #pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                  Frag4<bf16> uk;
+                  acc_frag4(uk, accU[c2][k]);
+                  mma16(accY[c2][i], la, uk);
+                }
+              }
+            }
+            Frag4<bf16> xd;
+            lds_frag4(xd, B.lm, kLDC, 16 * i + l16, 16 * i, g4);
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              Frag4<bf16> yi;
+              acc_frag4(yi, accY[c2][i]);
+              accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+              mma16(accU[c2][i], xd, yi);
+            }
+          }
+          Frag<bf16> uf[2][2];
+  #pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2)
+  #pragma unroll
+            for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[c2][kk], accU[c2][2 * kk], accU[c2][2 * kk + 1]);
+          // O^T += U^T P^T     (lane holds O[16 rt + l16][vcol + 16 c2 + 4 g4 + e]);
+          // quarter mode: only the k-step holding tile q (the other U tiles are zero)
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+  #pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              if (rt < t_lo || rt >= t_hi) continue;
+              if (kk <= rt / 2 && (!quarters || kk == rt / 2)) {
+                Frag<bf16> xp;
+                lds_frag_ck(xp, B.pm, kLDC, 16 * rt + l16, 32 * kk, g4);
+  #pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) mma(accOT[c2][rt], uf[c2][kk], xp);
+              }
+            }
+          // S' += Kc^T U   (Kc^T fragments by transposing loads of the row-major Kc)
+  #pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+  #pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              if (quarters && kk != q / 2) continue;
+              const bf16 *base = B.kc + chpos(16 * ct + 4 * (l16 & 3));
+              const int r0 = 32 * kk + 4 * g4 + (l16 >> 2);
+              const bf16x4 lo = lds_read_tr(base + r0 * kLDK);
+              const bf16x4 hi = lds_read_tr(base + (r0 + 16) * kLDK);
+              Frag<bf16> a;
+              a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  #pragma unroll
+              for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
+            }
+          // o rows of this window, after its last step: staged through this wave's
+          // own 32 columns of the window's nKr rows (read by no one after the last
+          // phase 1), so each store writes 64 contiguous bytes of a row
+          if (itm.write_o && q == nstep - 1) {
+            bf16 *stage = B.nkr + vcol;
+  #pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+  #pragma unroll
+              for (int c2 = 0; c2 < 2; ++c2)
+                store4<bf16>(stage + (16 * rt + l16) * kLDK + 16 * c2 + 4 * g4, accOT[c2][rt] * p.scale);
+            const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+                reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
+                (uint32_t)row_hi * (uint32_t)rowstride * 2u);
+  #pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int r = 16 * k + l16;
+              const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
+              if (r >= row_lo)
+                buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
+            }
+          }
+        }
+        block_sync();
+      }
+      if (!sm.buf[it & 1].info[3]) break;
+    }
+  } else {
+    // Window it - 1 in iteration it: Y and O^T products in the first phase, the
+    // substitution, state update and o stores in the second.
+    for (;; ++it) {
+      f32x4 accY[2][4], accOT[2][4];
+      // ====================== phase 1: Y and O^T products, one diagonal inverse
+      if (it > 0) {
+        Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
+        // bring the state to this window's scale
+  #pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const f32x4 m = *reinterpret_cast<const f32x4 *>(B.mfac + 16 * ct + 4 * g4);
+          acc[0][ct] *= m;
+          acc[1][ct] *= m;
+        }
+        Frag<bf16> sf[2][4];
+  #pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+  #pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], g4);
+        // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16])
+  #pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
+  #pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const bf16x4 v4 = lds_read_tr(sm.v + (16 * s4 + 4 * g4 + (l16 >> 2)) * kLDK + vcol +
+                                          16 * c2 + 4 * (l16 & 3));
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
+            accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        // O^T = S'^T Qr^T, sharing the S' fragments with Y
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+  #pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            Frag<bf16> xb, xq;
+            lds_frag_ch(xb, B.nkr, 16 * s4 + l16, kk, g4);
+            lds_frag_ch(xq, B.qr, 16 * s4 + l16, kk, g4);
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              mma(accY[c2][s4], xb, sf[c2][kk]);
+              mma(accOT[c2][s4], sf[c2][kk], xq);
+            }
+          }
+        // diagonal block cw of the triangular system, for the next phase
+        inverse(B, cw, l16, g4);
+      }
+      block_sync();
+      // ====================== phase 2: U, O, state update, o stores
+      if (it > 0) {
+        Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
+        const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
+        // U = (I + beta A)^{-1} Y by block forward substitution:
+        //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
+        f32x4 accU[2][4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+  #pragma unroll
+          for (int k = 0; k < i; ++k) {
+            Frag4<bf16> la;
+            lds_frag4(la, B.lm, kLDC, 16 * i + l16, 16 * k, g4);
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              Frag4<bf16> uk;
+              acc_frag4(uk, accU[c2][k]);
+              mma16(accY[c2][i], la, uk);
+            }
+          }
+          Frag4<bf16> xd;
+          lds_frag4(xd, B.lm, kLDC, 16 * i + l16, 16 * i, g4);
+  #pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            Frag4<bf16> yi;
+            acc_frag4(yi, accY[c2][i]);
+            accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma16(accU[c2][i], xd, yi);
+          }
+        }
+        Frag<bf16> uf[2][2];
+  #pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+  #pragma unroll
+          for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[c2][kk], accU[c2][2 * kk], accU[c2][2 * kk + 1]);
+        // O^T += U^T P^T     (lane holds O[16 rt + l16][vcol + 16 c2 + 4 g4 + e])
+  #pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+  #pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            if (kk <= rt / 2) {
+              Frag<bf16> xp;
+              lds_frag_ck(xp, B.pm, kLDC, 16 * rt + l16, 32 * kk, g4);
+  #pragma unroll
+              for (int c2 = 0; c2 < 2; ++c2) mma(accOT[c2][rt], uf[c2][kk], xp);
+            }
+          }
+        // S' += Kc^T U   (Kc^T fragments by transposing loads of the row-major Kc)
+  #pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+  #pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16 *base = B.kc + chpos(16 * ct + 4 * (l16 & 3));
+            const int r0 = 32 * kk + 4 * g4 + (l16 >> 2);
+            const bf16x4 lo = lds_read_tr(base + r0 * kLDK);
+            const bf16x4 hi = lds_read_tr(base + (r0 + 16) * kLDK);
+            Frag<bf16> a;
+            a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
+          }
+        // o rows of this window: staged through this wave's own 32 columns of the
+        // window's nKr rows (read by no one after phase 1), so each store writes
+        // 64 contiguous bytes of a row
+        if (itm.write_o) {
+          bf16 *stage = B.nkr + vcol;
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+              store4<bf16>(stage + (16 * rt + l16) * kLDK + 16 * c2 + 4 * g4, accOT[c2][rt] * p.scale);
+          const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+              reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
+              (uint32_t)row_hi * (uint32_t)rowstride * 2u);
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int r = 16 * k + l16;
+            const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
+            if (r >= row_lo)
+              buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
+          }
         }
       }
+      block_sync();
+      if (!sm.buf[it & 1].info[3]) break;
     }
-    block_sync();
-    if (!sm.buf[it & 1].info[3]) break;
   }
 
   // final state S = 2^{G_end - Gm} S' of the last window
@@ -844,7 +1059,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_pipe_kernel(ChunkParams p) {
   if (w >= 4)
     producer_loop<GATE>(p, itm, sm, w - 4, lane, nblk);
   else
-    consumer_loop(p, itm, sm, w, lane);
+    consumer_loop<GATE>(p, itm, sm, w, lane);
   if (itm.signal) publish_state(itm.signal, tid);
 }
 

@@ -73,6 +73,23 @@ def test_prefill_gate_and_beta_logits_vs_oracle(kda, dtype, params):
     check(inp, front(gp, -5.0), o, sf, chains, inp["dtype"], scale=0.8)
 
 
+def test_prefill_gate_quarter_mode_boundaries(kda):
+    """The "floor" parameters put most decays near the bound, so chunks take one
+    reference per 16-token quarter (quarter mode: one window whose quarters the
+    consumer waves take in four steps).  Sequences end at, just before and just
+    after every quarter boundary, leaving quarters partly or wholly past the end."""
+    announce("gate prefill quarter mode boundaries")
+    lens = (1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 127, 128, 129, 200)
+    H = 2
+    cfg = ki.PrefillConfig("t", lens, H, "bf16", init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=61, gate_logits=True, beta_logits=True)
+    gp = ki.make_gate_params(H, device="cuda", seed=63, **GATE_PARAMS["floor"])
+    o, sf = run(kda, inp, gp)
+    torch.cuda.synchronize()
+    chains = [(n, h) for n in range(len(lens)) for h in range(H)]
+    check(inp, front(gp, -5.0), o, sf, chains, inp["dtype"])
+
+
 @pytest.mark.parametrize("lower_bound", [-2.5, 0.0])
 def test_prefill_gate_other_bounds_without_bias(kda, lower_bound):
     """Other bounds in the accepted range, no dt_bias, beta given directly."""
