@@ -213,11 +213,11 @@ def test_backward_fixed_batch_equals_varlen(kda):
         assert torch.equal(a[n], b[n]), n
 
 
-def test_backward_full_b4_t8192_h96_last_tokens(kda):
+def test_backward_full_b4_t8192_h96_whole_chains(kda):
     """The 4 x 8,192 x 96 bf16 workload's backward, in the launch the benchmark
-    times; the last 64 tokens of three chains checked against the oracle run from
-    the state the forward reaches at token 8,128 (exact for those tokens)."""
-    announce("chunk bwd full b4 t8192 h96")
+    times; three whole chains (every token's gradients) against the oracle's
+    reverse pass over the same 8,192 tokens."""
+    announce("chunk bwd full b4 t8192 h96 whole chains")
     cfg = ki.CONFIGS["kda_prefill_b4_t8192_h96_bf16"]
     inp = ki.make_prefill(cfg, device="cuda", seed=1002)
     T, H = inp["q"].shape[0], inp["heads"]
@@ -225,19 +225,15 @@ def test_backward_full_b4_t8192_h96_last_tokens(kda):
     dO = torch.randn((T, H, 128), generator=gen, device="cuda").to(torch.bfloat16)
     got = grads_gpu(kda, inp, dO, None, varlen=False)
     torch.cuda.synchronize()
-    tail = 64
-    for n, h in ((0, 0), (2, 41), (3, 95)):
-        a, b = n * 8192, (n + 1) * 8192
-        sl = lambda t: t[a:b - tail, h:h + 1]
-        _, s_mid = oracle.recurrent(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["g"]),
-                                    sl(inp["beta"]))
-        tl = lambda t: t[b - tail:b, h:h + 1]
-        ref = oracle.recurrent_bwd(tl(inp["q"]), tl(inp["k"]), tl(inp["v"]), tl(inp["g"]),
-                                   tl(inp["beta"]), tl(dO), initial_state=s_mid)
-        sub = {k: (v[b - tail:b, h:h + 1] if v is not None and k != "dinitial_state" else None)
-               for k, v in got.items()}
-        compare(sub, ref)
-    del inp, got
+    chains = ((0, 0), (2, 41), (3, 95))
+    # one oracle call over the three chains packed one after another
+    pack = lambda t: torch.cat([t[n * 8192:(n + 1) * 8192, h:h + 1] for n, h in chains])
+    cu = [0, 8192, 16384, 24576]
+    ref = oracle.recurrent_bwd(pack(inp["q"]), pack(inp["k"]), pack(inp["v"]), pack(inp["g"]),
+                               pack(inp["beta"]), pack(dO), cu_seqlens=cu)
+    sub = {k: (pack(v) if v is not None and k != "dinitial_state" else None) for k, v in got.items()}
+    compare(sub, ref)
+    del inp, got, ref
     torch.cuda.empty_cache()
 
 
@@ -255,12 +251,15 @@ def test_backward_b1_t256_h2_f32_whole(kda):
     compare(got, ref)
 
 
-def test_backward_t65536_h96_last_tokens(kda):
+def test_backward_t65536_h96_last_and_middle_tokens(kda):
     """One 65,536-token sequence, 96 heads, bf16, nonzero initial state, decay
-    floored at -5 (4,096 sub-chunks per chain in the serial passes); the last 64
+    floored at -5 (4,096 sub-chunks per chain in the serial passes).  The last 64
     tokens of two chains against the oracle run from the state the forward
-    reaches at token 65,472."""
-    announce("chunk bwd t65536 h96 last tokens")
+    reaches at token 65,472; and a middle window, tokens 32,768 .. 32,831 of one
+    chain, against the oracle run from the forward state at token 32,768 with
+    the state gradient the oracle's reverse pass over tokens 32,832 .. 65,535
+    brings back to token 32,832."""
+    announce("chunk bwd t65536 h96 last and middle tokens")
     cfg = ki.CONFIGS["kda_prefill_t65536_h96_bf16_s0_gclamp5"]
     inp = ki.make_prefill(cfg, device="cuda", seed=1003)
     T, H = inp["q"].shape[0], inp["heads"]
@@ -280,5 +279,18 @@ def test_backward_t65536_h96_last_tokens(kda):
         sub = {k: (v[T - tail:, h:h + 1] if v is not None and k != "dinitial_state" else None)
                for k, v in got.items()}
         compare(sub, ref)
+    # middle window
+    h, a, b = 5, 32768, 32832
+    rng = lambda t, lo, hi: t[lo:hi, h:h + 1]
+    args = lambda lo, hi: [rng(inp[n], lo, hi) for n in ("q", "k", "v", "g", "beta")]
+    s0 = inp["initial_state"][:, h:h + 1]
+    _, s_a = oracle.recurrent(*args(0, a), initial_state=s0)
+    _, s_b = oracle.recurrent(*args(a, b), initial_state=s_a)
+    back = oracle.recurrent_bwd(*args(b, T), rng(dO, b, T), initial_state=s_b)
+    ref = oracle.recurrent_bwd(*args(a, b), rng(dO, a, b), initial_state=s_a,
+                               dS_final=back["dS0"])
+    sub = {k: (v[a:b, h:h + 1] if v is not None and k != "dinitial_state" else None)
+           for k, v in got.items()}
+    compare(sub, ref)
     del inp, got
     torch.cuda.empty_cache()
