@@ -388,7 +388,8 @@ def cpu_baseline(x, seconds, gp=None):
 PREFILL_KERNEL = "chunk_fwd_pipe_kernel"
 PREFILL_SOURCES = ["gated_delta_rule_10_amd/csrc/kda_chunk_pipe.hip",
                    "gated_delta_rule_10_amd/csrc/kda_chunk_common.h",
-                   "gated_delta_rule_10_amd/csrc/kda_device.h"]
+                   "gated_delta_rule_10_amd/csrc/kda_device.h",
+                   "gated_delta_rule_10_amd/csrc/kda_pipe_layout.h"]
 TRAFFIC_NAMES = {
     "kda_prefill_varlen32_t1m_h96_bf16": "chunk_fwd_bf16_varlen32_t1m_h96",
     "kda_prefill_b4_t8192_h96_bf16": "chunk_fwd_bf16_b4_t8192_h96",

@@ -37,30 +37,32 @@
 //
 // Workgroup of 8 waves, one (sequence, head) chain:
 //  * waves 4..7 (producers): per window, the elementwise work (decay factors,
-//    scaled operands to LDS), the Gram products on matrix cores, the inverse of
-//    the four diagonal 16x16 blocks (Neumann product in registers); they run
+//    scaled operands to LDS) and the Gram products on matrix cores; they run
 //    one window ahead of
 //  * waves 0..3 (consumers): 32 value columns each of the fp32 state (matrix-core
-//    accumulators, never leaving registers): Y and O products, block forward
+//    accumulators, never leaving registers): Y and O products, the inverse of
+//    one diagonal 16x16 block each (Neumann product in registers), block forward
 //    substitution, the state update, and o stores.
 // Producer and consumer of the same SIMD overlap vector and matrix work; two
 // barriers per window.  Operands are double-buffered in LDS; matrix-core
 // operands whose contraction runs over tokens (Kc^T, V) are read with gfx950's
-// transposing LDS load, so every operand is stored once, row-major.
+// transposing LDS load, so every operand is stored once, row-major, in the
+// bank-conflict-free layouts of kda_pipe_layout.h.
 #include "kda_chunk_common.h"
 #include "kda_internal.h"
+#include "kda_pipe_layout.h"
 
 namespace kda {
 namespace {
 
-constexpr int kLDK = 136;            // operand row stride: 128 bf16 + 16 bytes
+using layout::kRow;                  // operand and v row stride: 128 bf16, no padding
 constexpr int kLDC = 72;             // 64-wide matrices (Lm, Pm): 64 bf16 + 16 bytes
 constexpr float kMaxHalf = 64.f;     // largest log2-decay over each 32-token half of a window
 
 struct Buf {                   // one window's operands
-  bf16 nkr[64 * kLDK];         // -beta k 2^{G - Gm}      rows = tokens, columns chpos
-  bf16 qr[64 * kLDK];          // q 2^{G - Gm}
-  bf16 kc[64 * kLDK];          // k 2^{Gm - G}
+  bf16 nkr[64 * kRow];         // -beta k 2^{G - Gm}      rows = tokens, at layout::opnd_at
+  bf16 qr[64 * kRow];          // q 2^{G - Gm}
+  bf16 kc[64 * kRow];          // k 2^{Gm - G}
   bf16 lm[64 * kLDC];          // -beta A below the diagonal blocks, X_ii on them
   bf16 pm[64 * kLDC];          // P (s <= r), columns skpos
   float beta[64];
@@ -70,7 +72,8 @@ struct Buf {                   // one window's operands
 };
 struct Smem {
   Buf buf[2];
-  bf16 v[64 * kLDK];           // v of the current chunk (rows = tokens, natural columns)
+  bf16 v[64 * kRow];           // v of the current chunk (rows = tokens, at layout::v_at)
+  float dt[128];               // the lower-bounded gate's dt_bias of the chain's head
   float qtot[4][128];          // next chunk: sum of log2-decay over each 16-token quarter
   int flag[4];                 // next chunk: no positive log-decay in quarter pw
   int handoff_arrived;         // the tail's hand-over flag was seen set
@@ -89,13 +92,10 @@ __device__ __forceinline__ float *quarter_slot(Buf &B, int k) {
   return reinterpret_cast<float *>(B.lm + 16 * i * kLDC + 16 * j);
 }
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget exceeded");
-static_assert(kLDK * 2 >= 128 * 2 + 16, "v rows need 16 spare bytes");
 
-// The 16 spare bytes at the end of each v row (never read as v) hold the
-// lower-bounded gate's dt_bias of the chain's head: channels 4 r .. 4 r + 3 in
-// row r < 32.
-__device__ __forceinline__ float *gate_dt_slot(Smem &sm, int r) {
-  return reinterpret_cast<float *>(sm.v + r * kLDK + 128);
+// The two 8-byte halves of a 16-byte read, exchanged where sw.
+__device__ __forceinline__ f32x4 swap_halves(const f32x4 &x, bool sw) {
+  return f32x4{sw ? x[2] : x[0], sw ? x[3] : x[1], sw ? x[0] : x[2], sw ? x[1] : x[3]};
 }
 
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
@@ -130,29 +130,19 @@ __device__ __forceinline__ void halves(float v, float &lower, float &upper) {
   upper = __uint_as_float(r[1]);
 }
 
-// Column order of the channel-indexed operands (nKr, Qr, Kc).  A matrix-core
-// fragment over channels 32 kk .. 32 kk + 31 holds, in lane group g, the quad
-// 4 g .. 4 g + 3 of the lower and of the upper 16 channels (the rows of two
-// state tiles); those 8 channels form one 16-byte chunk, chunk kk + 4 g of the
-// row, so a fragment is one 16-byte read.  In chunks with odd g the upper quad
-// comes first: then the transposing reads of Kc (8 rows x the 4 quads of a
-// 16-channel tile) and the producers' row stores touch every LDS bank once.
-__device__ __forceinline__ int chpos(int c) {
-  const int kk = c >> 5, h = (c >> 4) & 1, q = (c >> 2) & 3;
-  return 8 * (kk + 4 * q) + 4 * (h ^ (q & 1)) + (c & 3);
-}
-__device__ __forceinline__ void lds_frag_ch(Frag<bf16> &f, const bf16 *base, int row, int kk,
-                                            int g) {
-  f.v = *reinterpret_cast<const bf16x8 *>(base + row * kLDK + 8 * kk + 32 * g);
+// A fragment of an operand matrix (layout::opnd_at): rows 16 t + l16, lane group
+// g's chunk of channels 32 kk .. 32 kk + 31, at frag_step(f0, t, kk) for the
+// lane's f0 = frag_lane(l16, g).
+__device__ __forceinline__ void lds_frag_ch(Frag<bf16> &f, const bf16 *base, int f0, int t, int kk) {
+  f.v = *reinterpret_cast<const bf16x8 *>(base + layout::frag_step(f0, t, kk));
 }
 // The state fragment matching lds_frag_ch: tiles lo (channels 32 kk + 4 g + e)
-// and hi (+16), in the chunk's order.
-__device__ __forceinline__ void acc_frag_ch(Frag<bf16> &f, const f32x4 &lo, const f32x4 &hi, int g) {
+// and hi (+16), in the chunk's order (hi first where sw, for g = 2, 3).
+__device__ __forceinline__ void acc_frag_ch(Frag<bf16> &f, const f32x4 &lo, const f32x4 &hi, bool sw) {
   Frag<bf16> t;
   acc_frag_sk(t, lo, hi);
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t w = __builtin_bit_cast(u32x4_t, t.v);
-  const bool sw = g & 1;
   const u32x4_t r = {sw ? w[2] : w[0], sw ? w[3] : w[1], sw ? w[0] : w[2], sw ? w[1] : w[3]};
   f.v = __builtin_bit_cast(bf16x8, r);
 }
@@ -208,6 +198,7 @@ __device__ __forceinline__ void gram(Buf &B, int l16, int g4) {
   f32x4 acc[5];
 #pragma unroll
   for (int u = 0; u < 5; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int f0 = layout::frag_lane(l16, g4);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -215,8 +206,8 @@ __device__ __forceinline__ void gram(Buf &B, int l16, int g4) {
       const Job jb = kJobs[P][u];
       // lane holds [r = 16 i + l16][s = 16 j + 4 g4 + e]
       Frag<bf16> fx, fy;
-      lds_frag_ch(fx, B.kc, 16 * jb.j + l16, kk, g4);
-      lds_frag_ch(fy, jb.kind == 0 ? B.nkr : B.qr, 16 * jb.i + l16, kk, g4);
+      lds_frag_ch(fx, B.kc, f0, jb.j, kk);
+      lds_frag_ch(fy, jb.kind == 0 ? B.nkr : B.qr, f0, jb.i, kk);
       mma(acc[u], fx, fy);
     }
   }
@@ -308,7 +299,9 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   const int ts = lane >> 4, co = lane & 15;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int r0 = 16 * pw + 4 * ts;                    // this lane's first row in the chunk
-  const int pA = chpos(8 * co), pB = chpos(8 * co + 4);  // stored columns of the two channel quads
+  // the lane's two channel quads in row r0 (row r0 + j: layout::opnd_row_step)
+  const int pA = layout::opnd_at(r0, 8 * co), pB = layout::opnd_at(r0, 8 * co + 4);
+  const int pV = layout::v_at(r0, 8 * co);  // its v chunk in row r0
 
   u32x4 Rq[4], Rk[4], Rv[4];   // 8 bf16 channels per token
   f32x4 Rg[4][2];              // 8 fp32 channels per token
@@ -326,8 +319,8 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   const bf16 *vg = reinterpret_cast<const bf16 *>(p.v) + (int64_t)h * kD;
   const float *gg = p.g + (int64_t)h * kD;
   // gate constants: the head's factor, and the bias of this lane's channels in
-  // registers for the first chunk (later chunks read it from the v rows' spare
-  // bytes, so it holds no registers through the loop)
+  // registers for the first chunk (later chunks read it from sm.dt, so it holds
+  // no registers through the loop)
   float gate_a = 0.f, dt0[8];
   if constexpr (GATE) {
     gate_a = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
@@ -335,9 +328,8 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
 #pragma unroll
     for (int i = 0; i < 8; ++i) dt0[i] = p.dt_bias ? p.dt_bias[h * kD + 8 * co + i] : 0.f;
     if (pw == 0 && ts == 0) {
-      *reinterpret_cast<f32x4 *>(gate_dt_slot(sm, 2 * co)) = f32x4{dt0[0], dt0[1], dt0[2], dt0[3]};
-      *reinterpret_cast<f32x4 *>(gate_dt_slot(sm, 2 * co + 1)) =
-          f32x4{dt0[4], dt0[5], dt0[6], dt0[7]};
+      *reinterpret_cast<f32x4 *>(sm.dt + 8 * co) = f32x4{dt0[0], dt0[1], dt0[2], dt0[3]};
+      *reinterpret_cast<f32x4 *>(sm.dt + 8 * co + 4) = f32x4{dt0[4], dt0[5], dt0[6], dt0[7]};
     }
   }
   const uint32_t voff_b16 = (uint32_t)r0 * row_b16 + 16u * co;
@@ -565,7 +557,6 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       auto operands = [&](bool keep) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = r0 + j;
           const float nb = -Rb[j];
           const u32x4 kr = keep ? Rk[j] : u32x4{0u, 0u, 0u, 0u};
           const u32x4 qr = keep ? Rq[j] : u32x4{0u, 0u, 0u, 0u};
@@ -581,12 +572,13 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
             b[i] = qv * e1;
             c[i] = kv * e2;
           }
-          store4<bf16>(B.nkr + r * kLDK + pA, f32x4{a[0], a[1], a[2], a[3]});
-          store4<bf16>(B.nkr + r * kLDK + pB, f32x4{a[4], a[5], a[6], a[7]});
-          store4<bf16>(B.qr + r * kLDK + pA, f32x4{b[0], b[1], b[2], b[3]});
-          store4<bf16>(B.qr + r * kLDK + pB, f32x4{b[4], b[5], b[6], b[7]});
-          store4<bf16>(B.kc + r * kLDK + pA, f32x4{c[0], c[1], c[2], c[3]});
-          store4<bf16>(B.kc + r * kLDK + pB, f32x4{c[4], c[5], c[6], c[7]});
+          const int oA = layout::opnd_row_step(pA, j), oB = layout::opnd_row_step(pB, j);
+          store4<bf16>(B.nkr + oA, f32x4{a[0], a[1], a[2], a[3]});
+          store4<bf16>(B.nkr + oB, f32x4{a[4], a[5], a[6], a[7]});
+          store4<bf16>(B.qr + oA, f32x4{b[0], b[1], b[2], b[3]});
+          store4<bf16>(B.qr + oB, f32x4{b[4], b[5], b[6], b[7]});
+          store4<bf16>(B.kc + oA, f32x4{c[0], c[1], c[2], c[3]});
+          store4<bf16>(B.kc + oB, f32x4{c[4], c[5], c[6], c[7]});
         }
       };
       if (!slow)
@@ -612,13 +604,13 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
         // were in the phase before the last barrier)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<u32x4 *>(sm.v + (r0 + j) * kLDK + 8 * co) = Rv[j];
+          *reinterpret_cast<u32x4 *>(sm.v + layout::v_row_step(pV, j)) = Rv[j];
       }
     }
     issue_v(blk + 1);  // v of the next chunk (written at its first window)
     if (blk < nblk && last && blk + 1 < nblk)  // read after the barrier
       digest_g((int)rows_of(blk + 1),
-               [&](int i) { return gate_dt_slot(sm, 2 * co + (i >> 2))[i & 3]; });
+               [&](int i) { return sm.dt[8 * co + i]; });
     issue_g(blk < nblk && last ? blk + 2 : blk + 1);
     bool fresh = false;  // a new chunk starts at the next window
     if (blk < nblk) {
@@ -650,6 +642,15 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   const int l16 = lane & 15, g4 = lane >> 4;
   const int vcol = 32 * cw;
   const int64_t rowstride = (int64_t)p.H * kD;
+  // lane offsets in the LDS layouts: operand fragments (whose chunks hold the
+  // upper tile's quad first where fsw), the transposing reads of Kc and v, the
+  // o staging stores and reads (quads swapped where ssw)
+  const int f0 = layout::frag_lane(l16, g4);
+  const bool fsw = (g4 >> 1) & 1;
+  const int kt0 = layout::kc_tr_lane(l16, g4);
+  const int vt0 = layout::v_tr_lane(l16, g4, vcol);
+  const int sw0 = layout::stage_w_lane(l16, g4), sr0 = layout::stage_r_lane(l16, g4);
+  const bool ssw = layout::stage_swapped(l16);
   f32x4 acc[2][8];  // acc[c2][ct] = S'[16 ct + 4 g4 + e][vcol + 16 c2 + l16]
   if (itm.s0) {
 #pragma unroll
@@ -714,7 +715,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2)
   #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], g4);
+            for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], fsw);
           if (q == 0) {
             // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16]);
             // beta V of every tile now: the producers replace V in this step's phase 2
@@ -723,8 +724,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
               const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
   #pragma unroll
               for (int c2 = 0; c2 < 2; ++c2) {
-                const bf16x4 v4 = lds_read_tr(sm.v + (16 * s4 + 4 * g4 + (l16 >> 2)) * kLDK + vcol +
-                                              16 * c2 + 4 * (l16 & 3));
+                const bf16x4 v4 = lds_read_tr(sm.v + layout::v_tr_step(vt0, s4, c2));
   #pragma unroll
                 for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
                 accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -738,8 +738,8 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
             for (int s4 = 0; s4 < 4; ++s4) {
               if (s4 < t_lo || s4 >= t_hi) continue;
               Frag<bf16> xb, xq;
-              lds_frag_ch(xb, B.nkr, 16 * s4 + l16, kk, g4);
-              lds_frag_ch(xq, B.qr, 16 * s4 + l16, kk, g4);
+              lds_frag_ch(xb, B.nkr, f0, s4, kk);
+              lds_frag_ch(xq, B.qr, f0, s4, kk);
   #pragma unroll
               for (int c2 = 0; c2 < 2; ++c2) {
                 mma(accY[c2][s4], xb, sf[c2][kk]);
@@ -812,32 +812,31 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
               if (quarters && kk != q / 2) continue;
-              const bf16 *base = B.kc + chpos(16 * ct + 4 * (l16 & 3));
-              const int r0 = 32 * kk + 4 * g4 + (l16 >> 2);
-              const bf16x4 lo = lds_read_tr(base + r0 * kLDK);
-              const bf16x4 hi = lds_read_tr(base + (r0 + 16) * kLDK);
+              const bf16x4 lo = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, kk, 0));
+              const bf16x4 hi = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, kk, 1));
               Frag<bf16> a;
               a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   #pragma unroll
               for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
             }
           // o rows of this window, after its last step: staged through this wave's
-          // own 32 columns of the window's nKr rows (read by no one after the last
-          // phase 1), so each store writes 64 contiguous bytes of a row
+          // own 16 rows of the window's nKr (read by no one after the last phase 1;
+          // layout::stage_at), so each store writes 64 contiguous bytes of a row
           if (itm.write_o && q == nstep - 1) {
-            bf16 *stage = B.nkr + vcol;
+            bf16 *stage = B.nkr + 16 * kRow * cw;
   #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
   #pragma unroll
               for (int c2 = 0; c2 < 2; ++c2)
-                store4<bf16>(stage + (16 * rt + l16) * kLDK + 16 * c2 + 4 * g4, accOT[c2][rt] * p.scale);
+                store4<bf16>(stage + layout::stage_w_step(sw0, rt, c2), accOT[c2][rt] * p.scale);
             const __amdgpu_buffer_rsrc_t ors = make_rsrc(
                 reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
                 (uint32_t)row_hi * (uint32_t)rowstride * 2u);
   #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int r = 16 * k + l16;
-              const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
+              const f32x4 val =
+                  swap_halves(*reinterpret_cast<const f32x4 *>(stage + layout::stage_r_step(sr0, k)), ssw);
               if (r >= row_lo)
                 buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
             }
@@ -866,15 +865,14 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
   #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], g4);
+          for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], fsw);
         // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16])
   #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
   #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            const bf16x4 v4 = lds_read_tr(sm.v + (16 * s4 + 4 * g4 + (l16 >> 2)) * kLDK + vcol +
-                                          16 * c2 + 4 * (l16 & 3));
+            const bf16x4 v4 = lds_read_tr(sm.v + layout::v_tr_step(vt0, s4, c2));
   #pragma unroll
             for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
             accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -886,8 +884,8 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   #pragma unroll
           for (int s4 = 0; s4 < 4; ++s4) {
             Frag<bf16> xb, xq;
-            lds_frag_ch(xb, B.nkr, 16 * s4 + l16, kk, g4);
-            lds_frag_ch(xq, B.qr, 16 * s4 + l16, kk, g4);
+            lds_frag_ch(xb, B.nkr, f0, s4, kk);
+            lds_frag_ch(xq, B.qr, f0, s4, kk);
   #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
               mma(accY[c2][s4], xb, sf[c2][kk]);
@@ -950,32 +948,31 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
         for (int ct = 0; ct < 8; ++ct)
   #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            const bf16 *base = B.kc + chpos(16 * ct + 4 * (l16 & 3));
-            const int r0 = 32 * kk + 4 * g4 + (l16 >> 2);
-            const bf16x4 lo = lds_read_tr(base + r0 * kLDK);
-            const bf16x4 hi = lds_read_tr(base + (r0 + 16) * kLDK);
+            const bf16x4 lo = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, kk, 0));
+            const bf16x4 hi = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, kk, 1));
             Frag<bf16> a;
             a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
           }
-        // o rows of this window: staged through this wave's own 32 columns of the
-        // window's nKr rows (read by no one after phase 1), so each store writes
-        // 64 contiguous bytes of a row
+        // o rows of this window: staged through this wave's own 16 rows of the
+        // window's nKr (read by no one after phase 1; layout::stage_at), so each
+        // store writes 64 contiguous bytes of a row
         if (itm.write_o) {
-          bf16 *stage = B.nkr + vcol;
+          bf16 *stage = B.nkr + 16 * kRow * cw;
   #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
   #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2)
-              store4<bf16>(stage + (16 * rt + l16) * kLDK + 16 * c2 + 4 * g4, accOT[c2][rt] * p.scale);
+              store4<bf16>(stage + layout::stage_w_step(sw0, rt, c2), accOT[c2][rt] * p.scale);
           const __amdgpu_buffer_rsrc_t ors = make_rsrc(
               reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
               (uint32_t)row_hi * (uint32_t)rowstride * 2u);
   #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int r = 16 * k + l16;
-            const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + r * kLDK + 8 * g4);
+            const f32x4 val =
+                swap_halves(*reinterpret_cast<const f32x4 *>(stage + layout::stage_r_step(sr0, k)), ssw);
             if (r >= row_lo)
               buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
           }
