@@ -27,13 +27,17 @@
 // G.  A chunk whose range exceeds 128 (2^64 either way) needs one reference per
 // 16-token quarter instead (under the pages' lower bound a 16-token range is at
 // most 115).  With the gate front end such a chunk stays one window in quarter
-// mode: every quarter's operands use its own reference (its token 8), the Gram
-// tiles needed are the diagonal ones (quarters meet only through the state),
-// and the consumers take the window in four steps, quarter q from the state
-// after quarters 0 .. q-1 -- factors 2^{end_{q-1} - ref_{q-1}} 2^{ref_q} bring it
-// from one reference to the next.  With log-decay input it runs as four
-// 16-token windows, which need no second consumer path (registers are the
-// limit of the non-gate kernel).
+// mode: every quarter's operands use its own reference Gm_q (its token 8); the
+// Gram tile of quarters (i, j), i > j, scales quarter j's Kc by
+// 2^{Gm_i - Gm_j} <= 1 per channel, so it pairs both at quarter i's reference
+// and holds the entries of the definition; quarter q's Y and O rows use the
+// window-start state at quarter q's reference (S' times 2^{Gm_q - Gm_0}); the
+// substitution and P U run over all tiles as in a one-reference window; and the
+// state update takes the quarters in order, moving the state by
+// 2^{Gm_q - Gm_{q-1}} before adding quarter q's Kc^T U.  Every factor is at most
+// 1 (a decay), so nothing overflows; what underflows is negligible against the
+// terms it is added to.  With log-decay input such a chunk runs as four 16-token
+// windows instead (registers are the limit of the non-gate kernel).
 //
 // Workgroup of 8 waves, one (sequence, head) chain:
 //  * waves 4..7 (producers): per window, the elementwise work (decay factors,
@@ -75,21 +79,27 @@ struct Smem {
   bf16 v[64 * kRow];           // v of the current chunk (rows = tokens, at layout::v_at)
   float dt[128];               // the lower-bounded gate's dt_bias of the chain's head
   float qtot[4][128];          // next chunk: sum of log2-decay over each 16-token quarter
+  float qref[4][128];          // next chunk: log2-decay from each quarter's start to its token 8
   int flag[4];                 // next chunk: no positive log-decay in quarter pw
   int handoff_arrived;         // the tail's hand-over flag was seen set
 };
 static_assert(sizeof(Buf) % 16 == 0, "buffer alignment");
 
-// Quarter mode keeps six per-channel factor vectors in Lm's upper tiles, which
-// no mode writes otherwise: slot k = tile (0,1), (0,2), (0,3), (1,2), (1,3),
-// (2,3); channel c at float (c / 8) * (kLDC / 2) + c % 8 of its slot, so four
-// consecutive channels 4 m .. 4 m + 3 are one aligned 16-byte access.  Slots
-// 0..2 hold the end factors of quarters 0..2, slots 3..5 the reference factors
-// of quarters 1..3.
+// Quarter mode keeps per-channel factor vectors in Lm's upper tiles, which no
+// mode writes otherwise: slot k = tile (0,1), (0,2), (0,3), (1,2), (1,3), (2,3);
+// channel c at float (c / 8) * (kLDC / 2) + c % 8 of its slot, so four
+// consecutive channels 4 m .. 4 m + 3 are one aligned 16-byte access
+// (quarter_off).  With Gm_q the log2-decay at quarter q's reference (its token
+// 8): slots 0..2 hold r_q = 2^{Gm_{q+1} - Gm_q}, slots 3 and 4 hold
+// d_q = 2^{Gm_q - Gm_0} for q = 2, 3 (d_1 = r_0); all are at most 1.
 __device__ __forceinline__ float *quarter_slot(Buf &B, int k) {
   const int i = k < 3 ? 0 : (k < 5 ? 1 : 2);
   const int j = k < 3 ? k + 1 : (k < 5 ? k - 1 : 3);
   return reinterpret_cast<float *>(B.lm + 16 * i * kLDC + 16 * j);
+}
+// Float offset within a slot of channels 16 ct + 4 g4 .. 16 ct + 4 g4 + 3.
+__device__ __forceinline__ int quarter_off(int ct, int g4) {
+  return (2 * ct + (g4 >> 1)) * (kLDC / 2) + 4 * (g4 & 1);
 }
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget exceeded");
 
@@ -192,9 +202,29 @@ __device__ constexpr Job kJobs[4][5] = {
     {{0, 1, 1}, {1, 1, 1}, {0, 2, 1}, {1, 2, 1}, {0, 3, 1}},
     {{0, 2, 2}, {1, 2, 2}, {1, 3, 1}, {0, 3, 2}, {1, 3, 2}}};
 
+// A Kc fragment of quarter j (channels 32 kk + 4 g4 + e of the lower and
+// 32 kk + 16 + 4 g4 + e of the upper tile, in the chunk's order) times
+// e_ij = r_j .. r_{i-1} = 2^{Gm_i - Gm_j} <= 1 per channel: in a quarter-mode
+// window, Gram tile (i, j) below the diagonal then pairs quarter i's rows with
+// quarter j's columns at quarter i's reference, and its entries are those of
+// the definition (no factor exceeds 1, so nothing overflows).
+__device__ __forceinline__ void scale_cross(Frag<bf16> &f, Buf &B, int i, int j, int kk, int g4) {
+  const bool hi_first = (g4 >> 1) & 1;
+  const int o0 = quarter_off(2 * kk + (hi_first ? 1 : 0), g4);
+  const int o1 = quarter_off(2 * kk + (hi_first ? 0 : 1), g4);
+  f32x4 e0 = f32x4{1.f, 1.f, 1.f, 1.f}, e1 = e0;
+  for (int t = j; t < i; ++t) {
+    const float *r = quarter_slot(B, t);
+    e0 *= *reinterpret_cast<const f32x4 *>(r + o0);
+    e1 *= *reinterpret_cast<const f32x4 *>(r + o1);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)((float)f.v[e] * (e < 4 ? e0[e] : e1[e - 4]));
+}
+
 // Gram products of one window: -beta A into Lm and P into Pm.
 template <int P>
-__device__ __forceinline__ void gram(Buf &B, int l16, int g4) {
+__device__ __forceinline__ void gram(Buf &B, int l16, int g4, bool quarters) {
   f32x4 acc[5];
 #pragma unroll
   for (int u = 0; u < 5; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -208,6 +238,7 @@ __device__ __forceinline__ void gram(Buf &B, int l16, int g4) {
       Frag<bf16> fx, fy;
       lds_frag_ch(fx, B.kc, f0, jb.j, kk);
       lds_frag_ch(fy, jb.kind == 0 ? B.nkr : B.qr, f0, jb.i, kk);
+      if (jb.i > jb.j && quarters) scale_cross(fx, B, jb.i, jb.j, kk, g4);
       mma(acc[u], fx, fy);
     }
   }
@@ -415,6 +446,12 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       *reinterpret_cast<f32x4 *>(&sm.qtot[pw][8 * co]) = f32x4{y[0], y[1], y[2], y[3]};
       *reinterpret_cast<f32x4 *>(&sm.qtot[pw][8 * co + 4]) = f32x4{y[4], y[5], y[6], y[7]};
     }
+    if constexpr (GATE) {
+      if (ts == 2) {  // the quarter's token 8: its reference in quarter mode
+        *reinterpret_cast<f32x4 *>(&sm.qref[pw][8 * co]) = f32x4{Gl[0][0], Gl[0][1], Gl[0][2], Gl[0][3]};
+        *reinterpret_cast<f32x4 *>(&sm.qref[pw][8 * co + 4]) = f32x4{Gl[0][4], Gl[0][5], Gl[0][6], Gl[0][7]};
+      }
+    }
     const bool wave_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
     if (lane == 0) sm.flag[pw] = wave_ok ? 1 : 0;
   };
@@ -475,11 +512,9 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
   block_sync();
   slow = !decide();
 
-  bool prev_quarters = false;  // the consumers run a quarter-mode window in this iteration
   for (int it = 0;; ++it) {
     Buf &B = sm.buf[it & 1];
     const Buf &Bprev = sm.buf[(it + 1) & 1];
-    const bool cur_quarters = GATE && blk < nblk && slow;
     const int Lc = (int)rows_of(blk);
     // A chunk too wide for one reference: with the gate front end, one window in
     // quarter mode (each quarter, the rows of one wave, with its own reference);
@@ -522,26 +557,52 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
           off[i] = -wref[i];
         }
       }
-      // The reference factor 2^{ref} (times the previous window's end factor for
-      // the window's first reference) and the end factor 2^{end - ref}: one
-      // wave's lanes of co; in quarter mode wave q for its quarter, the factors
-      // that are not the window's first or last going to Lm's upper tiles
+      // The reference factor 2^{ref} (times the previous window's end factor) and
+      // the end factor 2^{end - ref}: one wave's lanes of co.  In quarter mode
+      // wave 0 writes the first, wave 3 the second, and wave q >= 1 the factors
+      // r_{q-1} (previous quarter's reference to its own) and, q >= 2, d_q
+      // (quarter 0's reference to its own) into Lm's upper tiles, from the
+      // quarter totals and token-8 offsets of the digest
       const bool quarters = GATE && slow;
       const bool writer = ts == 0 && (quarters || (slow ? pw == win : pw == 0));
       if (writer) {
-        f32x4 mf[2], po[2];
+        if (!quarters || pw == 0) {
+          f32x4 mf[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float prev = (it > 0 && (!quarters || pw == 0)) ? Bprev.post[8 * co + i] : 1.f;
-          mf[i >> 2][i & 3] = prev * fast_exp2(wref[i]);
-          po[i >> 2][i & 3] = fast_exp2(wend[i] - wref[i]);
+          for (int i = 0; i < 8; ++i) {
+            const float prev = it > 0 ? Bprev.post[8 * co + i] : 1.f;
+            mf[i >> 2][i & 3] = prev * fast_exp2(wref[i]);
+          }
+          *reinterpret_cast<f32x4 *>(B.mfac + 8 * co) = mf[0];
+          *reinterpret_cast<f32x4 *>(B.mfac + 8 * co + 4) = mf[1];
         }
-        float *md = (!quarters || pw == 0) ? B.mfac + 8 * co : quarter_slot(B, 2 + pw) + co * (kLDC / 2);
-        float *pd = (!quarters || pw == 3) ? B.post + 8 * co : quarter_slot(B, pw) + co * (kLDC / 2);
-        *reinterpret_cast<f32x4 *>(md) = mf[0];
-        *reinterpret_cast<f32x4 *>(md + 4) = mf[1];
-        *reinterpret_cast<f32x4 *>(pd) = po[0];
-        *reinterpret_cast<f32x4 *>(pd + 4) = po[1];
+        if (!quarters || pw == 3) {
+          f32x4 po[2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) po[i >> 2][i & 3] = fast_exp2(wend[i] - wref[i]);
+          *reinterpret_cast<f32x4 *>(B.post + 8 * co) = po[0];
+          *reinterpret_cast<f32x4 *>(B.post + 8 * co + 4) = po[1];
+        }
+        if (GATE && quarters && pw > 0) {
+          f32x4 rr[2], dd[2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int c = 8 * co + i;
+            float before = 0.f;  // log2-decay of quarters 0 .. pw - 1
+#pragma unroll
+            for (int t = 0; t < 3; ++t) before += t < pw ? sm.qtot[t][c] : 0.f;
+            rr[i >> 2][i & 3] = fast_exp2(sm.qtot[pw - 1][c] - sm.qref[pw - 1][c] + wref[i]);
+            dd[i >> 2][i & 3] = fast_exp2(before + wref[i] - sm.qref[0][c]);
+          }
+          float *rd = quarter_slot(B, pw - 1) + co * (kLDC / 2);
+          *reinterpret_cast<f32x4 *>(rd) = rr[0];
+          *reinterpret_cast<f32x4 *>(rd + 4) = rr[1];
+          if (pw >= 2) {
+            float *dq = quarter_slot(B, pw + 1) + co * (kLDC / 2);
+            *reinterpret_cast<f32x4 *>(dq) = dd[0];
+            *reinterpret_cast<f32x4 *>(dq + 4) = dd[1];
+          }
+        }
       }
       if (co == 0) {
 #pragma unroll
@@ -593,11 +654,12 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     block_sync();
     // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
+      const bool quarters = GATE && slow;
       switch (pw) {
-        case 0: gram<0>(B, l16, g4); break;
-        case 1: gram<1>(B, l16, g4); break;
-        case 2: gram<2>(B, l16, g4); break;
-        default: gram<3>(B, l16, g4); break;
+        case 0: gram<0>(B, l16, g4, quarters); break;
+        case 1: gram<1>(B, l16, g4, quarters); break;
+        case 2: gram<2>(B, l16, g4, quarters); break;
+        default: gram<3>(B, l16, g4, quarters); break;
       }
       if (win == 0) {
         // v of this chunk for the consumers (their reads of the previous chunk's v
@@ -623,12 +685,6 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       }
     }
     block_sync();
-    if (prev_quarters) {
-      // the consumers' quarter steps 1..3 of the previous window
-#pragma unroll 1
-      for (int k = 0; k < 6; ++k) block_sync();
-    }
-    prev_quarters = cur_quarters;
     if (fresh) slow = !decide();
     if (!sm.buf[it & 1].info[3]) break;
   }
@@ -674,210 +730,75 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   block_sync();
 
   int it = 0;
-  if constexpr (GATE) {
-    // Window it - 1 in iteration it: Y and O^T products in the first phase, the
-    // substitution, state update and o stores in the second.  A quarter-mode
-    // window runs as four such steps, one per 16-token quarter q: step q brings
-    // the state after quarters 0 .. q-1 to quarter q's reference and does the
-    // work of row tile q alone (U_q = X_qq Y_q: the quarters meet only through
-    // the state); the producers pass the extra barriers idle.
-    for (;; ++it) {
-      f32x4 accY[2][4], accOT[2][4];
+  // Window it - 1 in iteration it: Y and O^T products in the first phase, the
+  // substitution, state update and o stores in the second.  A quarter-mode
+  // window (gate front end only) keeps one reference per 16-token quarter: its
+  // Y and O^T rows of quarter q use the window-start state at quarter q's
+  // reference (S' times d_q), the substitution and P U run over all tiles as
+  // usual (the producers scale the cross-quarter Gram tiles), and the state
+  // update walks the quarters, moving the state from one reference to the next
+  // (factor r_q) before adding quarter q + 1's K^T U.
+  for (;; ++it) {
+    f32x4 accY[2][4], accOT[2][4];
+    // ====================== phase 1: Y and O^T products, one diagonal inverse
+    if (it > 0) {
       Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
-      const bool quarters = it > 0 && B.info[3] == 2;
-      const int nstep = quarters ? 4 : 1;
-  #pragma unroll 1
-      for (int q = 0; q < nstep; ++q) {
-        const int t_lo = quarters ? q : 0, t_hi = quarters ? q + 1 : 4;  // row tiles of this step
-        // ====================== phase 1: Y and O^T products, one diagonal inverse
-        if (it > 0) {
-          // bring the state to this step's scale: the window's multiplier, or the
-          // end factor of quarter q - 1 times the reference factor of quarter q
-          if (q == 0) {
+      const bool quarters = GATE && __builtin_amdgcn_readfirstlane(B.info[3]) == 2;  // wave-uniform
+      // bring the state to this window's scale
   #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-              const f32x4 m = *reinterpret_cast<const f32x4 *>(B.mfac + 16 * ct + 4 * g4);
-              acc[0][ct] *= m;
-              acc[1][ct] *= m;
-            }
-          } else {
-            const float *fe = quarter_slot(B, q - 1), *fr = quarter_slot(B, 2 + q);
+      for (int ct = 0; ct < 8; ++ct) {
+        const f32x4 m = *reinterpret_cast<const f32x4 *>(B.mfac + 16 * ct + 4 * g4);
+        acc[0][ct] *= m;
+        acc[1][ct] *= m;
+      }
+      // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16])
   #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-              const int o = (2 * ct + (g4 >> 1)) * (kLDC / 2) + 4 * (g4 & 1);
-              const f32x4 m = *reinterpret_cast<const f32x4 *>(fe + o) *
-                              *reinterpret_cast<const f32x4 *>(fr + o);
-              acc[0][ct] *= m;
-              acc[1][ct] *= m;
-            }
-          }
-          Frag<bf16> sf[2][4];
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
   #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const bf16x4 v4 = lds_read_tr(sm.v + layout::v_tr_step(vt0, s4, c2));
   #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], fsw);
-          if (q == 0) {
-            // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16]);
-            // beta V of every tile now: the producers replace V in this step's phase 2
-  #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-              const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
-  #pragma unroll
-              for (int c2 = 0; c2 < 2; ++c2) {
-                const bf16x4 v4 = lds_read_tr(sm.v + layout::v_tr_step(vt0, s4, c2));
-  #pragma unroll
-                for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
-                accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
-              }
-            }
-          }
-          // O^T = S'^T Qr^T, sharing the S' fragments with Y
-  #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-  #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-              if (s4 < t_lo || s4 >= t_hi) continue;
-              Frag<bf16> xb, xq;
-              lds_frag_ch(xb, B.nkr, f0, s4, kk);
-              lds_frag_ch(xq, B.qr, f0, s4, kk);
-  #pragma unroll
-              for (int c2 = 0; c2 < 2; ++c2) {
-                mma(accY[c2][s4], xb, sf[c2][kk]);
-                mma(accOT[c2][s4], sf[c2][kk], xq);
-              }
-            }
-          // diagonal block cw of the triangular system, for the next phase
-          if (q == 0) inverse(B, cw, l16, g4);
+          for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
+          accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        block_sync();
-        // ====================== phase 2: U, O, state update, o stores
-        if (it > 0) {
-          const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
-          // U = (I + beta A)^{-1} Y by block forward substitution:
-          //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
-          // (quarter mode: U_q = X_qq Y_q, the other tiles zero)
-          f32x4 accU[2][4];
+      }
+      if constexpr (GATE) {
+        // row tile by row tile, the S' fragments formed as they are used; in a
+        // quarter-mode window quarter q's rows meet d_q S' (d_1 = r_0 in slot 0,
+        // d_2 and d_3 in slots 3 and 4), the state at quarter q's reference
   #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (i < t_lo || i >= t_hi) {
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float *dq = quarter_slot(B, s4 == 1 ? 0 : s4 + 1);
   #pragma unroll
-              for (int c2 = 0; c2 < 2; ++c2) accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-              continue;
-            }
-            if (!quarters) {
-  #pragma unroll
-              for (int k = 0; k < i; ++k) {
-                Frag4<bf16> la;
-                lds_frag4(la, B.lm, kLDC, 16 * i + l16, 16 * k, g4);
-  #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                  Frag4<bf16> uk;
-                  acc_frag4(uk, accU[c2][k]);
-                  mma16(accY[c2][i], la, uk);
-                }
-              }
-            }
-            Frag4<bf16> xd;
-            lds_frag4(xd, B.lm, kLDC, 16 * i + l16, 16 * i, g4);
-  #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-              Frag4<bf16> yi;
-              acc_frag4(yi, accY[c2][i]);
-              accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-              mma16(accU[c2][i], xd, yi);
-            }
-          }
-          Frag<bf16> uf[2][2];
-  #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2)
-  #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[c2][kk], accU[c2][2 * kk], accU[c2][2 * kk + 1]);
-          // O^T += U^T P^T     (lane holds O[16 rt + l16][vcol + 16 c2 + 4 g4 + e]);
-          // quarter mode: only the k-step holding tile q (the other U tiles are zero)
-  #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-  #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              if (rt < t_lo || rt >= t_hi) continue;
-              if (kk <= rt / 2 && (!quarters || kk == rt / 2)) {
-                Frag<bf16> xp;
-                lds_frag_ck(xp, B.pm, kLDC, 16 * rt + l16, 32 * kk, g4);
-  #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) mma(accOT[c2][rt], uf[c2][kk], xp);
-              }
-            }
-          // S' += Kc^T U   (Kc^T fragments by transposing loads of the row-major Kc)
-  #pragma unroll
-          for (int ct = 0; ct < 8; ++ct)
-  #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              if (quarters && kk != q / 2) continue;
-              const bf16x4 lo = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, kk, 0));
-              const bf16x4 hi = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, kk, 1));
-              Frag<bf16> a;
-              a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  #pragma unroll
-              for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
-            }
-          // o rows of this window, after its last step: staged through this wave's
-          // own 16 rows of the window's nKr (read by no one after the last phase 1;
-          // layout::stage_at), so each store writes 64 contiguous bytes of a row
-          if (itm.write_o && q == nstep - 1) {
-            bf16 *stage = B.nkr + 16 * kRow * cw;
-  #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+          for (int kk = 0; kk < 4; ++kk) {
+            Frag<bf16> sq[2];
+            if (quarters && s4 > 0) {
+              const f32x4 dl = *reinterpret_cast<const f32x4 *>(dq + quarter_off(2 * kk, g4));
+              const f32x4 dh = *reinterpret_cast<const f32x4 *>(dq + quarter_off(2 * kk + 1, g4));
   #pragma unroll
               for (int c2 = 0; c2 < 2; ++c2)
-                store4<bf16>(stage + layout::stage_w_step(sw0, rt, c2), accOT[c2][rt] * p.scale);
-            const __amdgpu_buffer_rsrc_t ors = make_rsrc(
-                reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
-                (uint32_t)row_hi * (uint32_t)rowstride * 2u);
+                acc_frag_ch(sq[c2], acc[c2][2 * kk] * dl, acc[c2][2 * kk + 1] * dh, fsw);
+            } else {
   #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int r = 16 * k + l16;
-              const f32x4 val =
-                  swap_halves(*reinterpret_cast<const f32x4 *>(stage + layout::stage_r_step(sr0, k)), ssw);
-              if (r >= row_lo)
-                buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
+              for (int c2 = 0; c2 < 2; ++c2) acc_frag_ch(sq[c2], acc[c2][2 * kk], acc[c2][2 * kk + 1], fsw);
+            }
+            Frag<bf16> xb, xq;
+            lds_frag_ch(xb, B.nkr, f0, s4, kk);
+            lds_frag_ch(xq, B.qr, f0, s4, kk);
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              mma(accY[c2][s4], xb, sq[c2]);
+              mma(accOT[c2][s4], sq[c2], xq);
             }
           }
         }
-        block_sync();
-      }
-      if (!sm.buf[it & 1].info[3]) break;
-    }
-  } else {
-    // Window it - 1 in iteration it: Y and O^T products in the first phase, the
-    // substitution, state update and o stores in the second.
-    for (;; ++it) {
-      f32x4 accY[2][4], accOT[2][4];
-      // ====================== phase 1: Y and O^T products, one diagonal inverse
-      if (it > 0) {
-        Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
-        // bring the state to this window's scale
-  #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          const f32x4 m = *reinterpret_cast<const f32x4 *>(B.mfac + 16 * ct + 4 * g4);
-          acc[0][ct] *= m;
-          acc[1][ct] *= m;
-        }
+      } else {
         Frag<bf16> sf[2][4];
   #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
   #pragma unroll
           for (int kk = 0; kk < 4; ++kk) acc_frag_ch(sf[c2][kk], acc[c2][2 * kk], acc[c2][2 * kk + 1], fsw);
-        // Y = beta V + nKr S'   (lane holds Y[16 s4 + 4 g4 + e][vcol + 16 c2 + l16])
-  #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(B.beta + 16 * s4 + 4 * g4);
-  #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const bf16x4 v4 = lds_read_tr(sm.v + layout::v_tr_step(vt0, s4, c2));
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) accY[c2][s4][e] = b4[e] * (float)v4[e];
-            accOT[c2][s4] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
         // O^T = S'^T Qr^T, sharing the S' fragments with Y
   #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -892,57 +813,89 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
               mma(accOT[c2][s4], sf[c2][kk], xq);
             }
           }
-        // diagonal block cw of the triangular system, for the next phase
-        inverse(B, cw, l16, g4);
       }
-      block_sync();
-      // ====================== phase 2: U, O, state update, o stores
-      if (it > 0) {
-        Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
-        const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
-        // U = (I + beta A)^{-1} Y by block forward substitution:
-        //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
-        f32x4 accU[2][4];
+      // diagonal block cw of the triangular system, for the next phase
+      inverse(B, cw, l16, g4);
+    }
+    block_sync();
+    // ====================== phase 2: U, O, state update, o stores
+    if (it > 0) {
+      Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
+      const bool quarters = GATE && __builtin_amdgcn_readfirstlane(B.info[3]) == 2;  // wave-uniform
+      const int row_lo = B.info[0], row_hi = B.info[1], tok0 = B.info[2];
+      // U = (I + beta A)^{-1} Y by block forward substitution:
+      //   U_i = X_ii (Y_i + sum_{k < i} Lm_ik U_k),  Lm_ik = -beta A_ik
+      f32x4 accU[2][4];
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
   #pragma unroll
-          for (int k = 0; k < i; ++k) {
-            Frag4<bf16> la;
-            lds_frag4(la, B.lm, kLDC, 16 * i + l16, 16 * k, g4);
-  #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-              Frag4<bf16> uk;
-              acc_frag4(uk, accU[c2][k]);
-              mma16(accY[c2][i], la, uk);
-            }
-          }
-          Frag4<bf16> xd;
-          lds_frag4(xd, B.lm, kLDC, 16 * i + l16, 16 * i, g4);
+        for (int k = 0; k < i; ++k) {
+          Frag4<bf16> la;
+          lds_frag4(la, B.lm, kLDC, 16 * i + l16, 16 * k, g4);
   #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            Frag4<bf16> yi;
-            acc_frag4(yi, accY[c2][i]);
-            accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            mma16(accU[c2][i], xd, yi);
+            Frag4<bf16> uk;
+            acc_frag4(uk, accU[c2][k]);
+            mma16(accY[c2][i], la, uk);
           }
         }
-        Frag<bf16> uf[2][2];
+        Frag4<bf16> xd;
+        lds_frag4(xd, B.lm, kLDC, 16 * i + l16, 16 * i, g4);
   #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < 2; ++c2) {
+          Frag4<bf16> yi;
+          acc_frag4(yi, accY[c2][i]);
+          accU[c2][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          mma16(accU[c2][i], xd, yi);
+        }
+      }
+      Frag<bf16> uf[2][2];
   #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[c2][kk], accU[c2][2 * kk], accU[c2][2 * kk + 1]);
-        // O^T += U^T P^T     (lane holds O[16 rt + l16][vcol + 16 c2 + 4 g4 + e])
+      for (int c2 = 0; c2 < 2; ++c2)
   #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int kk = 0; kk < 2; ++kk) acc_frag_sk(uf[c2][kk], accU[c2][2 * kk], accU[c2][2 * kk + 1]);
+      // O^T += U^T P^T     (lane holds O[16 rt + l16][vcol + 16 c2 + 4 g4 + e])
   #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            if (kk <= rt / 2) {
-              Frag<bf16> xp;
-              lds_frag_ck(xp, B.pm, kLDC, 16 * rt + l16, 32 * kk, g4);
+      for (int rt = 0; rt < 4; ++rt)
   #pragma unroll
-              for (int c2 = 0; c2 < 2; ++c2) mma(accOT[c2][rt], uf[c2][kk], xp);
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk <= rt / 2) {
+            Frag<bf16> xp;
+            lds_frag_ck(xp, B.pm, kLDC, 16 * rt + l16, 32 * kk, g4);
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) mma(accOT[c2][rt], uf[c2][kk], xp);
+          }
+        }
+      if constexpr (GATE) {
+        // S' += Kc_q^T U_q quarter by quarter (16-deep products); in a
+        // quarter-mode window the state first moves from quarter q - 1's
+        // reference to quarter q's (factor r_{q-1} in slot q - 1), ending at
+        // quarter 3's
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (quarters && q > 0) {
+            const float *rq = quarter_slot(B, q - 1);
+  #pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+              const f32x4 m = *reinterpret_cast<const f32x4 *>(rq + quarter_off(ct, g4));
+              acc[0][ct] *= m;
+              acc[1][ct] *= m;
             }
           }
+          Frag4<bf16> uq[2];  // U_q: half q & 1 of the packed 32-token fragment
+  #pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2)
+            uq[c2].v = (q & 1) ? __builtin_shufflevector(uf[c2][q >> 1].v, uf[c2][q >> 1].v, 4, 5, 6, 7)
+                               : __builtin_shufflevector(uf[c2][q >> 1].v, uf[c2][q >> 1].v, 0, 1, 2, 3);
+  #pragma unroll
+          for (int ct = 0; ct < 8; ++ct) {
+            Frag4<bf16> a;
+            a.v = lds_read_tr(B.kc + layout::kc_tr_step(kt0, ct, q >> 1, q & 1));
+  #pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) mma16(acc[c2][ct], a, uq[c2]);
+          }
+        }
+      } else {
         // S' += Kc^T U   (Kc^T fragments by transposing loads of the row-major Kc)
   #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
@@ -955,32 +908,32 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
   #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) mma(acc[c2][ct], a, uf[c2][kk]);
           }
-        // o rows of this window: staged through this wave's own 16 rows of the
-        // window's nKr (read by no one after phase 1; layout::stage_at), so each
-        // store writes 64 contiguous bytes of a row
-        if (itm.write_o) {
-          bf16 *stage = B.nkr + 16 * kRow * cw;
+      }
+      // o rows of this window: staged through this wave's own 16 rows of the
+      // window's nKr (read by no one after phase 1; layout::stage_at), so each
+      // store writes 64 contiguous bytes of a row
+      if (itm.write_o) {
+        bf16 *stage = B.nkr + 16 * kRow * cw;
   #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt)
   #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-              store4<bf16>(stage + layout::stage_w_step(sw0, rt, c2), accOT[c2][rt] * p.scale);
-          const __amdgpu_buffer_rsrc_t ors = make_rsrc(
-              reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
-              (uint32_t)row_hi * (uint32_t)rowstride * 2u);
+          for (int c2 = 0; c2 < 2; ++c2)
+            store4<bf16>(stage + layout::stage_w_step(sw0, rt, c2), accOT[c2][rt] * p.scale);
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+            reinterpret_cast<bf16 *>(p.o) + (itm.bos + tok0) * rowstride + (int64_t)itm.h * kD + vcol,
+            (uint32_t)row_hi * (uint32_t)rowstride * 2u);
   #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int r = 16 * k + l16;
-            const f32x4 val =
-                swap_halves(*reinterpret_cast<const f32x4 *>(stage + layout::stage_r_step(sr0, k)), ssw);
-            if (r >= row_lo)
-              buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
-          }
+        for (int k = 0; k < 4; ++k) {
+          const int r = 16 * k + l16;
+          const f32x4 val =
+              swap_halves(*reinterpret_cast<const f32x4 *>(stage + layout::stage_r_step(sr0, k)), ssw);
+          if (r >= row_lo)
+            buf_store_b128_cached(ors, (uint32_t)r * (uint32_t)rowstride * 2u + 16u * g4, val);
         }
       }
-      block_sync();
-      if (!sm.buf[it & 1].info[3]) break;
     }
+    block_sync();
+    if (!sm.buf[it & 1].info[3]) break;
   }
 
   // final state S = 2^{G_end - Gm} S' of the last window
