@@ -651,6 +651,13 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     }
     // q, k, beta of the next window's chunk
     issue_qk(last ? blk + 1 : blk);
+    // The operand phase (exponentials and conversions, the longest vector-ALU
+    // stream of a window) runs at raised wave priority, so the SIMD's issue
+    // arbiter prefers it over its consumer partner; the Gram phase runs at the
+    // default, where the consumers' substitution chain is the critical one
+    // (1-3% on the 4 x 8,192 and 1M-token workloads; raising it for the whole
+    // loop, or the consumers' in their second phase, gained nothing).
+    __builtin_amdgcn_s_setprio(0);
     block_sync();
     // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
@@ -685,6 +692,7 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
       }
     }
     block_sync();
+    __builtin_amdgcn_s_setprio(3);
     if (fresh) slow = !decide();
     if (!sm.buf[it & 1].info[3]) break;
   }
