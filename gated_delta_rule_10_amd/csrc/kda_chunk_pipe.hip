@@ -651,13 +651,6 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
     }
     // q, k, beta of the next window's chunk
     issue_qk(last ? blk + 1 : blk);
-    // The operand phase (exponentials and conversions, the longest vector-ALU
-    // stream of a window) runs at raised wave priority, so the SIMD's issue
-    // arbiter prefers it over its consumer partner; the Gram phase runs at the
-    // default, where the consumers' substitution chain is the critical one
-    // (1-3% on the 4 x 8,192 and 1M-token workloads; raising it for the whole
-    // loop, or the consumers' in their second phase, gained nothing).
-    __builtin_amdgcn_s_setprio(0);
     block_sync();
     // ====================== phase 2: Gram products of window it
     if (blk < nblk) {
@@ -676,6 +669,15 @@ __device__ __forceinline__ void producer_loop(const ChunkParams &p, const ChunkI
           *reinterpret_cast<u32x4 *>(sm.v + layout::v_row_step(pV, j)) = Rv[j];
       }
     }
+    // Wave priorities order the SIMD's issue between its producer and consumer
+    // wave: the producer runs its operands and Gram products at 3, the
+    // consumer its block substitution at 2, everything else runs at 0 (the
+    // loads, digest and decision here; the consumer's products with the state
+    // and o stores).  Measured on the 1M-token pack: -2.5% against no
+    // priorities; the producer at 3 in its whole loop, the consumer's
+    // substitution at 3, or the Gram below the substitution, gained less or
+    // nothing.
+    __builtin_amdgcn_s_setprio(0);
     issue_v(blk + 1);  // v of the next chunk (written at its first window)
     if (blk < nblk && last && blk + 1 < nblk)  // read after the barrier
       digest_g((int)rows_of(blk + 1),
@@ -827,6 +829,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
     }
     block_sync();
     // ====================== phase 2: U, O, state update, o stores
+    __builtin_amdgcn_s_setprio(2);  // the substitution chain (see producer_loop)
     if (it > 0) {
       Buf &B = sm.buf[(it + 1) & 1];  // window it - 1
       const bool quarters = GATE && __builtin_amdgcn_readfirstlane(B.info[3]) == 2;  // wave-uniform
@@ -857,6 +860,7 @@ __device__ __forceinline__ void consumer_loop(const ChunkParams &p, const ChunkI
           mma16(accU[c2][i], xd, yi);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       Frag<bf16> uf[2][2];
   #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
