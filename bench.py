@@ -7,7 +7,8 @@ heads, bf16 -- inputs resident in HBM before the timed region.  The 4 x 8,192 x
 96 batch and the single 65,536-token sequence (nonzero initial state, decay
 floor -5) are timed after it and reported as extra prefill lines; the recurrent
 decode workload (512 sequences x 96 heads, fp32 states in HBM, 1000 in-place
-steps) last, in the same JSON line.
+steps) last, in the same JSON line, after a kda_state_io line (a gather of
+512 fp32 states of 96 heads from a 1,024-slot pool in random order).
 
 With --front gate the prefill reads raw gate logits (fp32, in place of g), per-head
 A_log and per-channel dt_bias, and beta logits, and applies K3's lower-bounded gate
@@ -22,6 +23,7 @@ Algorithmic accounting (fixed; it does not depend on the implementation):
                                  + 3 x 256 (q, k, v) + 512 (g) + 4 (beta) + 256 (o) = 132,612
                                  (+ 4,608 for the fused step's three bf16 conv caches,
                                  read and rewritten; per-head weights are not counted)
+  state_io bytes per gathered (state, head) = 2 x 65,536 (read + write)
 Roofline peaks: HBM 8.0 TB/s; bf16 dense matrix 2.5 PFLOP/s (2,516.6 TFLOP/s).
 """
 from __future__ import annotations
@@ -57,6 +59,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-state-io", action="store_true",
+                    help="skip the kda_state_io gather line (512 x 96 fp32 states)")
     ap.add_argument("--decode-kernel", choices=("step", "fused", "spec"), default="step",
                     help="decode leg: the plain step (default), the fused step with the "
                          "short-convolution front end and the output RMSNorm, or the "
@@ -325,6 +329,35 @@ def time_decode(kda, ki, steps, warmup=10, kernel="step", window=4):
                 **extra)
 
 
+def time_state_io(kda, steps=20, warmup=3, states=512, heads=96):
+    """kda_state_io gathering `states` fp32 states of `heads` heads (a prefix-cache
+    restore: snapshots copied into request slots) from a pool of twice as many
+    slots, in a seeded random order; algorithmic bytes = the states read + written."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(3001)
+    pool = torch.randn((2 * states, heads, D, D), generator=gen, device="cuda")
+    dst = torch.empty((states, heads, D, D), device="cuda")
+    idx = torch.randperm(2 * states, generator=gen, device="cuda")[:states].to(torch.int32)
+    for _ in range(warmup):
+        kda.state_io(kda.STATE_GATHER, dst, pool, idx)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        kda.state_io(kda.STATE_GATHER, dst, pool, idx)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes = 2 * states * heads * STATE_BYTES
+    del pool, dst, idx
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(op="gather", states=states, heads=heads, dtype="f32", ms_per_call=ms, calls=steps,
+                bytes_per_call=nbytes, gb_per_s=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+                kernel="state_io_kernel", entry="kda_state_io")
+
+
 def baseline_chains(x):
     """The (sequence, head) chains the oracle baseline times: heads 0, 31, 63 and
     95 (spread over the 96) of every sequence, up to 32 sequences."""
@@ -561,6 +594,11 @@ def main():
         note(f"{wl}: {line['prefill_workloads'][wl]['ms_per_step']:.3f} ms per prefill")
         del p
         torch.cuda.empty_cache()
+    # (not in a counter-calibration run: the traffic record takes every state_io
+    # dispatch of that run as the calibration copy)
+    if not args.no_state_io and not args.copy_calibration_mib:
+        line["state_io"] = time_state_io(kda)
+        note("state_io timed")
     if not args.no_decode:
         line["decode"] = time_decode(kda, ki, args.decode_steps, kernel=args.decode_kernel,
                                      window=args.spec_window)

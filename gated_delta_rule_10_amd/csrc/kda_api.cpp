@@ -361,7 +361,7 @@ kda_status kda_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
   if (!valid_dtype(dst_dtype) || (op != KDA_STATE_ZERO && !valid_dtype(src_dtype)))
     return KDA_ERROR_INVALID_VALUE;
   if (head_dim != KDA_HEAD_DIM) return KDA_ERROR_UNSUPPORTED;
-  if ((int64_t)count * 64 > INT32_MAX) return KDA_ERROR_INVALID_VALUE;
+  if ((int64_t)count * num_heads > INT32_MAX) return KDA_ERROR_INVALID_VALUE;  // one workgroup per head
   if (count == 0) return KDA_SUCCESS;
   if (!dst || !aligned16(dst)) return KDA_ERROR_INVALID_VALUE;
   if (op != KDA_STATE_ZERO && (!src || !aligned16(src))) return KDA_ERROR_INVALID_VALUE;
@@ -381,9 +381,8 @@ kda_status kda_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
     const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
     if (s0 < d0 + db && d0 < s0 + sb) return KDA_ERROR_INVALID_VALUE;
   }
-  const int64_t elems = (int64_t)num_heads * head_dim * head_dim;
   return launch_status(kda::launch_state_io(op, src, src_dtype, src_slots, dst, dst_dtype,
-                                            dst_slots, indices, count, elems,
+                                            dst_slots, indices, count, num_heads,
                                             (hipStream_t)stream));
 }
 

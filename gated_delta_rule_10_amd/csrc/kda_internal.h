@@ -21,7 +21,7 @@ hipError_t launch_spec_verify(const kda_spec_verify_args &v, hipStream_t stream)
 hipError_t launch_state_io(kda_state_op op, const void *src, kda_dtype src_dtype,
                            int32_t src_slots, void *dst, kda_dtype dst_dtype,
                            int32_t dst_slots, const int32_t *indices, int32_t count,
-                           int64_t elems_per_state, hipStream_t stream);
+                           int32_t num_heads, hipStream_t stream);
 
 // Chunked prefill plan, computed on the host from sizes only.
 struct ChunkPlan {

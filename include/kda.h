@@ -466,7 +466,11 @@ kda_status kda_spec_verify_step(const kda_spec_verify_args *args, void *stream);
  *   KDA_STATE_SCATTER dst[indices[i]] = src[i]    (save a checkpoint)
  * converting between src_dtype and dst_dtype (fp32 -> bf16 rounds to nearest
  * even).  A negative index, or one >= the slot count of the indexed pool,
- * skips that i.  src and dst must not overlap.
+ * skips that i.  src and dst must not overlap.  Errors: an op out of range,
+ * count < 0, num_heads < 1, head_dim != 128 (KDA_ERROR_UNSUPPORTED), missing or
+ * misaligned (16-byte) pools, missing or misaligned indices for a gather or
+ * scatter, count beyond the pool it indexes directly, overlapping pools, and
+ * count x num_heads beyond 2^31 - 1 (one workgroup per head of a state).
  * ---------------------------------------------------------------------- */
 typedef enum kda_state_op {
   KDA_STATE_ZERO = 0,

@@ -167,6 +167,8 @@ def test_state_io_rejects_invalid_arguments(lib):
     assert f(kda.STATE_COPY, base, 0, 2, base * 4, 0, 2, None, 1, 4, 64, None) == 2
     assert f(kda.STATE_COPY, base, 0, 1, base * 4, 0, 2, None, 2, 4, 128, None) == 1  # count > src
     assert f(kda.STATE_ZERO, None, 0, 0, base, 0, 2, None, 0, 4, 128, None) == 0  # empty
+    # one workgroup per head: count x heads must fit the grid
+    assert f(kda.STATE_ZERO, None, 0, 0, base, 0, 1 << 30, None, 1 << 20, 4096, 128, None) == 1
 
 
 def _gate_args(**gate):
