@@ -61,6 +61,37 @@ def test_varlen_ragged_with_initial_state(kda, dtype):
     check_chains(inp, o, sf, chains, inp["dtype"], scale=0.7)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", ["beta0_g0", "scale0", "no_write"])
+def test_prefill_degenerate_parameters(kda, dtype, case):
+    """Degenerate values the recurrence allows ("How Kimi K3 Engineered Its Way
+    to the Frontier", "How KDA updates its state"): beta = 0 on every third token
+    (no write there) with g = 0 on 40 channels (no decay); scale = 0 (o is
+    exactly 0, the state evolves as usual); beta = 0 and g = 0 everywhere (the
+    state passes through unchanged and o_t = scale S0^T q_t)."""
+    announce(f"chunk degenerate {case} dtype={dtype}")
+    lens = (150, 77, 64)
+    cfg = ki.PrefillConfig("t", lens, 2, dtype, init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=91)
+    scale = 0.8
+    if case == "beta0_g0":
+        inp["beta"][::3] = 0.0
+        inp["g"][:, :, :40] = 0.0
+    elif case == "scale0":
+        scale = 0.0
+    else:
+        inp["beta"].zero_()
+        inp["g"].zero_()
+    o, sf = run(kda, inp, scale=scale)
+    torch.cuda.synchronize()
+    if case == "scale0":
+        assert float(o.abs().max()) == 0.0
+    if case == "no_write":
+        assert rel_err(to64(sf), to64(inp["initial_state"])) <= 1e-6
+    chains = [(n, h) for n in range(len(lens)) for h in range(2)]
+    check_chains(inp, o, sf, chains, inp["dtype"], scale=scale)
+
+
 def test_fixed_batch_matches_varlen(kda):
     announce("chunk fixed batch vs varlen")
     cfg = ki.PrefillConfig("t", (200, 200, 200), 4, "bf16", init_std=0.1)

@@ -49,6 +49,35 @@ def test_decode_small_slots_vs_oracle(kda, dtype):
         assert torch.equal(gpu_pool[s], pool[s])
 
 
+@pytest.mark.parametrize("case", ["beta0_g0", "scale0"])
+def test_decode_degenerate_parameters(kda, case):
+    """One decode step with beta = 0 on half the rows and g = 0 on 40 channels
+    (those rows of the state are carried unchanged), or with scale = 0 (o is
+    exactly 0)."""
+    announce(f"decode degenerate {case}")
+    dev = "cuda"
+    cfg = ki.DecodeConfig("t", 4, 3, 1)
+    x = ki.make_decode_ring(cfg, device=dev, ring=1)
+    q, k, v = x["q"][0], x["k"][0], x["v"][0]
+    g, beta = x["g"][0].clone(), x["beta"][0].clone()
+    scale = 0.6
+    if case == "beta0_g0":
+        beta[::2] = 0.0
+        g[:, :, :40] = 0.0
+    else:
+        scale = 0.0
+    st = x["state"].clone()
+    o = kda.recurrent_step(q, k, v, g, beta, st, scale=scale)
+    o_ref, s_ref = oracle.decode_step(q, k, v, g, beta, x["state"], scale=scale)
+    torch.cuda.synchronize()
+    if case == "scale0":
+        assert float(o.abs().max()) == 0.0
+    else:  # no write and no decay: key rows 0..39 of rows 0 and 2 carried bit for bit
+        assert torch.equal(st[::2, :, :40], x["state"][::2, :, :40])
+        assert rel_err(to64(o), o_ref) <= TOL[torch.bfloat16]
+    assert rel_err(to64(st), s_ref) <= 1e-4
+
+
 def test_decode_identity_slots(kda):
     announce("decode identity slots")
     dev = "cuda"
