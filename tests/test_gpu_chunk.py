@@ -92,6 +92,23 @@ def test_prefill_degenerate_parameters(kda, dtype, case):
     check_chains(inp, o, sf, chains, inp["dtype"], scale=scale)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_all_sequences_empty(kda, dtype):
+    """A pack whose sequences are all empty: no output rows, and every final
+    state is its initial state bit for bit (zero without one)."""
+    announce(f"chunk all sequences empty dtype={dtype}")
+    cfg = ki.PrefillConfig("t", (0, 0, 0), 2, dtype, init_std=0.3, varlen=True)
+    inp = ki.make_prefill(cfg, device="cuda", seed=5)
+    o, sf = run(kda, inp)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(sf, inp["initial_state"])
+    inp["initial_state"] = None
+    o, sf = run(kda, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(sf, torch.zeros_like(sf))
+
+
 def test_fixed_batch_matches_varlen(kda):
     announce("chunk fixed batch vs varlen")
     cfg = ki.PrefillConfig("t", (200, 200, 200), 4, "bf16", init_std=0.1)

@@ -78,6 +78,21 @@ def test_decode_degenerate_parameters(kda, case):
     assert rel_err(to64(st), s_ref) <= 1e-4
 
 
+def test_decode_empty_batch(kda):
+    """A step over no rows returns an empty output and leaves the pool as it was."""
+    announce("decode empty batch")
+    dev = "cuda"
+    cfg = ki.DecodeConfig("t", 2, 3, 1)
+    x = ki.make_decode_ring(cfg, device=dev, ring=1)
+    st = x["state"].clone()
+    e = lambda t: t[:0]
+    o = kda.recurrent_step(e(x["q"][0]), e(x["k"][0]), e(x["v"][0]), e(x["g"][0]),
+                           e(x["beta"][0]), st)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(st, x["state"])
+
+
 def test_decode_identity_slots(kda):
     announce("decode identity slots")
     dev = "cuda"
